@@ -1,0 +1,194 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged KV-cache decode library.
+ *
+ * What is computed comes from these pages (cited by title and section):
+ *   [BOOK] vLLM book ch.4 "PagedAttention：虚拟内存的启示" (yangyitao.com)
+ *   [GUST] "PagedAttention：KV Cache的虚拟内存" (thegustafson.com "Paged
+ *          Attention", bittide translation)
+ *   [P5]   "PagedAttention原理（下）" (5688vip, vLLM推理框架全解析 04)
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a device pointer unless stated otherwise.  The caller
+ *     owns all memory; the library never allocates, frees or keeps a pointer
+ *     after a call returns.  Work is enqueued on `stream` (0 = null stream)
+ *     and the call returns without synchronising.
+ *   - Errors are returned, never thrown.  Host-checkable arguments are
+ *     validated before anything is enqueued; a failed launch returns
+ *     PA_ERR_HIP.  Device-side preconditions are listed per call; where a
+ *     kernel can still check one cheaply it skips the offending element
+ *     instead of faulting (stated per call).
+ *   - fp16 buffers are IEEE binary16 and must be 16-byte aligned; int32
+ *     buffers 4-byte aligned.  All tensors are dense row-major.
+ *   - Layout of one layer's pool ([BOOK] §4.3.1): a (2, num_blocks,
+ *     block_size, num_kv_heads, head_size) fp16 tensor; index 0 of the first
+ *     axis is K, index 1 is V.  key_cache / value_cache below are the two
+ *     halves, each [num_blocks, block_size, num_kv_heads, head_size].  A
+ *     "slot" is a row index into a half seen as [num_blocks*block_size,
+ *     num_kv_heads, head_size], so slot = block * block_size + offset.
+ *   - Supported shapes: head_size 64 or 128; block_size 16, 32 or 64;
+ *     num_heads / num_kv_heads (the GQA group) 1, 2, 4 or 8.  Other shapes
+ *     return PA_ERR_UNSUPPORTED.
+ */
+#ifndef PAGED_KV_PA_H
+#define PAGED_KV_PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int pa_status;
+
+#define PA_OK 0
+#define PA_ERR_NULL 1          /* a required pointer is NULL */
+#define PA_ERR_SHAPE 2         /* a size is out of range or inconsistent */
+#define PA_ERR_UNSUPPORTED 3   /* head_size / block_size / group not built */
+#define PA_ERR_ALIGN 4         /* a pointer is not aligned as required */
+#define PA_ERR_WORKSPACE 5     /* split-KV workspace too small */
+#define PA_ERR_HIP 6           /* the HIP runtime reported an error */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pa_status_str(pa_status status);
+
+/* Shape of one layer's pool: writes (2, num_blocks, block_size, num_kv_heads,
+ * head_size) to out_shape[0..4] (host memory) ([BOOK] §4.3.1). */
+void pa_kv_cache_shape(int32_t num_blocks, int32_t block_size,
+                       int32_t num_kv_heads, int32_t head_size,
+                       int64_t out_shape[5]);
+
+/*
+ * pa_slot_mapping -- physical slot of each token to be written ([BOOK] §4.4.3).
+ *   For token j with table row r = seq_idx[j] and logical position
+ *   p = positions[j]:  slot_mapping[j] = block_tables[r, p / block_size] *
+ *   block_size + p % block_size.
+ *   block_tables  int32 [num_rows, max_blocks_per_seq]
+ *   seq_idx       int32 [num_tokens], positions int32 [num_tokens]
+ *   slot_mapping  int32 [num_tokens] (output)
+ *   A token whose row is outside [0, num_rows) or whose position is outside
+ *   [0, max_blocks_per_seq * block_size) gets slot -1 (no write).
+ *   num_tokens == 0 is a no-op.
+ */
+pa_status pa_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, int32_t num_rows,
+                          const int32_t* seq_idx, const int32_t* positions,
+                          int32_t num_tokens, int32_t block_size,
+                          hipStream_t stream);
+
+/*
+ * pa_cache_write -- write new tokens' K and V into their slots ([BOOK] §4.3.2,
+ * §4.5 (1): reshape_and_cache with slot_mapping).
+ *   key, value    fp16 [num_tokens, num_kv_heads, head_size]
+ *   key_cache, value_cache  fp16 [num_blocks, block_size, num_kv_heads,
+ *                 head_size] (written in place)
+ *   slot_mapping  int32 [num_tokens]; slot < 0 or >= num_blocks*block_size
+ *                 means "skip this token".
+ *   A bit-exact copy (no arithmetic).  Precondition: the non-negative slots
+ *   are distinct (otherwise which token lands last is unspecified).
+ *   num_tokens == 0 is a no-op.
+ */
+pa_status pa_cache_write(const void* key, const void* value, void* key_cache,
+                         void* value_cache, const int32_t* slot_mapping,
+                         int32_t num_tokens, int32_t num_blocks,
+                         int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_size, hipStream_t stream);
+
+/*
+ * pa_copy_blocks -- copy-on-write block copies ([GUST] copy-on-write
+ * paragraph; [P5] §4.3 steps): for each pair k, physical block src[k] of both
+ * key_cache and value_cache is copied bit-exactly into block dst[k].
+ *   src, dst      int32 [num_pairs]; a pair with an id outside
+ *                 [0, num_blocks) is skipped.
+ *   Precondition: no dst is also a src or another pair's dst.
+ */
+pa_status pa_copy_blocks(void* key_cache, void* value_cache,
+                         const int32_t* src, const int32_t* dst,
+                         int32_t num_pairs, int32_t num_blocks,
+                         int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_size, hipStream_t stream);
+
+/*
+ * pa_decode -- single-pass paged decode attention ([BOOK] §4.5, §4.6).
+ *   For sequence i and query head h (kv head h / (num_heads/num_kv_heads)):
+ *     out[i,h,:] = sum_t softmax_t(scale * <query[i,h,:], K_t>) * V_t
+ *   over exactly t = 0 .. context_lens[i]-1, where token t lives at offset
+ *   t % block_size of physical block block_tables[i, t / block_size].
+ *   Statistics and accumulation in fp32 (online softmax, [BOOK] §4.6); out
+ *   is rounded to fp16 (nearest even).
+ *   out, query    fp16 [num_seqs, num_heads, head_size]
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]; entries at or past
+ *                 ceil(context_lens[i]/block_size) are never read.
+ *   context_lens  int32 [num_seqs]; values above max_blocks_per_seq *
+ *                 block_size are clamped to it; a value <= 0 gives zeros.
+ *   Slots past context_lens[i] in the last block are never read, so they
+ *   may hold anything (Inf/NaN included).
+ *   Precondition: the table entries that are read are in [0, num_blocks);
+ *   a block outside that range is read as all-zero instead of faulting.
+ *   One workgroup walks one (sequence, kv head) end to end: use
+ *   pa_decode_splitk for long contexts.  num_seqs == 0 is a no-op.
+ */
+pa_status pa_decode(void* out, const void* query, const void* key_cache,
+                    const void* value_cache, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_size, int32_t block_size, int32_t num_blocks,
+                    float scale, hipStream_t stream);
+
+/*
+ * Split-KV workspace.  With Pmax = ceil(max_blocks_per_seq * block_size /
+ * partition_size), the workspace holds, in this order and back to back:
+ *   max_logits fp32 [num_seqs, num_heads, Pmax]
+ *   exp_sums   fp32 [num_seqs, num_heads, Pmax]
+ *   tmp_out    fp32 [num_seqs, num_heads, Pmax, head_size]
+ * pa_splitk_workspace_size returns its size in bytes (0 on bad arguments).
+ */
+size_t pa_splitk_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                int32_t head_size, int32_t max_blocks_per_seq,
+                                int32_t block_size, int32_t partition_size);
+
+/*
+ * pa_decode_splitk -- per-partition softmax state for split-KV decode.
+ *   Partition p of sequence i is tokens [p*P, min((p+1)*P, n_i)) with
+ *   P = partition_size (a multiple of block_size, at most 8192).  For each
+ *   non-empty (i, h, p) it stores, with x_t = scale * <query[i,h], K_t>:
+ *     max_logits[i,h,p] = m = max_t x_t
+ *     exp_sums[i,h,p]   = sum_t exp(x_t - m)
+ *     tmp_out[i,h,p,:]  = sum_t exp(x_t - m) * V_t      (not normalised)
+ *   Empty partitions (p*P >= n_i) are not written.  Arguments otherwise as
+ *   pa_decode; `workspace` is device memory of workspace_bytes >=
+ *   pa_splitk_workspace_size(...), 16-byte aligned.
+ */
+pa_status pa_decode_splitk(const void* query, const void* key_cache,
+                           const void* value_cache,
+                           const int32_t* block_tables,
+                           int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs,
+                           int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_size, int32_t block_size,
+                           int32_t num_blocks, float scale,
+                           int32_t partition_size, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pa_decode_reduce -- merge the partitions written by pa_decode_splitk with
+ * the online-softmax recurrence of [BOOK] §4.6:
+ *   M = max_p m_p,  S = sum_p s_p exp(m_p - M),
+ *   out[i,h,:] = sum_p exp(m_p - M) O_p / S     (fp16, nearest even)
+ * over the non-empty partitions p < ceil(n_i / P) only.  Same workspace,
+ * sizes and partition_size as the pa_decode_splitk call it follows (on the
+ * same stream).  A sequence with context_lens[i] <= 0 gets zeros.
+ */
+pa_status pa_decode_reduce(void* out, const void* workspace,
+                           size_t workspace_bytes,
+                           const int32_t* context_lens, int32_t num_seqs,
+                           int32_t num_heads, int32_t head_size,
+                           int32_t max_blocks_per_seq, int32_t block_size,
+                           int32_t partition_size, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_PA_H */

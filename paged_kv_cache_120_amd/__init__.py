@@ -1,0 +1,235 @@
+"""Paged KV-cache decode for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/pa.h`` (``libpagedkv.so``,
+built in-tree by ``python -m paged_kv_cache_120_amd.build``).  Each function
+here has the name of the C entry point it calls and only marshals arguments:
+it checks dtypes, devices and contiguity of the torch tensors, then passes
+their device pointers and the current HIP stream.  Every step of the path
+runs in the library's kernels; there is no fallback: the first call (or
+access to ``lib``) raises ImportError if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "PaError", "lib", "library_path", "pa_status_str", "pa_kv_cache_shape",
+    "pa_slot_mapping", "pa_cache_write", "pa_copy_blocks", "pa_decode",
+    "pa_splitk_workspace_size", "pa_decode_splitk", "pa_decode_reduce",
+    "STATUS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libpagedkv.so")
+
+STATUS = {
+    0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
+    4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP",
+}
+
+
+class PaError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__(f"{func} failed: {pa_status_str(status)} ({status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is missing: build it with "
+            "`python -m paged_kv_cache_120_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(library_path)
+    i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    sig = {
+        "pa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "pa_kv_cache_shape": (None, [i32, i32, i32, i32, ctypes.POINTER(i64)]),
+        "pa_slot_mapping": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, i32, i32, vp]),
+        "pa_cache_write": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]),
+        "pa_copy_blocks": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]),
+        "pa_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
+                                     i32, i32, f32, vp]),
+        "pa_splitk_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
+        "pa_decode_splitk": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
+                                            i32, i32, f32, i32, vp, sz, vp]),
+        "pa_decode_reduce": (ctypes.c_int, [vp, vp, sz, vp, i32, i32, i32, i32, i32,
+                                            i32, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def _lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def __getattr__(name):
+    if name == "lib":
+        return _lib()
+    raise AttributeError(name)
+
+
+def pa_status_str(status: int) -> str:
+    return _lib().pa_status_str(int(status)).decode()
+
+
+def pa_kv_cache_shape(num_blocks: int, block_size: int, num_kv_heads: int,
+                      head_size: int) -> Tuple[int, ...]:
+    out = (ctypes.c_int64 * 5)()
+    _lib().pa_kv_cache_shape(num_blocks, block_size, num_kv_heads, head_size, out)
+    return tuple(int(x) for x in out)
+
+
+def pa_splitk_workspace_size(num_seqs: int, num_heads: int, head_size: int,
+                             max_blocks_per_seq: int, block_size: int,
+                             partition_size: int) -> int:
+    return int(_lib().pa_splitk_workspace_size(num_seqs, num_heads, head_size,
+                                            max_blocks_per_seq, block_size,
+                                            partition_size))
+
+
+# ---------------------------------------------------------------------------
+# tensor marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _dev(t, dtype, name: str, ndim: Optional[int] = None) -> int:
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: expected a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _check(func: str, status: int) -> None:
+    if status != 0:
+        raise PaError(func, status)
+
+
+def pa_slot_mapping(slot_mapping, block_tables, seq_idx, positions,
+                    block_size: int, stream=None) -> None:
+    """slot_mapping[j] = block_tables[seq_idx[j], positions[j] // B] * B +
+    positions[j] % B (int32 device tensors)."""
+    torch = _torch()
+    n = int(positions.numel())
+    _check("pa_slot_mapping", _lib().pa_slot_mapping(
+        _dev(slot_mapping, torch.int32, "slot_mapping", 1),
+        _dev(block_tables, torch.int32, "block_tables", 2),
+        block_tables.shape[1], block_tables.shape[0],
+        _dev(seq_idx, torch.int32, "seq_idx", 1),
+        _dev(positions, torch.int32, "positions", 1),
+        n, block_size, _stream(stream)))
+
+
+def pa_cache_write(key, value, key_cache, value_cache, slot_mapping,
+                   stream=None) -> None:
+    """key/value fp16 [N, H_kv, D] -> key_cache/value_cache fp16
+    [nb, B, H_kv, D] at slot_mapping (int32 [N])."""
+    torch = _torch()
+    nb, B, Hkv, D = key_cache.shape
+    if tuple(value_cache.shape) != (nb, B, Hkv, D) or key.shape[1:] != (Hkv, D) \
+            or value.shape != key.shape:
+        raise ValueError("pa_cache_write: inconsistent shapes")
+    _check("pa_cache_write", _lib().pa_cache_write(
+        _dev(key, torch.float16, "key", 3), _dev(value, torch.float16, "value", 3),
+        _dev(key_cache, torch.float16, "key_cache", 4),
+        _dev(value_cache, torch.float16, "value_cache", 4),
+        _dev(slot_mapping, torch.int32, "slot_mapping", 1),
+        key.shape[0], nb, B, Hkv, D, _stream(stream)))
+
+
+def pa_copy_blocks(key_cache, value_cache, src, dst, stream=None) -> None:
+    torch = _torch()
+    nb, B, Hkv, D = key_cache.shape
+    if src.shape != dst.shape:
+        raise ValueError("pa_copy_blocks: src/dst shapes differ")
+    _check("pa_copy_blocks", _lib().pa_copy_blocks(
+        _dev(key_cache, torch.float16, "key_cache", 4),
+        _dev(value_cache, torch.float16, "value_cache", 4),
+        _dev(src, torch.int32, "src", 1), _dev(dst, torch.int32, "dst", 1),
+        src.numel(), nb, B, Hkv, D, _stream(stream)))
+
+
+def _decode_common(query, key_cache, value_cache, block_tables, context_lens):
+    torch = _torch()
+    S, H, D = query.shape
+    nb, B, Hkv, D2 = key_cache.shape
+    if D2 != D or tuple(value_cache.shape) != (nb, B, Hkv, D):
+        raise ValueError("decode: inconsistent head_size / cache shapes")
+    if block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("decode: block_tables / context_lens do not match query")
+    ptrs = (_dev(query, torch.float16, "query", 3),
+            _dev(key_cache, torch.float16, "key_cache", 4),
+            _dev(value_cache, torch.float16, "value_cache", 4),
+            _dev(block_tables, torch.int32, "block_tables", 2),
+            _dev(context_lens, torch.int32, "context_lens", 1))
+    return ptrs, (S, H, Hkv, D, B, nb, block_tables.shape[1])
+
+
+def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens,
+              scale: float, stream=None) -> None:
+    torch = _torch()
+    (q, kc, vc, bt, cl), (S, H, Hkv, D, B, nb, M) = _decode_common(
+        query, key_cache, value_cache, block_tables, context_lens)
+    if tuple(out.shape) != (S, H, D):
+        raise ValueError("pa_decode: out shape")
+    _check("pa_decode", _lib().pa_decode(
+        _dev(out, torch.float16, "out", 3), q, kc, vc, bt, M, cl, S, H, Hkv, D,
+        B, nb, float(scale), _stream(stream)))
+
+
+def pa_decode_splitk(query, key_cache, value_cache, block_tables, context_lens,
+                     scale: float, partition_size: int, workspace,
+                     stream=None) -> None:
+    """workspace: any contiguous device tensor of at least
+    pa_splitk_workspace_size(...) bytes (e.g. torch.uint8)."""
+    (q, kc, vc, bt, cl), (S, H, Hkv, D, B, nb, M) = _decode_common(
+        query, key_cache, value_cache, block_tables, context_lens)
+    ws = _dev(workspace, workspace.dtype, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("pa_decode_splitk", _lib().pa_decode_splitk(
+        q, kc, vc, bt, M, cl, S, H, Hkv, D, B, nb, float(scale),
+        int(partition_size), ws, nbytes, _stream(stream)))
+
+
+def pa_decode_reduce(out, workspace, context_lens, max_blocks_per_seq: int,
+                     block_size: int, partition_size: int, stream=None) -> None:
+    torch = _torch()
+    S, H, D = out.shape
+    ws = _dev(workspace, workspace.dtype, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("pa_decode_reduce", _lib().pa_decode_reduce(
+        _dev(out, torch.float16, "out", 3), ws, nbytes,
+        _dev(context_lens, torch.int32, "context_lens", 1), S, H, D,
+        int(max_blocks_per_seq), int(block_size), int(partition_size),
+        _stream(stream)))

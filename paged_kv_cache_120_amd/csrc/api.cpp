@@ -1,0 +1,274 @@
+// C ABI of the paged KV-cache library: argument validation, launch shapes
+// and dispatch to the gfx950 kernels.  Declarations and contracts: pa.h.
+#include "pa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "decode.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+bool supported_head(int32_t d) { return d == 64 || d == 128; }
+bool supported_block(int32_t b) { return b == 16 || b == 32 || b == 64; }
+bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+// Checks shared by the decode entry points.
+pa_status check_decode(const void* query, const void* key_cache,
+                       const void* value_cache, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_size,
+                       int32_t block_size, int32_t num_blocks, float scale) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0 || num_seqs > 65535 ||
+      num_kv_heads > 65535 || num_heads % num_kv_heads != 0 || !isfinite(scale))
+    return PA_ERR_SHAPE;
+  if (!supported_head(head_size) || !supported_block(block_size) ||
+      !supported_group(num_heads / num_kv_heads))
+    return PA_ERR_UNSUPPORTED;
+  // per-block buffer records are 32-bit; table positions are int32
+  const uint64_t block_bytes =
+      (uint64_t)block_size * num_kv_heads * head_size * 2;
+  if (block_bytes >= (1ull << 31) ||
+      (int64_t)max_blocks_per_seq * block_size >= (1ll << 31))
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return PA_ERR_NULL;
+  if (!aligned(query, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(block_tables, 4) ||
+      !aligned(context_lens, 4))
+    return PA_ERR_ALIGN;
+  return PA_OK;
+}
+
+int64_t max_partitions(int32_t max_blocks_per_seq, int32_t block_size,
+                       int32_t partition_size) {
+  const int64_t tokens = (int64_t)max_blocks_per_seq * block_size;
+  return (tokens + partition_size - 1) / partition_size;
+}
+
+pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_str(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+void pa_kv_cache_shape(int32_t num_blocks, int32_t block_size,
+                       int32_t num_kv_heads, int32_t head_size,
+                       int64_t out_shape[5]) {
+  if (!out_shape) return;
+  out_shape[0] = 2;
+  out_shape[1] = num_blocks;
+  out_shape[2] = block_size;
+  out_shape[3] = num_kv_heads;
+  out_shape[4] = head_size;
+}
+
+pa_status pa_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, int32_t num_rows,
+                          const int32_t* seq_idx, const int32_t* positions,
+                          int32_t num_tokens, int32_t block_size,
+                          hipStream_t stream) {
+  if (num_tokens < 0 || num_rows < 0 || max_blocks_per_seq <= 0 ||
+      block_size <= 0 ||
+      (int64_t)max_blocks_per_seq * block_size >= (1ll << 31))
+    return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!slot_mapping || !block_tables || !seq_idx || !positions) return PA_ERR_NULL;
+  if (!aligned(slot_mapping, 4) || !aligned(block_tables, 4) ||
+      !aligned(seq_idx, 4) || !aligned(positions, 4))
+    return PA_ERR_ALIGN;
+  return hip_status(pa::launch_slot_mapping(slot_mapping, block_tables,
+                                            max_blocks_per_seq, num_rows,
+                                            seq_idx, positions, num_tokens,
+                                            block_size, stream));
+}
+
+pa_status pa_cache_write(const void* key, const void* value, void* key_cache,
+                         void* value_cache, const int32_t* slot_mapping,
+                         int32_t num_tokens, int32_t num_blocks,
+                         int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_size, hipStream_t stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || block_size <= 0 ||
+      num_kv_heads <= 0 || head_size <= 0 || head_size % 8 != 0)
+    return PA_ERR_SHAPE;
+  const int64_t cpr = (int64_t)num_kv_heads * head_size / 8;  // 16-byte chunks
+  if (cpr >= (1ll << 31)) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return PA_ERR_NULL;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(slot_mapping, 4))
+    return PA_ERR_ALIGN;
+  return hip_status(pa::launch_cache_write(
+      key, value, key_cache, value_cache, slot_mapping, num_tokens,
+      (int64_t)num_blocks * block_size, (int)cpr, stream));
+}
+
+pa_status pa_copy_blocks(void* key_cache, void* value_cache,
+                         const int32_t* src, const int32_t* dst,
+                         int32_t num_pairs, int32_t num_blocks,
+                         int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_size, hipStream_t stream) {
+  if (num_pairs < 0 || num_blocks <= 0 || block_size <= 0 ||
+      num_kv_heads <= 0 || head_size <= 0 || head_size % 8 != 0)
+    return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !src || !dst) return PA_ERR_NULL;
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) ||
+      !aligned(src, 4) || !aligned(dst, 4))
+    return PA_ERR_ALIGN;
+  const int64_t cpb = (int64_t)block_size * num_kv_heads * head_size / 8;
+  return hip_status(pa::launch_copy_blocks(key_cache, value_cache, src, dst,
+                                           num_pairs, num_blocks, cpb, stream));
+}
+
+pa_status pa_decode(void* out, const void* query, const void* key_cache,
+                    const void* value_cache, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_size, int32_t block_size, int32_t num_blocks,
+                    float scale, hipStream_t stream) {
+  pa_status st = check_decode(query, key_cache, value_cache, block_tables,
+                              max_blocks_per_seq, context_lens, num_seqs,
+                              num_heads, num_kv_heads, head_size, block_size,
+                              num_blocks, scale);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (!out) return PA_ERR_NULL;
+  if (!aligned(out, 16)) return PA_ERR_ALIGN;
+  pa::DecodeArgs a = {};
+  a.out = static_cast<_Float16*>(out);
+  a.query = static_cast<const _Float16*>(query);
+  a.key_cache = static_cast<const char*>(key_cache);
+  a.value_cache = static_cast<const char*>(value_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.partition_size = max_blocks_per_seq * block_size;   // whole sequence
+  a.max_partitions = 1;
+  a.split = 0;
+  a.scale = scale;
+  dim3 grid(1, num_kv_heads, num_seqs);
+  return hip_status(pa::launch_decode(a, head_size, block_size,
+                                      num_heads / num_kv_heads, grid, stream));
+}
+
+size_t pa_splitk_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                int32_t head_size, int32_t max_blocks_per_seq,
+                                int32_t block_size, int32_t partition_size) {
+  if (num_seqs < 0 || num_heads <= 0 || head_size <= 0 ||
+      max_blocks_per_seq <= 0 || block_size <= 0 || partition_size <= 0)
+    return 0;
+  const int64_t pm = max_partitions(max_blocks_per_seq, block_size, partition_size);
+  const uint64_t rows = (uint64_t)num_seqs * num_heads * pm;
+  return (size_t)(rows * 4 * 2 + rows * head_size * 4);
+}
+
+pa_status pa_decode_splitk(const void* query, const void* key_cache,
+                           const void* value_cache,
+                           const int32_t* block_tables,
+                           int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs,
+                           int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_size, int32_t block_size,
+                           int32_t num_blocks, float scale,
+                           int32_t partition_size, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  pa_status st = check_decode(query, key_cache, value_cache, block_tables,
+                              max_blocks_per_seq, context_lens, num_seqs,
+                              num_heads, num_kv_heads, head_size, block_size,
+                              num_blocks, scale);
+  if (st != PA_OK) return st;
+  if (partition_size <= 0 || partition_size % block_size != 0)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  const int64_t pm = max_partitions(max_blocks_per_seq, block_size, partition_size);
+  if (pm > 65535 * 32) return PA_ERR_SHAPE;
+  if (!workspace) return PA_ERR_NULL;
+  if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
+  if (workspace_bytes < pa_splitk_workspace_size(num_seqs, num_heads, head_size,
+                                                 max_blocks_per_seq, block_size,
+                                                 partition_size))
+    return PA_ERR_WORKSPACE;
+  const size_t rows = (size_t)num_seqs * num_heads * pm;
+  pa::DecodeArgs a = {};
+  a.ws_max = static_cast<float*>(workspace);
+  a.ws_sum = a.ws_max + rows;
+  a.ws_out = a.ws_sum + rows;
+  a.query = static_cast<const _Float16*>(query);
+  a.key_cache = static_cast<const char*>(key_cache);
+  a.value_cache = static_cast<const char*>(value_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.partition_size = partition_size;
+  a.max_partitions = (int)pm;
+  a.split = 1;
+  a.scale = scale;
+  dim3 grid((unsigned)pm, num_kv_heads, num_seqs);
+  return hip_status(pa::launch_decode(a, head_size, block_size,
+                                      num_heads / num_kv_heads, grid, stream));
+}
+
+pa_status pa_decode_reduce(void* out, const void* workspace,
+                           size_t workspace_bytes,
+                           const int32_t* context_lens, int32_t num_seqs,
+                           int32_t num_heads, int32_t head_size,
+                           int32_t max_blocks_per_seq, int32_t block_size,
+                           int32_t partition_size, hipStream_t stream) {
+  if (num_seqs < 0 || num_heads <= 0 || max_blocks_per_seq <= 0 ||
+      num_seqs > 65535 || num_heads > 65535 || block_size <= 0 ||
+      partition_size <= 0 || partition_size % block_size != 0 ||
+      (int64_t)max_blocks_per_seq * block_size >= (1ll << 31))
+    return PA_ERR_SHAPE;
+  if (!supported_head(head_size) || !supported_block(block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !workspace || !context_lens) return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(workspace, 16) || !aligned(context_lens, 4))
+    return PA_ERR_ALIGN;
+  if (workspace_bytes < pa_splitk_workspace_size(num_seqs, num_heads, head_size,
+                                                 max_blocks_per_seq, block_size,
+                                                 partition_size))
+    return PA_ERR_WORKSPACE;
+  const int64_t pm = max_partitions(max_blocks_per_seq, block_size, partition_size);
+  const size_t rows = (size_t)num_seqs * num_heads * pm;
+  pa::ReduceArgs a = {};
+  a.out = static_cast<_Float16*>(out);
+  a.ws_max = static_cast<const float*>(workspace);
+  a.ws_sum = a.ws_max + rows;
+  a.ws_out = a.ws_sum + rows;
+  a.context_lens = context_lens;
+  a.num_heads = num_heads;
+  a.max_partitions = (int)pm;
+  a.partition_size = partition_size;
+  a.max_tokens = max_blocks_per_seq * block_size;
+  return hip_status(pa::launch_reduce(a, head_size, num_seqs, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Internal helpers shared by the HIP sources of the library (not part of
+// the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
+// no swizzle, no index stride.  Loads past num_records return zero without
+// touching memory, which is how padding slots are kept out of every read.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)bytes, kBufferRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r,
+                                        uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+}
+
+
+// Cross-lane moves inside a 16-lane DPP row (all lanes must be active).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                         0xF, 0xF, false));
+}
+
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Sum over aligned groups of LANES (8 or 16) lanes; every lane of a group
+// ends with the bitwise-identical total (each step adds two equal-order
+// partial sums, so the result does not depend on the lane).
+template <int LANES>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(LANES == 8 || LANES == 16, "group of 8 or 16 lanes");
+  v += dpp<kQuadXor1>(v);
+  v += dpp<kQuadXor2>(v);
+  v += dpp<kRowHalfMirror>(v);
+  if (LANES == 16) v += dpp<kRowMirror>(v);
+  return v;
+}
+
+// Reinterpret one 32-bit word as two fp16 values.  The word must arrive as
+// a scalar: with this compiler, bit-casting a vector element expression in
+// place (v.y, v.z, v.w) reads element x instead.
+__device__ __forceinline__ f16x2 as_h2(unsigned w) {
+  return __builtin_bit_cast(f16x2, w);
+}
+
+// Eight fp16 products of two 16-byte chunks accumulated in fp32
+// (v_dot2_f32_f16: exact fp16 products, fp32 sums).
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
+  const unsigned a0 = a.x, a1 = a.y, a2 = a.z, a3 = a.w;
+  const unsigned b0 = b.x, b1 = b.y, b2 = b.z, b3 = b.w;
+  float s = __builtin_amdgcn_fdot2(as_h2(a0), as_h2(b0), 0.f, false);
+  s = __builtin_amdgcn_fdot2(as_h2(a1), as_h2(b1), s, false);
+  s = __builtin_amdgcn_fdot2(as_h2(a2), as_h2(b2), s, false);
+  s = __builtin_amdgcn_fdot2(as_h2(a3), as_h2(b3), s, false);
+  return s;
+}
+
+__device__ __forceinline__ float half_at(u32x4 v, int e) {
+  const unsigned w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return (float)as_h2(w)[e & 1];
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);   // v_exp_f32; exp2(-inf) = 0
+}
+
+}  // namespace pa

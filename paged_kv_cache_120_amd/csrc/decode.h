@@ -1,0 +1,58 @@
+// Internal launch interface of the decode kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeArgs {
+  _Float16* out;             // [S, H, D]      single-pass mode
+  float* ws_max;             // [S, H, Pmax]   split mode
+  float* ws_sum;             // [S, H, Pmax]
+  float* ws_out;             // [S, H, Pmax, D]
+  const _Float16* query;     // [S, H, D]
+  const char* key_cache;     // [nb, B, H_kv, D] fp16
+  const char* value_cache;
+  const int* block_tables;   // [S, M]
+  const int* context_lens;   // [S]
+  int max_blocks_per_seq;
+  int num_heads;
+  int num_kv_heads;
+  int num_blocks;
+  int partition_size;        // tokens; a multiple of B
+  int max_partitions;        // Pmax (split mode)
+  int split;
+  float scale;
+};
+
+struct ReduceArgs {
+  _Float16* out;
+  const float* ws_max;
+  const float* ws_sum;
+  const float* ws_out;
+  const int* context_lens;
+  int num_heads;
+  int max_partitions;
+  int partition_size;
+  int max_tokens;            // M * B
+};
+
+hipError_t launch_decode(const DecodeArgs& a, int head_size, int block_size,
+                         int group, dim3 grid, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, int head_size, int num_seqs,
+                         hipStream_t stream);
+
+// cache operations
+hipError_t launch_slot_mapping(int* out, const int* block_tables, int M,
+                               int rows, const int* seq, const int* pos, int n,
+                               int block_size, hipStream_t stream);
+hipError_t launch_cache_write(const void* key, const void* value, void* kc,
+                              void* vc, const int* slots, int n,
+                              int64_t num_slots, int chunks_per_row,
+                              hipStream_t stream);
+hipError_t launch_copy_blocks(void* kc, void* vc, const int* src,
+                              const int* dst, int pairs, int num_blocks,
+                              int64_t chunks_per_block, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,149 @@
+"""Drive one decode step through the library on device tensors.
+
+A step is: copy-on-write block copies (if any), the slot mapping of the new
+tokens, the cache write, then decode -- single-pass (``pa_decode``) or split
+(``pa_decode_splitk`` + ``pa_decode_reduce``).  Inputs are plain arrays (a
+workload object with the attributes used below); this module only uploads
+them and calls the binding, so every step runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import (pa_cache_write, pa_copy_blocks, pa_decode, pa_decode_reduce,
+               pa_decode_splitk, pa_slot_mapping, pa_splitk_workspace_size)
+
+
+def _t(a, dev, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(dev)
+
+
+@dataclasses.dataclass
+class DevWrite:
+    table: torch.Tensor
+    seq: torch.Tensor
+    pos: torch.Tensor
+    key: torch.Tensor
+    value: torch.Tensor
+    slots: torch.Tensor
+
+
+@dataclasses.dataclass
+class DevCopy:
+    src: torch.Tensor
+    dst: torch.Tensor
+
+
+@dataclasses.dataclass
+class DeviceStep:
+    block_size: int
+    scale: float
+    partition_size: int
+    pool: torch.Tensor             # fp16 [2, nb, B, H_kv, D]
+    query: torch.Tensor            # fp16 [S, H, D]
+    block_tables: torch.Tensor     # int32 [S, M]
+    context_lens: torch.Tensor     # int32 [S]
+    out: torch.Tensor              # fp16 [S, H, D]
+    copies: Optional[DevCopy]
+    write: DevWrite
+    workspace: torch.Tensor        # uint8 split-KV workspace
+
+    @property
+    def key_cache(self):
+        return self.pool[0]
+
+    @property
+    def value_cache(self):
+        return self.pool[1]
+
+
+def _dev_phase(ph, dev):
+    if ph is None:
+        return None
+    if hasattr(ph, "src"):
+        return DevCopy(_t(ph.src, dev), _t(ph.dst, dev))
+    n = len(ph.pos)
+    return DevWrite(_t(ph.table, dev), _t(ph.seq, dev), _t(ph.pos, dev),
+                    _t(ph.key, dev), _t(ph.value, dev),
+                    torch.empty(n, dtype=torch.int32, device=dev))
+
+
+def run_phase(ph, pool, block_size: int, stream=None) -> None:
+    if ph is None:
+        return
+    if isinstance(ph, DevCopy):
+        pa_copy_blocks(pool[0], pool[1], ph.src, ph.dst, stream=stream)
+        return
+    pa_slot_mapping(ph.slots, ph.table, ph.seq, ph.pos, block_size, stream=stream)
+    pa_cache_write(ph.key, ph.value, pool[0], pool[1], ph.slots, stream=stream)
+
+
+def upload(w, device: str = "cuda", pool: Optional[torch.Tensor] = None) -> DeviceStep:
+    """Device copies of a workload's pool (initial garbage), decode inputs and
+    step phases.  ``pool`` reuses an existing device pool tensor."""
+    dev = torch.device(device)
+    if pool is None:
+        pool = _t(w.pool_init.view(np.float16), dev)
+    S, H, D = w.query.shape
+    ws = pa_splitk_workspace_size(S, H, D, w.max_blocks_per_seq, w.block_size,
+                                  w.partition_size)
+    return DeviceStep(
+        block_size=w.block_size, scale=w.scale, partition_size=w.partition_size,
+        pool=pool, query=_t(w.query, dev), block_tables=_t(w.block_tables, dev),
+        context_lens=_t(w.context_lens, dev),
+        out=torch.empty((S, H, D), dtype=torch.float16, device=dev),
+        copies=_dev_phase(w.step_copies, dev), write=_dev_phase(w.step_write, dev),
+        workspace=torch.empty(max(ws, 16), dtype=torch.uint8, device=dev))
+
+
+def apply_history(w, step: DeviceStep, stream=None) -> None:
+    """Bring the device pool to the pre-step state (prefill writes, COW)."""
+    for ph in w.history:
+        d = _dev_phase(ph, step.pool.device)
+        run_phase(d, step.pool, w.block_size, stream=stream)
+        del d
+
+
+def write_step(step: DeviceStep, stream=None) -> None:
+    run_phase(step.copies, step.pool, step.block_size, stream=stream)
+    run_phase(step.write, step.pool, step.block_size, stream=stream)
+
+
+def decode_step(step: DeviceStep, mode: str = "splitk", stream=None) -> None:
+    if mode == "single":
+        pa_decode(step.out, step.query, step.key_cache, step.value_cache,
+                  step.block_tables, step.context_lens, step.scale, stream=stream)
+    elif mode == "splitk":
+        pa_decode_splitk(step.query, step.key_cache, step.value_cache,
+                         step.block_tables, step.context_lens, step.scale,
+                         step.partition_size, step.workspace, stream=stream)
+        pa_decode_reduce(step.out, step.workspace, step.context_lens,
+                         step.block_tables.shape[1], step.block_size,
+                         step.partition_size, stream=stream)
+    else:
+        raise ValueError(mode)
+
+
+def full_step(step: DeviceStep, mode: str = "splitk", stream=None) -> None:
+    write_step(step, stream=stream)
+    decode_step(step, mode=mode, stream=stream)
+
+
+def split_views(step: DeviceStep, S: int, H: int, D: int, M: int, B: int, P: int):
+    """(max_logits, exp_sums, tmp_out) views of the split-KV workspace."""
+    pm = (M * B + P - 1) // P
+    rows = S * H * pm
+    f = step.workspace[: (2 * rows + rows * D) * 4].view(torch.float32)
+    return (f[:rows].view(S, H, pm), f[rows:2 * rows].view(S, H, pm),
+            f[2 * rows:].view(S, H, pm, D))
+
+
+__all__: List[str] = ["DeviceStep", "upload", "apply_history", "write_step",
+                      "decode_step", "full_step", "run_phase", "split_views"]

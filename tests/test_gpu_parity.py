@@ -1,0 +1,310 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on MI355X.
+
+Cache writes, slot mappings and block copies must be bit-exact over the
+whole pool; attention outputs must satisfy, elementwise,
+|y - r| <= 2e-3  or  |y - r| <= 1e-2 * |r|
+(fp16 I/O, fp32 accumulation) against the float64 oracle r."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.helpers import oracle_pool
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+RTOL = 1e-2
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_120_amd as pa
+    from paged_kv_cache_120_amd import runner
+    return pa, runner
+
+
+def assert_attention_close(y, r, what=""):
+    y = np.asarray(y, np.float64)
+    err = np.abs(y - r)
+    ok = (err <= ATOL) | (err <= RTOL * np.abs(r))
+    big = np.abs(r) >= 0.2
+    rel = (err[big] / np.abs(r[big])).max() if big.any() else 0.0
+    assert np.isfinite(y).all(), f"{what}: non-finite output"
+    assert ok.all(), (f"{what}: {int((~ok).sum())} of {ok.size} outside tolerance; "
+                      f"max abs {err.max():.3e}, max rel {rel:.3e}")
+    return float(err.max()), float(rel)
+
+
+def run_gpu(w, mode, stream=None):
+    pa, runner = _gpu()
+    st = runner.upload(w)
+    runner.apply_history(w, st)
+    runner.full_step(st, mode=mode)
+    torch.cuda.synchronize()
+    return st
+
+
+def check_all(w, mode, full_oracle=True, pairs=None):
+    st = run_gpu(w, mode)
+    kc, vc = oracle_pool(w, oracle)
+    gpool = st.pool.cpu().numpy().view(np.uint16)
+    assert (gpool[0] == kc).all(), "key cache differs from the oracle's"
+    assert (gpool[1] == vc).all(), "value cache differs from the oracle's"
+    ref_slots = oracle.slot_mapping(w.step_write.table, w.step_write.seq,
+                                    w.step_write.pos, w.block_size)
+    assert (st.write.slots.cpu().numpy() == ref_slots).all()
+    out = st.out.cpu().numpy()
+    if full_oracle:
+        ref = oracle.decode(w.query, kc, vc, w.block_tables, w.context_lens, w.scale)
+        assert_attention_close(out, ref, f"{w.name}/{mode}")
+    else:
+        ref = oracle.decode_heads(w.query, kc, vc, w.block_tables, w.context_lens,
+                                  w.scale, pairs)
+        got = np.stack([out[i, h] for i, h in pairs])
+        assert_attention_close(got, ref, f"{w.name}/{mode} sampled")
+    return st, kc, vc
+
+
+SMALL = ["c1", "c1_page_tables", "c2_small", "c3_small", "c4_small", "c4_r0_small",
+         "c5_b32_small", "c5_b64_small"]
+
+
+@pytest.mark.parametrize("mode", ["single", "splitk"])
+@pytest.mark.parametrize("name", SMALL)
+def test_parity_small(name, mode):
+    print(f"[parity] {name} {mode}", flush=True)
+    check_all(workloads.make(name), mode)
+
+
+@pytest.mark.parametrize("name", ["c3_small", "c5_b32_small", "c2_small"])
+def test_split_partials_match_oracle(name):
+    print(f"[partials] {name}", flush=True)
+    pa, runner = _gpu()
+    w = workloads.make(name)
+    st = run_gpu(w, "splitk")
+    kc, vc = oracle_pool(w, oracle)
+    S, H, D = w.query.shape
+    M, B, P = w.max_blocks_per_seq, w.block_size, w.partition_size
+    gm, gs, go = [t.cpu().numpy().astype(np.float64)
+                  for t in runner.split_views(st, S, H, D, M, B, P)]
+    pm = gm.shape[2]
+    m, s, O = oracle.partials(w.query, kc, vc, w.block_tables, w.context_lens,
+                              w.scale, P, pm)
+    for i, n in enumerate(w.context_lens):
+        used = (int(n) + P - 1) // P
+        assert np.allclose(gm[i, :, :used], m[i, :, :used], rtol=1e-5, atol=1e-5)
+        assert np.allclose(gs[i, :, :used], s[i, :, :used], rtol=2e-3, atol=1e-5)
+        scale = s[i, :, :used, None]
+        assert np.allclose(go[i, :, :used] / scale, O[i, :, :used] / scale,
+                           rtol=1e-2, atol=2e-3)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,mode", [("c1", "splitk"), ("c2", "splitk"), ("c2", "single"),
+                                       ("c3", "splitk"), ("c4", "splitk")])
+def test_parity_full(name, mode):
+    print(f"[parity-full] {name} {mode}", flush=True)
+    check_all(workloads.make(name), mode)
+
+
+@pytest.mark.parametrize("name", ["c5_b32", "c5_b64"])
+def test_parity_full_long_context_sampled(name):
+    print(f"[parity-full] {name} splitk (sampled heads)", flush=True)
+    w = workloads.make(name)
+    rng = np.random.default_rng(7)
+    pairs = [(i, int(h)) for i in range(w.num_seqs)
+             for h in rng.choice(w.num_heads, 6, replace=False)]
+    pairs += [(int(np.argmax(w.context_lens)), 0), (int(np.argmin(w.context_lens)), 63)]
+    check_all(w, "splitk", full_oracle=False, pairs=sorted(pairs))
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+EDGE_LENS = [1, 2, 15, 16, 17, 31, 33, 511, 512, 513, 1023, 1024, 1025, 2047, 2048]
+
+
+@pytest.mark.parametrize("mode", ["single", "splitk"])
+@pytest.mark.parametrize("D,B,H,Hkv", [(128, 16, 32, 8), (64, 64, 16, 2),
+                                       (128, 32, 8, 8), (64, 16, 8, 4),
+                                       (128, 64, 16, 8)])
+def test_edge_lengths(D, B, H, Hkv, mode):
+    print(f"[edge] D{D} B{B} H{H}/{Hkv} {mode}", flush=True)
+    w = workloads.make("c1", D=D, B=B, H=H, Hkv=Hkv, lens=EDGE_LENS,
+                       pool=("choice_scale", 1.3), max_context=2048, seed=D + B + H)
+    check_all(w, mode)
+
+
+@pytest.mark.parametrize("mode", ["single", "splitk"])
+def test_full_table(mode):
+    """context_len = max_blocks_per_seq * block_size (every entry used)."""
+    w = workloads.make("c1", D=128, B=32, H=16, Hkv=4, lens=[640, 1, 640, 639],
+                       pool=("choice_scale", 1.0), max_context=640, seed=3)
+    assert w.max_blocks_per_seq * w.block_size == 640
+    check_all(w, mode)
+
+
+@pytest.mark.parametrize("mode", ["single", "splitk"])
+def test_nonfinite_garbage_is_never_read(mode):
+    w = workloads.make("c3_small", garbage="nonfinite")
+    check_all(w, mode)
+
+
+@pytest.mark.parametrize("P", [16, 64, 256, 1024, 4096])
+def test_splitk_partition_sizes(P):
+    w = workloads.make("c3_small")
+    w.partition_size = P
+    check_all(w, "splitk")
+
+
+@pytest.mark.parametrize("mode", ["single", "splitk"])
+def test_zero_context_gives_zeros(mode):
+    pa, runner = _gpu()
+    w = workloads.make("c2_small")
+    st = runner.upload(w)
+    runner.apply_history(w, st)
+    runner.write_step(st)
+    ctx = w.context_lens.copy()
+    ctx[2] = 0
+    st.context_lens.copy_(torch.from_numpy(ctx))
+    runner.decode_step(st, mode)
+    torch.cuda.synchronize()
+    out = st.out.cpu().numpy().astype(np.float64)
+    assert (out[2] == 0).all()
+    kc, vc = oracle_pool(w, oracle)
+    keep = [i for i in range(w.num_seqs) if i != 2]
+    ref = oracle.decode(w.query[keep], kc, vc, w.block_tables[keep], ctx[keep], w.scale)
+    assert_attention_close(out[keep], ref, "zero-context neighbours")
+
+
+def test_permutation_invariance_bitwise():
+    """Relabelling physical blocks leaves the GPU result bit-identical."""
+    pa, runner = _gpu()
+    w = workloads.make("c3_small")
+    outs = []
+    for relabel in (False, True):
+        st = runner.upload(w)
+        runner.apply_history(w, st)
+        runner.write_step(st)
+        if relabel:
+            perm = np.random.default_rng(11).permutation(w.num_blocks)
+            inv = torch.from_numpy(np.argsort(perm)).cuda()
+            newpool = st.pool[:, inv].contiguous()        # newpool[:, perm[b]] = pool[:, b]
+            st.pool = newpool
+            st.block_tables = torch.from_numpy(perm[w.block_tables].astype(np.int32)).cuda()
+        for mode in ("single", "splitk"):
+            runner.decode_step(st, mode)
+            torch.cuda.synchronize()
+            outs.append(st.out.cpu().numpy().copy())
+    assert (outs[0].view(np.uint16) == outs[2].view(np.uint16)).all()
+    assert (outs[1].view(np.uint16) == outs[3].view(np.uint16)).all()
+
+
+def test_shared_prefix_equals_private_copies_bitwise():
+    pa, runner = _gpu()
+    w = workloads.make("c4_small")
+    st = run_gpu(w, "splitk")
+    shared = st.out.cpu().numpy().copy()
+    # private layout built on the device: every sample gets copies of its blocks
+    S, M = w.num_seqs, w.max_blocks_per_seq
+    total = int(w.blocks_used.sum())
+    src, tables = [], np.zeros((S, M), np.int32)
+    nxt = 0
+    for i in range(S):
+        for lb in range(int(w.blocks_used[i])):
+            src.append(int(w.block_tables[i, lb]))
+            tables[i, lb] = nxt
+            nxt += 1
+    pool2 = torch.empty((2, total) + tuple(st.pool.shape[2:]), dtype=torch.float16,
+                        device="cuda")
+    idx = torch.tensor(src, dtype=torch.int64, device="cuda")
+    pool2.copy_(st.pool[:, idx])
+    st.pool = pool2
+    st.block_tables = torch.from_numpy(tables).cuda()
+    runner.decode_step(st, "splitk")
+    torch.cuda.synchronize()
+    assert (st.out.cpu().numpy().view(np.uint16) == shared.view(np.uint16)).all()
+
+
+def test_repeat_calls_deterministic():
+    pa, runner = _gpu()
+    w = workloads.make("c2_small")
+    st = run_gpu(w, "splitk")
+    a = st.out.cpu().numpy().copy()
+    runner.decode_step(st, "splitk")
+    torch.cuda.synchronize()
+    assert (a.view(np.uint16) == st.out.cpu().numpy().view(np.uint16)).all()
+
+
+def test_cache_write_skips_negative_and_out_of_range_slots():
+    pa, runner = _gpu()
+    nb, B, Hkv, D = 6, 16, 2, 64
+    rng = np.random.default_rng(5)
+    pool = rng.integers(0, 1 << 16, (2, nb, B, Hkv, D), dtype=np.uint16)
+    key = rng.integers(0, 1 << 16, (4, Hkv, D), dtype=np.uint16)
+    val = rng.integers(0, 1 << 16, (4, Hkv, D), dtype=np.uint16)
+    slots = np.array([3, -1, nb * B, 95], np.int32)
+    gp = torch.from_numpy(pool.view(np.float16)).cuda()
+    pa.pa_cache_write(torch.from_numpy(key.view(np.float16)).cuda(),
+                      torch.from_numpy(val.view(np.float16)).cuda(), gp[0], gp[1],
+                      torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    kc, vc = pool[0].copy(), pool[1].copy()
+    oracle.cache_write(kc, vc, key, val, np.where(slots < nb * B, slots, -1))
+    g = gp.cpu().numpy().view(np.uint16)
+    assert (g[0] == kc).all() and (g[1] == vc).all()
+
+
+def test_copy_blocks_parity():
+    pa, runner = _gpu()
+    nb, B, Hkv, D = 9, 32, 4, 128
+    rng = np.random.default_rng(6)
+    pool = rng.integers(0, 1 << 16, (2, nb, B, Hkv, D), dtype=np.uint16)
+    src = np.array([1, 4, 7, 2], np.int32)
+    dst = np.array([0, 5, 8, 99], np.int32)          # last pair out of range: skipped
+    gp = torch.from_numpy(pool.view(np.float16)).cuda()
+    pa.pa_copy_blocks(gp[0], gp[1], torch.from_numpy(src).cuda(),
+                      torch.from_numpy(dst).cuda())
+    torch.cuda.synchronize()
+    kc, vc = pool[0].copy(), pool[1].copy()
+    oracle.copy_blocks(kc, vc, src[:3], dst[:3])
+    g = gp.cpu().numpy().view(np.uint16)
+    assert (g[0] == kc).all() and (g[1] == vc).all()
+
+
+def test_slot_mapping_parity_and_guards():
+    pa, runner = _gpu()
+    rng = np.random.default_rng(8)
+    M, B = 12, 16
+    table = rng.integers(0, 500, (5, M)).astype(np.int32)
+    seq = rng.integers(0, 5, 300).astype(np.int32)
+    pos = rng.integers(0, M * B, 300).astype(np.int32)
+    seq[:3] = [5, -1, 0]
+    pos[2] = M * B
+    out = torch.empty(300, dtype=torch.int32, device="cuda")
+    pa.pa_slot_mapping(out, torch.from_numpy(table).cuda(), torch.from_numpy(seq).cuda(),
+                       torch.from_numpy(pos).cuda(), B)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert (got[:3] == -1).all()
+    ref = oracle.slot_mapping(table, seq[3:], pos[3:], B)
+    assert (got[3:] == ref).all()
+
+
+def test_empty_batch_is_noop():
+    pa, runner = _gpu()
+    z = torch.zeros((0, 8, 128), dtype=torch.float16, device="cuda")
+    kc = torch.zeros((4, 16, 2, 128), dtype=torch.float16, device="cuda")
+    bt = torch.zeros((0, 4), dtype=torch.int32, device="cuda")
+    cl = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    pa.pa_decode(z, z, kc, kc, bt, cl, 0.1)
+    s = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    pa.pa_cache_write(z[:, :2], z[:, :2], kc, kc, s)
+    torch.cuda.synchronize()
