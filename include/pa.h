@@ -151,7 +151,8 @@ size_t pa_splitk_workspace_size(int32_t num_seqs, int32_t num_heads,
 /*
  * pa_decode_splitk -- per-partition softmax state for split-KV decode.
  *   Partition p of sequence i is tokens [p*P, min((p+1)*P, n_i)) with
- *   P = partition_size (a multiple of block_size, at most 8192).  For each
+ *   P = partition_size (a multiple of block_size; Pmax below must not
+ *   exceed 65535).  For each
  *   non-empty (i, h, p) it stores, with x_t = scale * <query[i,h], K_t>:
  *     max_logits[i,h,p] = m = max_t x_t
  *     exp_sums[i,h,p]   = sum_t exp(x_t - m)

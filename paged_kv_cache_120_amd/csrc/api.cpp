@@ -170,7 +170,7 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
   a.max_partitions = 1;
   a.split = 0;
   a.scale = scale;
-  dim3 grid(1, num_kv_heads, num_seqs);
+  dim3 grid(num_kv_heads, num_seqs, 1);
   return hip_status(pa::launch_decode(a, head_size, block_size,
                                       num_heads / num_kv_heads, grid, stream));
 }
@@ -205,7 +205,7 @@ pa_status pa_decode_splitk(const void* query, const void* key_cache,
     return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   const int64_t pm = max_partitions(max_blocks_per_seq, block_size, partition_size);
-  if (pm > 65535 * 32) return PA_ERR_SHAPE;
+  if (pm > 65535) return PA_ERR_SHAPE;        // grid.z
   if (!workspace) return PA_ERR_NULL;
   if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
   if (workspace_bytes < pa_splitk_workspace_size(num_seqs, num_heads, head_size,
@@ -230,7 +230,7 @@ pa_status pa_decode_splitk(const void* query, const void* key_cache,
   a.max_partitions = (int)pm;
   a.split = 1;
   a.scale = scale;
-  dim3 grid((unsigned)pm, num_kv_heads, num_seqs);
+  dim3 grid(num_kv_heads, num_seqs, (unsigned)pm);
   return hip_status(pa::launch_decode(a, head_size, block_size,
                                       num_heads / num_kv_heads, grid, stream));
 }

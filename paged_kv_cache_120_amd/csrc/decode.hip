@@ -4,7 +4,7 @@
 // (walk the block table in logical order, read each physical block) and §4.6
 // (online softmax; fp32 statistics and accumulators).
 //
-// Work decomposition.  One workgroup (4 waves) owns one (sequence, kv head,
+// Work decomposition.  One workgroup (4 waves) owns one (kv head, sequence,
 // partition).  A partition is a run of whole blocks (P tokens, P a multiple of
 // the block size); the single-pass entry point uses one partition per
 // sequence.  The workgroup serves all g query heads of its kv head, so each
@@ -49,9 +49,14 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
   __shared__ float sm_m[NW][G];
   __shared__ float sm_l[NW][G];
 
-  const int p = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int seq = blockIdx.z;
+  // grid (kv heads, sequences, partitions): consecutive workgroup ids -- which
+  // the dispatcher deals round-robin to the 8 XCDs -- differ in kv head and
+  // sequence, so every XCD gets a share of each partition index; partition 0
+  // of every sequence is dispatched first, the (possibly empty) later
+  // partitions last.
+  const int kvh = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int p = blockIdx.z;
   const int H = a.num_heads;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
