@@ -119,6 +119,43 @@ def cpu_baseline(w, gpu_out=None, min_s: float = 10.0, max_s: float = 30.0):
     }
 
 
+KERNEL_SOURCES = ["paged_kv_cache_120_amd/csrc/decode.hip",
+                  "paged_kv_cache_120_amd/csrc/common.h",
+                  "paged_kv_cache_120_amd/csrc/decode.h"]
+
+
+def kernel_source_hash(root: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(args, root: str):
+    """HBM bytes per launch of the decode kernel from the committed counter
+    summary for this workload and mode, if it was taken on the current
+    kernel sources (else None)."""
+    path = os.path.join(root, "profiles",
+                        f"decode_partition_kernel_{args.config}_{args.mode}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    t = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                t[k.strip()] = v.strip()
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(root) or \
+            t.get("partition_size") != str(args.partition):
+        return None
+    try:
+        return int(float(t["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +166,9 @@ def main(argv=None) -> int:
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--partition", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", type=int, default=0, metavar="PAIRS",
+                    help="after timing, copy PAIRS unreferenced blocks with "
+                         "pa_copy_blocks (known bytes) to calibrate HBM counters")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -194,12 +234,27 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
+    calib = None
+    if args.calibrate:
+        free = np.flatnonzero(w.ref_cnt == 0)
+        k = min(args.calibrate, len(free) // 2)
+        if k > 0:
+            src = torch.from_numpy(free[:k].astype(np.int32)).to(dev)
+            dst = torch.from_numpy(free[k:2 * k].astype(np.int32)).to(dev)
+            torch.cuda.synchronize()
+            pa.pa_copy_blocks(steps[0].key_cache, steps[0].value_cache, src, dst)
+            torch.cuda.synchronize()
+            blk = w.block_size * w.num_kv_heads * w.head_size * 2
+            calib = {"kernel": "copy_blocks_kernel", "pairs": int(k),
+                     "read_bytes": int(2 * k * blk), "write_bytes": int(2 * k * blk)}
+
     kvb = kv_bytes(w)
     kb = split_kernel_bytes(w) if args.mode == "splitk" else single_kernel_bytes(w)
     achieved = kb / (kms * 1e-3) / 1e9
     value = kvb / (ms_step * 1e-3) / 1e9
 
     gpu_out = steps[(args.steps - 1) % R].out.cpu().numpy()
+    traffic = load_traffic(args, ROOT)
 
     rec = {
         "metric": METRIC,
@@ -229,12 +284,14 @@ def main(argv=None) -> int:
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "decode_partition_kernel" if args.mode == "splitk"
             else "decode_partition_kernel (single pass)",
             "kernel_ms": round(kms, 5), "algorithmic_bytes": kb,
         },
     }
+    if calib:
+        rec["copy_calibration"] = calib
     if not args.no_cpu_baseline:
         rec["parity"], rec["cpu_baseline"] = cpu_baseline(w, gpu_out)
     print(json.dumps(rec), flush=True)

@@ -188,6 +188,44 @@ pa_status pa_decode_reduce(void* out, const void* workspace,
                            int32_t max_blocks_per_seq, int32_t block_size,
                            int32_t partition_size, hipStream_t stream);
 
+/*
+ * Balanced split-KV decode: the same result as pa_decode (within the same
+ * tolerance; the summation order differs), with the work divided evenly
+ * instead of by fixed partitions.  The KV work of all (sequence, kv head)
+ * pairs is laid end to end -- sequence-major, then kv head, then token, each
+ * sequence padded to a multiple of 16 tokens -- and cut into `grid` equal
+ * slices, one per workgroup; a workgroup writes one partial softmax state
+ * (max, sum, unnormalised output; the form of [BOOK] §4.6) for every pair its
+ * slice touches, and a second kernel merges each pair's states with the
+ * §4.6 recurrence.  With `grid` = pa_balanced_grid(...) every workgroup is
+ * resident from the start, so none waits and none straggles.
+ *
+ * pa_balanced_grid: workgroups of the balanced kernel that the current
+ *   device holds at once for this shape (0 if unsupported or unknown).
+ * pa_balanced_workspace_size: bytes of device workspace for `grid`
+ *   workgroups (0 on bad arguments).  Layout: [total int64][prefix int64 x
+ *   num_seqs] padded to 16 bytes, then fp32 max [rows], sum [rows], out
+ *   [rows, head_size] with rows = (grid + num_seqs*num_kv_heads) * group.
+ * pa_decode_balanced: arguments as pa_decode plus grid (> 0) and the
+ *   workspace (16-byte aligned, >= pa_balanced_workspace_size).  Enqueues
+ *   two kernels on `stream`.  Same preconditions and guards as pa_decode.
+ */
+int32_t pa_balanced_grid(int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size);
+size_t pa_balanced_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_size,
+                                  int32_t grid);
+pa_status pa_decode_balanced(void* out, const void* query,
+                             const void* key_cache, const void* value_cache,
+                             const int32_t* block_tables,
+                             int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs,
+                             int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_size, int32_t block_size,
+                             int32_t num_blocks, float scale, int32_t grid,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

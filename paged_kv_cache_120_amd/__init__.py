@@ -18,6 +18,7 @@ __all__ = [
     "PaError", "lib", "library_path", "pa_status_str", "pa_kv_cache_shape",
     "pa_slot_mapping", "pa_cache_write", "pa_copy_blocks", "pa_decode",
     "pa_splitk_workspace_size", "pa_decode_splitk", "pa_decode_reduce",
+    "pa_balanced_grid", "pa_balanced_workspace_size", "pa_decode_balanced",
     "STATUS",
 ]
 
@@ -57,6 +58,10 @@ def _load() -> ctypes.CDLL:
                                             i32, i32, f32, i32, vp, sz, vp]),
         "pa_decode_reduce": (ctypes.c_int, [vp, vp, sz, vp, i32, i32, i32, i32, i32,
                                             i32, vp]),
+        "pa_balanced_grid": (i32, [i32, i32, i32, i32]),
+        "pa_balanced_workspace_size": (sz, [i32, i32, i32, i32, i32]),
+        "pa_decode_balanced": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
+                                              i32, i32, i32, f32, i32, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -98,6 +103,19 @@ def pa_splitk_workspace_size(num_seqs: int, num_heads: int, head_size: int,
     return int(_lib().pa_splitk_workspace_size(num_seqs, num_heads, head_size,
                                             max_blocks_per_seq, block_size,
                                             partition_size))
+
+
+def pa_balanced_grid(num_heads: int, num_kv_heads: int, head_size: int,
+                     block_size: int) -> int:
+    """Workgroups of the balanced decode the current device holds at once
+    (0 if unknown).  Initialises the HIP runtime on the current device."""
+    return int(_lib().pa_balanced_grid(num_heads, num_kv_heads, head_size, block_size))
+
+
+def pa_balanced_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int,
+                               head_size: int, grid: int) -> int:
+    return int(_lib().pa_balanced_workspace_size(num_seqs, num_heads, num_kv_heads,
+                                                 head_size, grid))
 
 
 # ---------------------------------------------------------------------------
@@ -233,3 +251,20 @@ def pa_decode_reduce(out, workspace, context_lens, max_blocks_per_seq: int,
         _dev(context_lens, torch.int32, "context_lens", 1), S, H, D,
         int(max_blocks_per_seq), int(block_size), int(partition_size),
         _stream(stream)))
+
+
+def pa_decode_balanced(out, query, key_cache, value_cache, block_tables,
+                       context_lens, scale: float, grid: int, workspace,
+                       stream=None) -> None:
+    """Balanced split-KV decode (two kernels); workspace: a contiguous device
+    tensor of at least pa_balanced_workspace_size(...) bytes."""
+    torch = _torch()
+    (q, kc, vc, bt, cl), (S, H, Hkv, D, B, nb, M) = _decode_common(
+        query, key_cache, value_cache, block_tables, context_lens)
+    if tuple(out.shape) != (S, H, D):
+        raise ValueError("pa_decode_balanced: out shape")
+    ws = _dev(workspace, workspace.dtype, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("pa_decode_balanced", _lib().pa_decode_balanced(
+        _dev(out, torch.float16, "out", 3), q, kc, vc, bt, M, cl, S, H, Hkv, D, B, nb,
+        float(scale), int(grid), ws, nbytes, _stream(stream)))

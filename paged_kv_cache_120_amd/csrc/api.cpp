@@ -271,4 +271,93 @@ pa_status pa_decode_reduce(void* out, const void* workspace,
   return hip_status(pa::launch_reduce(a, head_size, num_seqs, stream));
 }
 
+int32_t pa_balanced_grid(int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size) {
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+      !supported_head(head_size) || !supported_block(block_size) ||
+      !supported_group(num_heads / num_kv_heads))
+    return 0;
+  return pa::balanced_grid(head_size, block_size, num_heads / num_kv_heads);
+}
+
+// [total int64][prefix int64 x S] padded to 16 bytes, then max, sum (fp32
+// [rows]) and out (fp32 [rows, D]) with rows = (grid + S*H_kv) * g.
+static size_t balanced_header_bytes(int32_t num_seqs) {
+  return ((size_t)(1 + num_seqs) * 8 + 15) & ~(size_t)15;
+}
+
+size_t pa_balanced_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_size,
+                                  int32_t grid) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+      grid <= 0 || num_heads % num_kv_heads != 0)
+    return 0;
+  const uint64_t rows = ((uint64_t)grid + (uint64_t)num_seqs * num_kv_heads) *
+                        (uint64_t)(num_heads / num_kv_heads);
+  return balanced_header_bytes(num_seqs) + (size_t)(rows * 8 + rows * head_size * 4);
+}
+
+pa_status pa_decode_balanced(void* out, const void* query, const void* key_cache,
+                             const void* value_cache,
+                             const int32_t* block_tables,
+                             int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs,
+                             int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_size, int32_t block_size,
+                             int32_t num_blocks, float scale, int32_t grid,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  pa_status st = check_decode(query, key_cache, value_cache, block_tables,
+                              max_blocks_per_seq, context_lens, num_seqs,
+                              num_heads, num_kv_heads, head_size, block_size,
+                              num_blocks, scale);
+  if (st != PA_OK) return st;
+  if (grid <= 0 || grid > (1 << 20)) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !workspace) return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(workspace, 16)) return PA_ERR_ALIGN;
+  if (workspace_bytes < pa_balanced_workspace_size(num_seqs, num_heads,
+                                                   num_kv_heads, head_size, grid))
+    return PA_ERR_WORKSPACE;
+  const int32_t g = num_heads / num_kv_heads;
+  const size_t rows = ((size_t)grid + (size_t)num_seqs * num_kv_heads) * g;
+  char* ws = static_cast<char*>(workspace);
+  int64_t* total = reinterpret_cast<int64_t*>(ws);
+  int64_t* prefix = total + 1;
+  float* fmax = reinterpret_cast<float*>(ws + balanced_header_bytes(num_seqs));
+  pa::DecodeArgs a = {};
+  a.ws_max = fmax;
+  a.ws_sum = fmax + rows;
+  a.ws_out = fmax + 2 * rows;
+  a.query = static_cast<const _Float16*>(query);
+  a.key_cache = static_cast<const char*>(key_cache);
+  a.value_cache = static_cast<const char*>(value_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.bal_total = total;
+  a.bal_prefix = prefix;
+  a.split = 1;
+  a.scale = scale;
+  st = hip_status(pa::launch_balanced(a, head_size, block_size, g, grid, stream));
+  if (st != PA_OK) return st;
+  pa::BalancedReduceArgs r = {};
+  r.out = static_cast<_Float16*>(out);
+  r.ws_max = a.ws_max;
+  r.ws_sum = a.ws_sum;
+  r.ws_out = a.ws_out;
+  r.context_lens = context_lens;
+  r.total = total;
+  r.prefix = prefix;
+  r.num_heads = num_heads;
+  r.num_kv_heads = num_kv_heads;
+  r.grid = grid;
+  r.max_tokens = max_blocks_per_seq * block_size;
+  return hip_status(pa::launch_balanced_reduce(r, head_size, num_seqs, stream));
+}
+
 }  // extern "C"

@@ -23,7 +23,24 @@ struct DecodeArgs {
   int partition_size;        // tokens; a multiple of B
   int max_partitions;        // Pmax (split mode)
   int split;
+  int num_seqs;              // balanced split
+  int64_t* bal_total;        // [1]  sum of padded lengths (per kv head)
+  int64_t* bal_prefix;       // [S]  exclusive prefix of padded lengths
   float scale;
+};
+
+struct BalancedReduceArgs {
+  _Float16* out;
+  const float* ws_max;
+  const float* ws_sum;
+  const float* ws_out;
+  const int* context_lens;
+  const int64_t* total;
+  const int64_t* prefix;
+  int num_heads;
+  int num_kv_heads;
+  int grid;
+  int max_tokens;            // M * B
 };
 
 struct ReduceArgs {
@@ -42,6 +59,13 @@ hipError_t launch_decode(const DecodeArgs& a, int head_size, int block_size,
                          int group, dim3 grid, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_size, int num_seqs,
                          hipStream_t stream);
+hipError_t launch_balanced(const DecodeArgs& a, int head_size, int block_size,
+                           int group, int grid, hipStream_t stream);
+hipError_t launch_balanced_reduce(const BalancedReduceArgs& a, int head_size,
+                                  int num_seqs, hipStream_t stream);
+// workgroups of the balanced kernel resident at once on the current device
+// (0 if it cannot be determined)
+int balanced_grid(int head_size, int block_size, int group);
 
 // cache operations
 hipError_t launch_slot_mapping(int* out, const int* block_tables, int M,

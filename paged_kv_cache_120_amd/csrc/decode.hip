@@ -2,33 +2,32 @@
 //
 // What it computes: vLLM book ch.4 "PagedAttention：虚拟内存的启示", §4.5
 // (walk the block table in logical order, read each physical block) and §4.6
-// (online softmax; fp32 statistics and accumulators).
+// (online softmax; fp32 statistics and accumulators).  For sequence i and
+// query head h, over exactly context_len tokens:
+//   out[i,h] = sum_t softmax_t(scale <q[i,h], K_t>) V_t,  kv head = h / g.
 //
-// Work decomposition.  One workgroup (4 waves) owns one (kv head, sequence,
-// partition).  A partition is a run of whole blocks (P tokens, P a multiple of
-// the block size); the single-pass entry point uses one partition per
-// sequence.  The workgroup serves all g query heads of its kv head, so each
-// K/V byte is fetched from HBM once and reused from registers g times.
+// A workgroup (4 waves) processes a token range [t0, t1) of one (kv head,
+// sequence) and serves all g query heads of that kv head, so each K/V byte is
+// fetched from HBM once and reused g times.  Two range bodies exist:
+//   ValuPath -- vector ALU, dot products reduced with DPP (g = 1, 2, 4);
+//   MfmaPath -- both contractions on the matrix cores (g = 8).
+// Kernels driving them:
+//   partition_kernel -- one range per workgroup: a whole sequence (single
+//                       pass) or one fixed partition (split-KV);
+//   balanced_kernel  -- a grid sized to the workgroups the chip holds at
+//                       once; each takes an equal slice of all the KV work
+//                       (possibly several ranges) and writes one partial
+//                       state per range;
+//   reduce_kernel / balanced_reduce_kernel -- merge partial states with the
+//                       §4.6 recurrence.
 //
-// Inside a wave, a 16-byte load per lane covers one token row of one head
-// (D/8 lanes per row), so one load instruction reads D*2*64/16 bytes of
-// consecutive memory per row group -- whole 128-byte lines.  A wave walks a
-// batch of TB tokens (NJ loads of K and NJ of V per lane in flight at once);
-// the four waves take batches round-robin.  Physical block ids for the
-// partition are fetched once with one vector load per wave (lane k holds
-// logical block k of the current 64-block window) and broadcast with
-// v_readlane, so the table read sits off the critical path of the K/V loads.
-// Each block gets its own buffer resource whose record count ends at the
-// last valid token: slots past context_len are never fetched, so padding may
-// hold anything (Inf/NaN included) without reaching the result.
-//
-// Each row group (D/8 lanes = one token of a load) keeps its own online
-// softmax state (m, l, acc[8] per head, replicated in the row).  The dot
-// product is reduced across the row with four DPP adds (bitwise identical in
-// every lane); everything else is lane-local until the end, where the row
-// groups are merged with cross-lane shuffles, and the waves through LDS.
-// Scores are kept in base-2 units (x * log2 e) so every exponential is a
-// single v_exp_f32.
+// Common to both bodies: K/V rows are read with 16-byte buffer loads whose
+// resource is rebased per physical block (64-bit base in SGPRs) with a record
+// count that ends at the last valid token, so slots past context_len are
+// never fetched (padding may hold Inf/NaN).  The loads are non-temporal: each
+// byte is used once per step.  Block ids for a 64-block window come from one
+// vector load per wave and are broadcast with v_readlane.  Scores are kept in
+// base-2 units (x log2 e) so every exponential is one v_exp_f32.
 #include "common.h"
 #include "decode.h"
 
@@ -36,33 +35,416 @@ namespace pa {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWaves = 4;
 
+// Physical block ids of logical blocks [win, win + 64) of one sequence, one
+// per lane; entries at or past `end` are never read from the table.
+struct BlockWindow {
+  const int* bt;
+  int end;
+  int win;
+  int ids;
+  __device__ void init(const int* row, int first, int end_, int lane) {
+    bt = row;
+    end = end_;
+    win = first;
+    ids = (win + lane < end) ? bt[win + lane] : 0;
+  }
+  // make the window hold logical blocks first .. last (last - first < 64)
+  __device__ void cover(int first, int last, int lane) {
+    if (last >= win + 64) {
+      win = first;
+      ids = (win + lane < end) ? bt[win + lane] : 0;
+    }
+  }
+  __device__ int block(int lb) const {
+    return __builtin_amdgcn_readlane(ids, lb - win);
+  }
+};
+
+// Buffer resource over the valid rows of logical block lb of one head:
+// record count = valid tokens x row stride (0 for a block past the end or an
+// id outside the pool, which then reads as zeros without touching memory).
+template <int B>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(
+    const char* head_base, int blk, int lb, int t1, uint32_t row_stride,
+    uint64_t blk_bytes, int num_blocks) {
+  int valid = t1 - lb * B;
+  valid = valid < B ? valid : B;
+  const bool ok = valid > 0 && (unsigned)blk < (unsigned)num_blocks;
+  return make_rsrc(head_base + (ok ? (uint64_t)blk * blk_bytes : 0),
+                   ok ? (uint32_t)valid * row_stride : 0u);
+}
+
+// Final cross-wave merge.  Each wave left (m, l) per head and acc[head][d] in
+// LDS; every thread folds one (head, channel) and hands the result to `sink`
+// as (head in group, channel, max in base-2 units, sum, unnormalised out).
+template <int D, int G, class Smem, class Sink>
+__device__ __forceinline__ void merge_waves(Smem& sm, Sink& sink) {
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
+    const int gi = idx / D;
+    const int d = idx % D;
+    float mx = sm.m[0][gi];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][gi]);
+    const float sh = mx == -INFINITY ? 0.f : mx;
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2(sm.m[w][gi] - sh);
+      L += sm.l[w][gi] * f;
+      O += sm.acc[w][gi][d] * f;
+    }
+    sink(gi, d, mx, L, O);
+  }
+  __syncthreads();    // LDS free for the next range
+}
+
+// ---------------------------------------------------------------------------
+// Vector-ALU range body
+// ---------------------------------------------------------------------------
+//
+// A 16-byte load per lane covers one token row of one head (D/8 lanes per
+// row), so one load instruction reads whole 128-byte lines.  A wave batch is
+// NJ loads of K and NJ of V per lane in flight; the 4 waves take batches
+// round-robin.  Each row group (one token of a load) keeps its own online
+// softmax state (m, l, acc[8] per head, replicated in the row): the dot
+// product is reduced across the row with four DPP adds (bitwise identical in
+// every lane) and everything else is lane-local until the end, where row
+// groups merge with cross-lane shuffles and waves through LDS.
 template <int D, int B, int G, int NJ>
-__global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
-  constexpr int LPR = D / 8;          // lanes per token row
-  constexpr int RPI = 64 / LPR;       // token rows per wave load
-  constexpr int TB = RPI * NJ;        // tokens per wave batch
-  constexpr int NW = 4;               // waves per workgroup
+struct ValuPath {
+  static constexpr int LPR = D / 8;       // lanes per token row
+  static constexpr int RPI = 64 / LPR;    // token rows per wave load
+  static constexpr int TB = RPI * NJ;     // tokens per wave batch
   static_assert(B % RPI == 0, "a load must not straddle two blocks");
 
-  __shared__ float sm_acc[NW][G][D];
-  __shared__ float sm_m[NW][G];
-  __shared__ float sm_l[NW][G];
+  struct Smem {
+    float acc[kWaves][G][D];
+    float m[kWaves][G];
+    float l[kWaves][G];
+  };
 
-  // grid (kv heads, sequences, partitions): consecutive workgroup ids -- which
-  // the dispatcher deals round-robin to the 8 XCDs -- differ in kv head and
-  // sequence, so every XCD gets a share of each partition index; partition 0
-  // of every sequence is dispatched first, the (possibly empty) later
-  // partitions last.
+  // t0 must be a multiple of RPI (callers pass multiples of 16)
+  template <class Sink>
+  __device__ static void run(const DecodeArgs& a, Smem& sm, int kvh, int seq,
+                             int t0, int t1, Sink& sink) {
+    const int H = a.num_heads;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane / LPR;
+    const int c = lane % LPR;
+
+    u32x4 qv[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+      qv[gi] = *reinterpret_cast<const u32x4*>(
+          a.query + ((size_t)seq * H + (size_t)kvh * G + gi) * D + c * 8);
+
+    BlockWindow bw;
+    bw.init(a.block_tables + (size_t)seq * a.max_blocks_per_seq, t0 / B,
+            (t1 + B - 1) / B, lane);
+    const uint32_t row_stride = (uint32_t)a.num_kv_heads * D * 2;
+    const uint64_t blk_bytes = (uint64_t)B * row_stride;
+    const char* kbase = a.key_cache + (size_t)kvh * D * 2;
+    const char* vbase = a.value_cache + (size_t)kvh * D * 2;
+    const float sl2 = a.scale * kLog2e;
+
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      m[gi] = -INFINITY;
+      l[gi] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[gi][e] = 0.f;
+    }
+
+    for (int base = t0 + wave * TB; base < t1; base += kWaves * TB) {
+      bw.cover(base / B, (base + TB - 1) / B, lane);
+      u32x4 kk[NJ], vv[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int tok0 = base + j * RPI;   // wave-uniform
+        const int lb = tok0 / B;
+        const int blk = bw.block(lb);
+        const uint32_t off = (uint32_t)(tok0 % B + r) * row_stride + c * 16;
+        kk[j] = load16(block_rsrc<B>(kbase, blk, lb, t1, row_stride, blk_bytes,
+                                     a.num_blocks), off);
+        vv[j] = load16(block_rsrc<B>(vbase, blk, lb, t1, row_stride, blk_bytes,
+                                     a.num_blocks), off);
+      }
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        float s[NJ];
+        float bm = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const float d = group_sum<LPR>(dot8(qv[gi], kk[j]));
+          const int tok = base + j * RPI + r;
+          s[j] = tok < t1 ? d * sl2 : -INFINITY;
+          bm = fmaxf(bm, s[j]);
+        }
+        const float mn = fmaxf(m[gi], bm);
+        const float sh = mn == -INFINITY ? 0.f : mn;
+        const float al = fast_exp2(m[gi] - sh);
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          s[j] = fast_exp2(s[j] - sh);
+          ps += s[j];
+        }
+        l[gi] = l[gi] * al + ps;
+        m[gi] = mn;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float x = acc[gi][e] * al;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            x = __builtin_fmaf(s[j], half_at(vv[j], e), x);
+          acc[gi][e] = x;
+        }
+      }
+    }
+
+    // merge the row groups of the wave (lanes sharing channel chunk c)
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const float mo = __shfl_xor(m[gi], off);
+        const float lo = __shfl_xor(l[gi], off);
+        const float mn = fmaxf(m[gi], mo);
+        const float sh = mn == -INFINITY ? 0.f : mn;
+        const float fa = fast_exp2(m[gi] - sh);
+        const float fb = fast_exp2(mo - sh);
+        l[gi] = l[gi] * fa + lo * fb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float ao = __shfl_xor(acc[gi][e], off);
+          acc[gi][e] = acc[gi][e] * fa + ao * fb;
+        }
+        m[gi] = mn;
+      }
+    }
+    if (r == 0) {
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.acc[wave][gi][c * 8 + e] = acc[gi][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        sm.m[wave][gi] = m[gi];
+        sm.l[wave][gi] = l[gi];
+      }
+    }
+    merge_waves<D, G>(sm, sink);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Matrix-core range body (g = 8)
+// ---------------------------------------------------------------------------
+//
+// Per wave, a batch is MT tiles of 16 tokens.  With the 16x16x32 fp16 MFMA
+// (lane l holds A[l%16][8(l/16)+i], B[8(l/16)+i][l%16], D[4(l/16)+i][l%16]):
+//   S^T (16 tokens x 16 heads) = K (A: a 16-byte load of token l%16, channels
+//        32kk + 8(l/16)..) x Q^T (B: the group's query heads, zero past g),
+//        D/32 MFMAs per tile;
+//   O^T (16 channels x 16 heads) += V^T (A) x P^T (B), D/16 MFMAs per pair of
+//        tiles.
+// P^T needs no data movement: a lane's eight S^T values (4 tokens of each of
+// two tiles, one head) are exactly the eight reduction slots it supplies to
+// B, provided V^T's reduction slots use the same token order.  V^T is the
+// transposed V tile, so V goes through LDS: each lane stores its 16-byte
+// rows, then gathers its column with 2-byte reads; rows are padded by 8 bytes
+// so the four lane groups of a read hit disjoint banks.  Every per-head
+// quantity (running max, sum, rescale factor) lives in the lanes owning that
+// head's column, and O^T's rows are channels, so the rescale is lane-local.
+template <int D, int B, int G>
+struct MfmaPath {
+  static constexpr int MT = D == 128 ? 2 : 4;   // 16-token tiles per batch
+  static constexpr int TB = 16 * MT;
+  static constexpr int KK = D / 32;             // MFMA k-steps over channels
+  static constexpr int DT = D / 16;             // channel tiles of O^T
+  static constexpr int VS = D + 4;              // padded LDS row (halves)
+  static_assert(B % 16 == 0, "a tile must not straddle two blocks");
+  static_assert(G <= 16, "one MFMA column per query head");
+
+  struct Smem {
+    _Float16 vs[kWaves][TB][VS];
+    float acc[kWaves][G][D];
+    float m[kWaves][G];
+    float l[kWaves][G];
+  };
+
+  // t0 must be a multiple of 16
+  template <class Sink>
+  __device__ static void run(const DecodeArgs& a, Smem& sm, int kvh, int seq,
+                             int t0, int t1, Sink& sink) {
+    const int H = a.num_heads;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15;                  // token row (A) / head (B, D)
+    const int grp = lane >> 4;                  // lane group 0..3
+
+    f16x8 qb[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (col < G)
+        v = *reinterpret_cast<const u32x4*>(
+            a.query + ((size_t)seq * H + (size_t)kvh * G + col) * D + kk * 32 +
+            grp * 8);
+      qb[kk] = __builtin_bit_cast(f16x8, v);
+    }
+
+    BlockWindow bw;
+    bw.init(a.block_tables + (size_t)seq * a.max_blocks_per_seq, t0 / B,
+            (t1 + B - 1) / B, lane);
+    const uint32_t row_stride = (uint32_t)a.num_kv_heads * D * 2;
+    const uint64_t blk_bytes = (uint64_t)B * row_stride;
+    const char* kbase = a.key_cache + (size_t)kvh * D * 2;
+    const char* vbase = a.value_cache + (size_t)kvh * D * 2;
+    const float sl2 = a.scale * kLog2e;
+
+    float m = -INFINITY;                        // running max of head `col`
+    float l = 0.f;                              // this lane's share of the sum
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    _Float16* vw = &sm.vs[wave][0][0];
+
+    for (int base = t0 + wave * TB; base < t1; base += kWaves * TB) {
+      bw.cover(base / B, (base + TB - 1) / B, lane);
+      u32x4 kr[MT][KK], vr[MT][KK];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int tile0 = base + mt * 16;       // wave-uniform
+        const int lb = tile0 / B;
+        const int blk = bw.block(lb);
+        const __amdgpu_buffer_rsrc_t rk = block_rsrc<B>(
+            kbase, blk, lb, t1, row_stride, blk_bytes, a.num_blocks);
+        const __amdgpu_buffer_rsrc_t rv = block_rsrc<B>(
+            vbase, blk, lb, t1, row_stride, blk_bytes, a.num_blocks);
+        const uint32_t off = (uint32_t)(tile0 % B + col) * row_stride + grp * 16;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          kr[mt][kk] = load16(rk, off + kk * 64);
+          vr[mt][kk] = load16(rv, off + kk * 64);
+        }
+      }
+
+      // scores: the lane holds tokens tile0 + 4grp + i of head `col`
+      float sc[MT][4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(f16x8, kr[mt][kk]), qb[kk], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = base + mt * 16 + grp * 4 + i;
+          sc[mt][i] = tok < t1 ? acc[i] * sl2 : -INFINITY;
+        }
+      }
+
+      // V tile to LDS in token-major rows (two 8-byte stores per chunk)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          _Float16* dst = vw + (mt * 16 + col) * VS + kk * 32 + grp * 8;
+          const u32x4 v = vr[mt][kk];
+          reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
+          reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
+        }
+
+      // online softmax for head `col` (max over the batch and the 4 groups)
+      float bm = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[mt][i]);
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float mn = fmaxf(m, bm);
+      const float sh = mn == -INFINITY ? 0.f : mn;
+      const float al = fast_exp2(m - sh);
+      m = mn;
+      float ps = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[mt][i] = fast_exp2(sc[mt][i] - sh);
+          ps += sc[mt][i];
+        }
+      l = l * al + ps;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
+
+      // O^T += V^T P^T, one k-step of 32 tokens per pair of tiles
+#pragma unroll
+      for (int pr = 0; pr < MT / 2; ++pr) {
+        f16x8 pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[i] = (_Float16)sc[2 * pr][i];
+          pb[4 + i] = (_Float16)sc[2 * pr + 1][i];
+        }
+        const _Float16* vrow0 = vw + (pr * 32 + grp * 4) * VS + col;
+        const _Float16* vrow1 = vrow0 + 16 * VS;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          f16x8 va;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            va[i] = vrow0[i * VS + dt * 16];
+            va[4 + i] = vrow1[i * VS + dt * 16];
+          }
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o[dt], 0, 0, 0);
+        }
+      }
+    }
+
+    // the sum over the 4 lane groups; then merge the waves through LDS
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (col < G) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sm.acc[wave][col][dt * 16 + grp * 4 + i] = o[dt][i];
+      if (grp == 0) {
+        sm.m[wave][col] = m;
+        sm.l[wave][col] = l;
+      }
+    }
+    merge_waves<D, G>(sm, sink);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Fixed partitions (single pass and split-KV)
+// ---------------------------------------------------------------------------
+
+// Grid (kv heads, sequences, partitions): consecutive workgroup ids -- which
+// the dispatcher deals round-robin to the 8 XCDs -- differ in kv head and
+// sequence, so every XCD gets a share of each partition index; partition 0
+// of every sequence is dispatched first, later (possibly empty) ones last.
+template <class Path, int D, int B, int G>
+__global__ __launch_bounds__(256) void partition_kernel(DecodeArgs a) {
+  __shared__ typename Path::Smem sm;
   const int kvh = blockIdx.x;
   const int seq = blockIdx.y;
   const int p = blockIdx.z;
   const int H = a.num_heads;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane / LPR;
-  const int c = lane % LPR;
-
   int n = a.context_lens[seq];
   const int max_tok = a.max_blocks_per_seq * B;
   n = n < max_tok ? n : max_tok;
@@ -75,138 +457,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
     return;
   }
   const int t1 = (t0 + a.partition_size) < n ? (t0 + a.partition_size) : n;
-
-  // this lane's 8 channels of each query head of the group
-  u32x4 qv[G];
-#pragma unroll
-  for (int gi = 0; gi < G; ++gi)
-    qv[gi] = *reinterpret_cast<const u32x4*>(
-        a.query + ((size_t)seq * H + (size_t)kvh * G + gi) * D + c * 8);
-
-  const int* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
-  const int lb_end = (t1 + B - 1) / B;
-  int win = t0 / B;                          // logical block held by lane 0
-  int ids = (win + lane < lb_end) ? bt[win + lane] : 0;
-
-  const uint32_t row_stride = (uint32_t)a.num_kv_heads * D * 2;
-  const uint64_t blk_bytes = (uint64_t)B * row_stride;
-  const char* kbase = a.key_cache + (size_t)kvh * D * 2;
-  const char* vbase = a.value_cache + (size_t)kvh * D * 2;
-  const float sl2 = a.scale * kLog2e;
-
-  float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int gi = 0; gi < G; ++gi) {
-    m[gi] = -INFINITY;
-    l[gi] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[gi][e] = 0.f;
-  }
-
-  for (int base = t0 + wave * TB; base < t1; base += NW * TB) {
-    // keep the id window over every block this batch touches
-    if ((base + TB - 1) / B >= win + 64) {
-      win = base / B;
-      ids = (win + lane < lb_end) ? bt[win + lane] : 0;
-    }
-    u32x4 kk[NJ], vv[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int tok0 = base + j * RPI;       // wave-uniform
-      const int lb = tok0 / B;
-      const int blk = __builtin_amdgcn_readlane(ids, lb - win);
-      int valid = t1 - lb * B;
-      valid = valid < B ? valid : B;
-      const bool ok = valid > 0 && (unsigned)blk < (unsigned)a.num_blocks;
-      const uint32_t bytes = ok ? (uint32_t)valid * row_stride : 0u;
-      const uint64_t boff = ok ? (uint64_t)blk * blk_bytes : 0;
-      const uint32_t off = (uint32_t)(tok0 % B + r) * row_stride + c * 16;
-      kk[j] = load16(make_rsrc(kbase + boff, bytes), off);
-      vv[j] = load16(make_rsrc(vbase + boff, bytes), off);
-    }
-
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      float s[NJ];
-      float bm = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const float d = group_sum<LPR>(dot8(qv[gi], kk[j]));
-        const int tok = base + j * RPI + r;
-        s[j] = tok < t1 ? d * sl2 : -INFINITY;
-        bm = fmaxf(bm, s[j]);
-      }
-      const float mn = fmaxf(m[gi], bm);
-      const float sh = mn == -INFINITY ? 0.f : mn;
-      const float al = fast_exp2(m[gi] - sh);
-      float ps = 0.f;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        s[j] = fast_exp2(s[j] - sh);
-        ps += s[j];
-      }
-      l[gi] = l[gi] * al + ps;
-      m[gi] = mn;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x = acc[gi][e] * al;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) x = __builtin_fmaf(s[j], half_at(vv[j], e), x);
-        acc[gi][e] = x;
-      }
-    }
-  }
-
-  // merge the row groups of the wave (lanes sharing channel chunk c)
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      const float mo = __shfl_xor(m[gi], off);
-      const float lo = __shfl_xor(l[gi], off);
-      const float mn = fmaxf(m[gi], mo);
-      const float sh = mn == -INFINITY ? 0.f : mn;
-      const float fa = fast_exp2(m[gi] - sh);
-      const float fb = fast_exp2(mo - sh);
-      l[gi] = l[gi] * fa + lo * fb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float ao = __shfl_xor(acc[gi][e], off);
-        acc[gi][e] = acc[gi][e] * fa + ao * fb;
-      }
-      m[gi] = mn;
-    }
-  }
-  if (r == 0) {
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm_acc[wave][gi][c * 8 + e] = acc[gi][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      sm_m[wave][gi] = m[gi];
-      sm_l[wave][gi] = l[gi];
-    }
-  }
-  __syncthreads();
-
-  // merge the waves; one thread per (head of the group, channel)
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int gi = idx / D;
-    const int d = idx % D;
-    float mx = sm_m[0][gi];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, sm_m[w][gi]);
-    const float sh = mx == -INFINITY ? 0.f : mx;
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = fast_exp2(sm_m[w][gi] - sh);
-      L += sm_l[w][gi] * f;
-      O += sm_acc[w][gi][d] * f;
-    }
+  auto sink = [&](int gi, int d, float mx, float L, float O) {
     const size_t h = (size_t)kvh * G + gi;
     if (a.split) {
       const size_t pi = ((size_t)seq * H + h) * a.max_partitions + p;
@@ -218,11 +469,12 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
     } else {
       a.out[((size_t)seq * H + h) * D + d] = (_Float16)(O / L);
     }
-  }
+  };
+  Path::run(a, sm, kvh, seq, t0, t1, sink);
 }
 
-// One workgroup of D threads per (query head, sequence): fold the partition
-// states in order with the online-softmax recurrence.
+// One workgroup of D threads per (query head, sequence): fold the fixed
+// partitions in order with the online-softmax recurrence.
 template <int D>
 __global__ __launch_bounds__(D) void reduce_kernel(ReduceArgs a) {
   const int h = blockIdx.x;
@@ -249,43 +501,267 @@ __global__ __launch_bounds__(D) void reduce_kernel(ReduceArgs a) {
   *o = (_Float16)(O / S);
 }
 
+// ---------------------------------------------------------------------------
+// Balanced split
+// ---------------------------------------------------------------------------
+//
+// Flat work order: sequence-major, then kv head, then token, every sequence's
+// length padded to a multiple of 16 (padded_len).  With T the flat total and
+// C = ceil(T / grid) rounded up to 16, workgroup w owns flat positions
+// [w*C, (w+1)*C).  The part of pair q = seq*H_kv + kvh inside workgroup w is
+// one range; its state goes to slot w + q.  Along the flat order w and q
+// never decrease and at least one grows at every range boundary, so slots
+// are distinct and below grid + S*H_kv.  Pairs of one sequence are adjacent,
+// so neighbouring workgroups read neighbouring heads of the same token rows.
+__device__ __forceinline__ int64_t padded_len(int n, int max_tok) {
+  n = n < max_tok ? n : max_tok;
+  return n <= 0 ? 0 : (int64_t)((n + 15) & ~15);
+}
+
+__device__ __forceinline__ int64_t balanced_chunk(int64_t total, int grid) {
+  const int64_t c = (total + grid - 1) / grid;
+  return (c + 15) & ~(int64_t)15;
+}
+
+// Inclusive scan over the 256 threads of a workgroup (LDS buffer `buf`).
+__device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* buf) {
+  buf[threadIdx.x] = v;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int64_t u = threadIdx.x >= (unsigned)off ? buf[threadIdx.x - off] : 0;
+    __syncthreads();
+    buf[threadIdx.x] += u;
+    __syncthreads();
+  }
+  return buf[threadIdx.x];
+}
+
+template <class Path, int D, int B, int G>
+__global__ __launch_bounds__(256) void balanced_kernel(DecodeArgs a) {
+  __shared__ typename Path::Smem sm;
+  __shared__ int64_t scan[256];
+  __shared__ int64_t found_start;
+  __shared__ int found_seq;
+  const int S = a.num_seqs;
+  const int Hkv = a.num_kv_heads;
+  const int max_tok = a.max_blocks_per_seq * B;
+  const int w = blockIdx.x;
+
+  // padded length per kv head, prefix over sequences, 256 at a time; the
+  // first workgroup records the prefix and the total for the reduce, every
+  // workgroup finds the sequence holding its first flat position
+  if (threadIdx.x == 0) found_seq = -1;
+  int64_t run = 0;                       // per-kv-head prefix before chunk
+  int64_t total_per_kvh = 0;
+  for (int s0 = 0; s0 < S; s0 += 256) {
+    const int si = s0 + (int)threadIdx.x;
+    const int64_t len = si < S ? padded_len(a.context_lens[si], max_tok) : 0;
+    const int64_t inc = block_scan(len, scan);
+    const int64_t chunk_sum = scan[255];
+    if (w == 0 && si < S) a.bal_prefix[si] = run + inc - len;
+    __syncthreads();
+    run += chunk_sum;
+  }
+  total_per_kvh = run;
+  if (w == 0 && threadIdx.x == 0) a.bal_total[0] = total_per_kvh;
+  const int64_t total = total_per_kvh * Hkv;
+  const int64_t C = balanced_chunk(total, gridDim.x);
+  const int64_t start = (int64_t)w * C;
+  if (total == 0 || start >= total) return;
+  const int64_t end = start + C < total ? start + C : total;
+
+  run = 0;
+  for (int s0 = 0; s0 < S; s0 += 256) {
+    const int si = s0 + (int)threadIdx.x;
+    const int64_t len = si < S ? padded_len(a.context_lens[si], max_tok) * Hkv : 0;
+    const int64_t inc = block_scan(len, scan);
+    const int64_t chunk_sum = scan[255];
+    // the one sequence whose flat span [run+inc-len, run+inc) holds start
+    if (len > 0 && run + inc - len <= start && start < run + inc) {
+      found_seq = si;
+      found_start = run + inc - len;
+    }
+    __syncthreads();
+    if (found_seq >= 0) break;
+    run += chunk_sum;
+  }
+  int s = found_seq;
+  int64_t E = found_start;               // flat start of sequence s
+  if (s < 0) return;                     // unreachable while start < total
+
+  int64_t pos = start;
+  while (pos < end && s < S) {
+    int n = a.context_lens[s];
+    n = n < max_tok ? n : max_tok;
+    const int64_t np = padded_len(n, max_tok);
+    if (np == 0) {
+      ++s;
+      continue;
+    }
+    const int kvh = (int)((pos - E) / np);
+    const int ta = (int)((pos - E) - (int64_t)kvh * np);
+    const int64_t pair_end = E + (int64_t)(kvh + 1) * np;
+    const int64_t seg_end = end < pair_end ? end : pair_end;
+    const int tb = ta + (int)(seg_end - pos);
+    const int tv = tb < n ? tb : n;
+    if (ta < tv) {
+      const int64_t slot = (int64_t)w + (int64_t)s * Hkv + kvh;
+      auto sink = [&](int gi, int d, float mx, float L, float O) {
+        const size_t pi = (size_t)slot * G + gi;
+        if (d == 0) {
+          a.ws_max[pi] = mx * kLn2;
+          a.ws_sum[pi] = L;
+        }
+        a.ws_out[pi * D + d] = O;
+      };
+      Path::run(a, sm, kvh, s, ta, tv, sink);
+    }
+    pos = seg_end;
+    if (pos == E + (int64_t)Hkv * np) {
+      E = pos;
+      ++s;
+    }
+  }
+}
+
+// Merge of the balanced ranges of one (query head, sequence): the ranges of
+// pair q are those of the workgroups whose flat slice meets [F, F + padded),
+// F = prefix*H_kv + kvh*padded; a range holding only padding tokens was
+// never written and is skipped (so are all later ones).
+template <int D>
+__global__ __launch_bounds__(D) void balanced_reduce_kernel(BalancedReduceArgs a) {
+  const int h = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int d = threadIdx.x;
+  const int H = a.num_heads;
+  const int G = H / a.num_kv_heads;
+  const int kvh = h / G;
+  const int gi = h - kvh * G;
+  int n = a.context_lens[seq];
+  n = n < a.max_tokens ? n : a.max_tokens;
+  _Float16* o = a.out + ((size_t)seq * H + h) * D + d;
+  if (n <= 0) {
+    *o = (_Float16)0.f;
+    return;
+  }
+  const int64_t np = (int64_t)((n + 15) & ~15);
+  const int64_t total = a.total[0] * a.num_kv_heads;
+  const int64_t C = balanced_chunk(total, a.grid);
+  const int64_t F = a.prefix[seq] * a.num_kv_heads + (int64_t)kvh * np;
+  const int64_t q = (int64_t)seq * a.num_kv_heads + kvh;
+  const int64_t w0 = F / C;
+  const int64_t w1 = (F + np - 1) / C;
+  float mx = -INFINITY;
+  for (int64_t w = w0; w <= w1; ++w) {
+    const int64_t lo = (w * C > F ? w * C : F) - F;
+    if (lo >= n) break;
+    mx = fmaxf(mx, a.ws_max[(size_t)(w + q) * G + gi]);
+  }
+  float S = 0.f, O = 0.f;
+  for (int64_t w = w0; w <= w1; ++w) {
+    const int64_t lo = (w * C > F ? w * C : F) - F;
+    if (lo >= n) break;
+    const size_t pi = (size_t)(w + q) * G + gi;
+    const float f = fast_exp2((a.ws_max[pi] - mx) * kLog2e);
+    S += a.ws_sum[pi] * f;
+    O += a.ws_out[pi * D + d] * f;
+  }
+  *o = (_Float16)(O / S);
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch
+// ---------------------------------------------------------------------------
+
+// Loads in flight per wave batch (16-byte K and V loads per lane) for the
+// vector-ALU body; measured on MI355X: 8 is best for groups of 1-2, 4 for a
+// group of 4 (fewer registers, one more wave per SIMD).  A group of 8 runs
+// on the matrix cores.
 template <int D, int B, int G>
-static hipError_t launch_dbg(const DecodeArgs& a, dim3 grid, hipStream_t st) {
-  constexpr int NJ = 8;
-  hipLaunchKernelGGL((decode_partition_kernel<D, B, G, NJ>), grid, dim3(256), 0,
-                     st, a);
-  return hipGetLastError();
+struct PathFor {
+  using type = ValuPath<D, B, G, (G >= 4 ? 4 : 8)>;
+};
+template <int D, int B>
+struct PathFor<D, B, 8> {
+  using type = MfmaPath<D, B, 8>;
+};
+
+enum class Op { kPartition, kBalanced, kOccupancy };
+
+template <int D, int B, int G>
+static hipError_t run_op(Op op, const DecodeArgs* a, dim3 grid,
+                         hipStream_t st, int* occ) {
+  using P = typename PathFor<D, B, G>::type;
+  switch (op) {
+    case Op::kPartition:
+      hipLaunchKernelGGL((partition_kernel<P, D, B, G>), grid, dim3(256), 0, st, *a);
+      return hipGetLastError();
+    case Op::kBalanced:
+      hipLaunchKernelGGL((balanced_kernel<P, D, B, G>), grid, dim3(256), 0, st, *a);
+      return hipGetLastError();
+    case Op::kOccupancy:
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          occ, reinterpret_cast<const void*>(&balanced_kernel<P, D, B, G>), 256, 0);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int D, int B>
-static hipError_t launch_db(const DecodeArgs& a, int G, dim3 grid, hipStream_t st) {
+static hipError_t dispatch_db(Op op, int G, const DecodeArgs* a, dim3 grid,
+                              hipStream_t st, int* occ) {
   switch (G) {
-    case 1: return launch_dbg<D, B, 1>(a, grid, st);
-    case 2: return launch_dbg<D, B, 2>(a, grid, st);
-    case 4: return launch_dbg<D, B, 4>(a, grid, st);
-    case 8: return launch_dbg<D, B, 8>(a, grid, st);
+    case 1: return run_op<D, B, 1>(op, a, grid, st, occ);
+    case 2: return run_op<D, B, 2>(op, a, grid, st, occ);
+    case 4: return run_op<D, B, 4>(op, a, grid, st, occ);
+    case 8: return run_op<D, B, 8>(op, a, grid, st, occ);
   }
   return hipErrorInvalidValue;
 }
 
 template <int D>
-static hipError_t launch_d(const DecodeArgs& a, int B, int G, dim3 grid,
-                           hipStream_t st) {
+static hipError_t dispatch_d(Op op, int B, int G, const DecodeArgs* a, dim3 grid,
+                             hipStream_t st, int* occ) {
   switch (B) {
-    case 16: return launch_db<D, 16>(a, G, grid, st);
-    case 32: return launch_db<D, 32>(a, G, grid, st);
-    case 64: return launch_db<D, 64>(a, G, grid, st);
+    case 16: return dispatch_db<D, 16>(op, G, a, grid, st, occ);
+    case 32: return dispatch_db<D, 32>(op, G, a, grid, st, occ);
+    case 64: return dispatch_db<D, 64>(op, G, a, grid, st, occ);
+  }
+  return hipErrorInvalidValue;
+}
+
+static hipError_t dispatch(Op op, int D, int B, int G, const DecodeArgs* a,
+                           dim3 grid, hipStream_t st, int* occ) {
+  switch (D) {
+    case 64: return dispatch_d<64>(op, B, G, a, grid, st, occ);
+    case 128: return dispatch_d<128>(op, B, G, a, grid, st, occ);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int head_size, int block_size,
                          int group, dim3 grid, hipStream_t stream) {
-  switch (head_size) {
-    case 64: return launch_d<64>(a, block_size, group, grid, stream);
-    case 128: return launch_d<128>(a, block_size, group, grid, stream);
-  }
-  return hipErrorInvalidValue;
+  return dispatch(Op::kPartition, head_size, block_size, group, &a, grid,
+                  stream, nullptr);
+}
+
+hipError_t launch_balanced(const DecodeArgs& a, int head_size, int block_size,
+                           int group, int grid, hipStream_t stream) {
+  return dispatch(Op::kBalanced, head_size, block_size, group, &a,
+                  dim3(grid), stream, nullptr);
+}
+
+int balanced_grid(int head_size, int block_size, int group) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+      hipSuccess)
+    return 0;
+  int per_cu = 0;
+  if (dispatch(Op::kOccupancy, head_size, block_size, group, nullptr, dim3(1),
+               nullptr, &per_cu) != hipSuccess)
+    return 0;
+  return per_cu > 0 ? per_cu * cus : 0;
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, int head_size, int num_seqs,
@@ -297,6 +773,20 @@ hipError_t launch_reduce(const ReduceArgs& a, int head_size, int num_seqs,
       return hipGetLastError();
     case 128:
       hipLaunchKernelGGL(reduce_kernel<128>, grid, dim3(128), 0, stream, a);
+      return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_balanced_reduce(const BalancedReduceArgs& a, int head_size,
+                                  int num_seqs, hipStream_t stream) {
+  dim3 grid(a.num_heads, num_seqs);
+  switch (head_size) {
+    case 64:
+      hipLaunchKernelGGL(balanced_reduce_kernel<64>, grid, dim3(64), 0, stream, a);
+      return hipGetLastError();
+    case 128:
+      hipLaunchKernelGGL(balanced_reduce_kernel<128>, grid, dim3(128), 0, stream, a);
       return hipGetLastError();
   }
   return hipErrorInvalidValue;

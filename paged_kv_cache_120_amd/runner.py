@@ -14,7 +14,8 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-from . import (pa_cache_write, pa_copy_blocks, pa_decode, pa_decode_reduce,
+from . import (pa_balanced_grid, pa_balanced_workspace_size, pa_cache_write,
+               pa_copy_blocks, pa_decode, pa_decode_balanced, pa_decode_reduce,
                pa_decode_splitk, pa_slot_mapping, pa_splitk_workspace_size)
 
 
@@ -54,6 +55,8 @@ class DeviceStep:
     copies: Optional[DevCopy]
     write: DevWrite
     workspace: torch.Tensor        # uint8 split-KV workspace
+    grid: int                      # balanced decode workgroups
+    bal_workspace: torch.Tensor    # uint8 balanced decode workspace
 
     @property
     def key_cache(self):
@@ -94,13 +97,20 @@ def upload(w, device: str = "cuda", pool: Optional[torch.Tensor] = None) -> Devi
     S, H, D = w.query.shape
     ws = pa_splitk_workspace_size(S, H, D, w.max_blocks_per_seq, w.block_size,
                                   w.partition_size)
+    with torch.cuda.device(dev):
+        grid = pa_balanced_grid(H, w.num_kv_heads, D, w.block_size)
+    if grid <= 0:
+        raise RuntimeError("pa_balanced_grid failed")
+    bws = pa_balanced_workspace_size(S, H, w.num_kv_heads, D, grid)
     return DeviceStep(
         block_size=w.block_size, scale=w.scale, partition_size=w.partition_size,
         pool=pool, query=_t(w.query, dev), block_tables=_t(w.block_tables, dev),
         context_lens=_t(w.context_lens, dev),
         out=torch.empty((S, H, D), dtype=torch.float16, device=dev),
         copies=_dev_phase(w.step_copies, dev), write=_dev_phase(w.step_write, dev),
-        workspace=torch.empty(max(ws, 16), dtype=torch.uint8, device=dev))
+        workspace=torch.empty(max(ws, 16), dtype=torch.uint8, device=dev),
+        grid=grid,
+        bal_workspace=torch.empty(max(bws, 16), dtype=torch.uint8, device=dev))
 
 
 def apply_history(w, step: DeviceStep, stream=None) -> None:
@@ -120,6 +130,10 @@ def decode_step(step: DeviceStep, mode: str = "splitk", stream=None) -> None:
     if mode == "single":
         pa_decode(step.out, step.query, step.key_cache, step.value_cache,
                   step.block_tables, step.context_lens, step.scale, stream=stream)
+    elif mode == "balanced":
+        pa_decode_balanced(step.out, step.query, step.key_cache, step.value_cache,
+                           step.block_tables, step.context_lens, step.scale,
+                           step.grid, step.bal_workspace, stream=stream)
     elif mode == "splitk":
         pa_decode_splitk(step.query, step.key_cache, step.value_cache,
                          step.block_tables, step.context_lens, step.scale,

@@ -72,7 +72,10 @@ SMALL = ["c1", "c1_page_tables", "c2_small", "c3_small", "c4_small", "c4_r0_smal
          "c5_b32_small", "c5_b64_small"]
 
 
-@pytest.mark.parametrize("mode", ["single", "splitk"])
+MODES = ["single", "splitk", "balanced"]
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("name", SMALL)
 def test_parity_small(name, mode):
     print(f"[parity] {name} {mode}", flush=True)
@@ -107,21 +110,24 @@ def test_split_partials_match_oracle(name):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name,mode", [("c1", "splitk"), ("c2", "splitk"), ("c2", "single"),
-                                       ("c3", "splitk"), ("c4", "splitk")])
+                                       ("c2", "balanced"), ("c3", "splitk"),
+                                       ("c3", "balanced"), ("c4", "splitk"),
+                                       ("c4", "balanced")])
 def test_parity_full(name, mode):
     print(f"[parity-full] {name} {mode}", flush=True)
     check_all(workloads.make(name), mode)
 
 
+@pytest.mark.parametrize("mode", ["splitk", "balanced"])
 @pytest.mark.parametrize("name", ["c5_b32", "c5_b64"])
-def test_parity_full_long_context_sampled(name):
-    print(f"[parity-full] {name} splitk (sampled heads)", flush=True)
+def test_parity_full_long_context_sampled(name, mode):
+    print(f"[parity-full] {name} {mode} (sampled heads)", flush=True)
     w = workloads.make(name)
     rng = np.random.default_rng(7)
     pairs = [(i, int(h)) for i in range(w.num_seqs)
              for h in rng.choice(w.num_heads, 6, replace=False)]
     pairs += [(int(np.argmax(w.context_lens)), 0), (int(np.argmin(w.context_lens)), 63)]
-    check_all(w, "splitk", full_oracle=False, pairs=sorted(pairs))
+    check_all(w, mode, full_oracle=False, pairs=sorted(pairs))
 
 
 # ---------------------------------------------------------------------------
@@ -131,7 +137,7 @@ def test_parity_full_long_context_sampled(name):
 EDGE_LENS = [1, 2, 15, 16, 17, 31, 33, 511, 512, 513, 1023, 1024, 1025, 2047, 2048]
 
 
-@pytest.mark.parametrize("mode", ["single", "splitk"])
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("D,B,H,Hkv", [(128, 16, 32, 8), (64, 64, 16, 2),
                                        (128, 32, 8, 8), (64, 16, 8, 4),
                                        (128, 64, 16, 8)])
@@ -142,7 +148,7 @@ def test_edge_lengths(D, B, H, Hkv, mode):
     check_all(w, mode)
 
 
-@pytest.mark.parametrize("mode", ["single", "splitk"])
+@pytest.mark.parametrize("mode", MODES)
 def test_full_table(mode):
     """context_len = max_blocks_per_seq * block_size (every entry used)."""
     w = workloads.make("c1", D=128, B=32, H=16, Hkv=4, lens=[640, 1, 640, 639],
@@ -151,7 +157,7 @@ def test_full_table(mode):
     check_all(w, mode)
 
 
-@pytest.mark.parametrize("mode", ["single", "splitk"])
+@pytest.mark.parametrize("mode", MODES)
 def test_nonfinite_garbage_is_never_read(mode):
     w = workloads.make("c3_small", garbage="nonfinite")
     check_all(w, mode)
@@ -164,7 +170,7 @@ def test_splitk_partition_sizes(P):
     check_all(w, "splitk")
 
 
-@pytest.mark.parametrize("mode", ["single", "splitk"])
+@pytest.mark.parametrize("mode", MODES)
 def test_zero_context_gives_zeros(mode):
     pa, runner = _gpu()
     w = workloads.make("c2_small")
@@ -199,12 +205,13 @@ def test_permutation_invariance_bitwise():
             newpool = st.pool[:, inv].contiguous()        # newpool[:, perm[b]] = pool[:, b]
             st.pool = newpool
             st.block_tables = torch.from_numpy(perm[w.block_tables].astype(np.int32)).cuda()
-        for mode in ("single", "splitk"):
+        for mode in MODES:
             runner.decode_step(st, mode)
             torch.cuda.synchronize()
             outs.append(st.out.cpu().numpy().copy())
-    assert (outs[0].view(np.uint16) == outs[2].view(np.uint16)).all()
-    assert (outs[1].view(np.uint16) == outs[3].view(np.uint16)).all()
+    k = len(MODES)
+    for i in range(k):
+        assert (outs[i].view(np.uint16) == outs[k + i].view(np.uint16)).all(), MODES[i]
 
 
 def test_shared_prefix_equals_private_copies_bitwise():
@@ -233,14 +240,37 @@ def test_shared_prefix_equals_private_copies_bitwise():
     assert (st.out.cpu().numpy().view(np.uint16) == shared.view(np.uint16)).all()
 
 
+@pytest.mark.parametrize("grid", [1, 3, 17, 200, 5000])
+@pytest.mark.parametrize("name", ["c3_small", "c2_small", "c5_b64_small"])
+def test_balanced_any_grid(name, grid):
+    """Any workgroup count gives the same answer: a slice may hold many
+    (sequence, head) ranges (grid 1) or less than one tile (grid 5000)."""
+    print(f"[balanced-grid] {name} grid={grid}", flush=True)
+    pa, runner = _gpu()
+    w = workloads.make(name)
+    st = runner.upload(w)
+    runner.apply_history(w, st)
+    runner.write_step(st)
+    nbytes = pa.pa_balanced_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads,
+                                           w.head_size, grid)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    pa.pa_decode_balanced(st.out, st.query, st.key_cache, st.value_cache,
+                          st.block_tables, st.context_lens, st.scale, grid, ws)
+    torch.cuda.synchronize()
+    kc, vc = oracle_pool(w, oracle)
+    ref = oracle.decode(w.query, kc, vc, w.block_tables, w.context_lens, w.scale)
+    assert_attention_close(st.out.cpu().numpy(), ref, f"{name} grid {grid}")
+
+
 def test_repeat_calls_deterministic():
     pa, runner = _gpu()
     w = workloads.make("c2_small")
-    st = run_gpu(w, "splitk")
-    a = st.out.cpu().numpy().copy()
-    runner.decode_step(st, "splitk")
-    torch.cuda.synchronize()
-    assert (a.view(np.uint16) == st.out.cpu().numpy().view(np.uint16)).all()
+    for mode in MODES:
+        st = run_gpu(w, mode)
+        a = st.out.cpu().numpy().copy()
+        runner.decode_step(st, mode)
+        torch.cuda.synchronize()
+        assert (a.view(np.uint16) == st.out.cpu().numpy().view(np.uint16)).all(), mode
 
 
 def test_cache_write_skips_negative_and_out_of_range_slots():
