@@ -2,8 +2,11 @@
 """Paged decode benchmark on one MI355X.
 
 A step is one pass of the whole decode path over one batch: slot mapping of
-the new tokens, the cache write, then split-KV decode and its reduce (or
-the single-pass decode with --mode single).  Inputs are seeded synthetic
+the new tokens, the cache write, then decode.  Default (--mode fused):
+pa_decode_step, where the balanced split-KV kernel also derives each new
+token's slot and writes its K/V, followed by the reduce.  Other modes run
+pa_slot_mapping + pa_cache_write and then balanced, fixed-partition split-KV
+(+ reduce) or single-pass decode.  Inputs are seeded synthetic
 workloads already resident in HBM.  Timed steps rotate over --rotate copies
 of the pool so repeated reads cannot be served by the 256 MB MALL or L2.
 
@@ -55,6 +58,43 @@ def split_kernel_bytes(w) -> int:
     table = int(((n + B - 1) // B).sum()) * 4
     parts = int(((n + P - 1) // P).sum()) * H * (D + 2) * 4
     return kv_bytes(w) + S * H * D * 2 + table + parts
+
+
+def balanced_ranges(w, grid: int) -> int:
+    """Number of (workgroup, sequence, kv head) ranges with valid tokens in
+    the balanced decode (each writes one partial state per query head)."""
+    M = w.max_blocks_per_seq * w.block_size
+    n = np.minimum(w.context_lens.astype(np.int64), M)
+    pad = np.where(n > 0, (n + 15) // 16 * 16, 0)
+    Hkv = w.num_kv_heads
+    total = int(pad.sum()) * Hkv
+    if total == 0:
+        return 0
+    C = -(-total // grid)
+    C = (C + 15) // 16 * 16
+    prefix = np.concatenate([[0], np.cumsum(pad)[:-1]])
+    count = 0
+    for i in range(w.num_seqs):
+        if n[i] <= 0:
+            continue
+        for kvh in range(Hkv):
+            F = int(prefix[i]) * Hkv + kvh * int(pad[i])
+            for wg in range(F // C, (F + int(pad[i]) - 1) // C + 1):
+                if max(wg * C, F) - F < n[i]:
+                    count += 1
+    return count
+
+
+def balanced_kernel_bytes(w, grid: int, fused: bool) -> int:
+    """Algorithmic bytes of one balanced partials launch: KV rows, query,
+    table entries, partial states written, and (fused step) this step's K/V
+    rows read and written plus the slots."""
+    S, H, D = w.query.shape
+    n = w.context_lens.astype(np.int64)
+    table = int(((n + w.block_size - 1) // w.block_size).sum()) * 4
+    parts = balanced_ranges(w, grid) * w.group * (D + 2) * 4
+    extra = (2 * 2 * S * w.num_kv_heads * D * 2 + S * 4) if fused else 0
+    return kv_bytes(w) + S * H * D * 2 + table + parts + extra
 
 
 def single_kernel_bytes(w) -> int:
@@ -138,7 +178,7 @@ def load_traffic(args, root: str):
     summary for this workload and mode, if it was taken on the current
     kernel sources (else None)."""
     path = os.path.join(root, "profiles",
-                        f"decode_partition_kernel_{args.config}_{args.mode}_traffic.txt")
+                        f"decode_{args.config}_{args.mode}_traffic.txt")
     if not os.path.exists(path):
         return None
     t = {}
@@ -162,7 +202,10 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOADS))
-    ap.add_argument("--mode", default="splitk", choices=["splitk", "single"])
+    ap.add_argument("--mode", default="fused",
+                    choices=["fused", "balanced", "splitk", "single"],
+                    help="fused: pa_decode_step (append + balanced decode, 2 kernels); "
+                         "balanced/splitk/single: slot mapping + cache write + that decode")
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--partition", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -214,23 +257,47 @@ def main(argv=None) -> int:
 
     # pass 2: the same steps, events bracketing the dominant kernel
     import paged_kv_cache_120_amd as pa
+
+    def dominant(st, e0, e1):
+        if args.mode == "fused":
+            runner.run_phase(st.copies, st.pool, st.block_size)
+            wr = st.write
+            e0.record()
+            pa.pa_decode_balanced_partials(st.query, st.key_cache, st.value_cache,
+                                           st.block_tables, st.context_lens, st.scale,
+                                           st.grid, st.bal_workspace, key=wr.key,
+                                           value=wr.value, slot_mapping=wr.slots)
+            e1.record()
+            pa.pa_decode_balanced_reduce(st.out, st.bal_workspace, st.context_lens,
+                                         st.key_cache.shape[2], st.block_tables.shape[1],
+                                         st.block_size, st.grid, slot_mapping=wr.slots)
+            return
+        runner.write_step(st)
+        e0.record()
+        if args.mode == "splitk":
+            pa.pa_decode_splitk(st.query, st.key_cache, st.value_cache, st.block_tables,
+                                st.context_lens, st.scale, st.partition_size, st.workspace)
+            e1.record()
+            pa.pa_decode_reduce(st.out, st.workspace, st.context_lens,
+                                st.block_tables.shape[1], st.block_size, st.partition_size)
+        elif args.mode == "balanced":
+            pa.pa_decode_balanced_partials(st.query, st.key_cache, st.value_cache,
+                                           st.block_tables, st.context_lens, st.scale,
+                                           st.grid, st.bal_workspace)
+            e1.record()
+            pa.pa_decode_balanced_reduce(st.out, st.bal_workspace, st.context_lens,
+                                         st.key_cache.shape[2], st.block_tables.shape[1],
+                                         st.block_size, st.grid)
+        else:
+            pa.pa_decode(st.out, st.query, st.key_cache, st.value_cache, st.block_tables,
+                         st.context_lens, st.scale)
+            e1.record()
+
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
-        st = steps[i % R]
-        runner.write_step(st)
-        evs[i][0].record()
-        if args.mode == "splitk":
-            pa.pa_decode_splitk(st.query, st.key_cache, st.value_cache, st.block_tables,
-                                st.context_lens, st.scale, st.partition_size, st.workspace)
-            evs[i][1].record()
-            pa.pa_decode_reduce(st.out, st.workspace, st.context_lens,
-                                st.block_tables.shape[1], st.block_size, st.partition_size)
-        else:
-            pa.pa_decode(st.out, st.query, st.key_cache, st.value_cache, st.block_tables,
-                         st.context_lens, st.scale)
-            evs[i][1].record()
+        dominant(steps[i % R], *evs[i])
     torch.cuda.synchronize()
     kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
@@ -249,7 +316,13 @@ def main(argv=None) -> int:
                      "read_bytes": int(2 * k * blk), "write_bytes": int(2 * k * blk)}
 
     kvb = kv_bytes(w)
-    kb = split_kernel_bytes(w) if args.mode == "splitk" else single_kernel_bytes(w)
+    if args.mode == "splitk":
+        kb, kname = split_kernel_bytes(w), "partition_kernel (split-KV)"
+    elif args.mode == "single":
+        kb, kname = single_kernel_bytes(w), "partition_kernel (single pass)"
+    else:
+        kb = balanced_kernel_bytes(w, steps[0].grid, args.mode == "fused")
+        kname = "balanced_kernel" + (" (fused append)" if args.mode == "fused" else "")
     achieved = kb / (kms * 1e-3) / 1e9
     value = kvb / (ms_step * 1e-3) / 1e9
 
@@ -277,6 +350,7 @@ def main(argv=None) -> int:
             "total_context_tokens": int(w.context_lens.sum()),
             "decode": args.mode, "partition_size": args.partition,
             "rotated_pool_copies": R, "seed": w.seed,
+            "balanced_grid": steps[0].grid,
         },
         "accumulate": "f32",
         "kv_bytes_per_step": kvb,
@@ -285,8 +359,7 @@ def main(argv=None) -> int:
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "decode_partition_kernel" if args.mode == "splitk"
-            else "decode_partition_kernel (single pass)",
+            "kernel": kname,
             "kernel_ms": round(kms, 5), "algorithmic_bytes": kb,
         },
     }

@@ -212,6 +212,36 @@ pa_status pa_decode_reduce(void* out, const void* workspace,
  */
 int32_t pa_balanced_grid(int32_t num_heads, int32_t num_kv_heads,
                          int32_t head_size, int32_t block_size);
+
+/*
+ * The two launches of the balanced decode, for callers that schedule (or
+ * time) them separately; pa_decode_balanced and pa_decode_step below are
+ * these two in order on one stream.
+ * pa_decode_balanced_partials: the per-range states.  key / value (fp16
+ *   [num_seqs, num_kv_heads, head_size], both or neither) make it also
+ *   append this step's token as pa_decode_step does; key_cache /
+ *   value_cache are then written, else only read.  slot_mapping (int32
+ *   [num_seqs] or NULL) receives the slots written.
+ * pa_decode_balanced_reduce: merges the states into out; needs the same
+ *   context_lens, shapes, grid and workspace; writes -1 to slot_mapping (if
+ *   given) for sequences with context_lens[i] <= 0.
+ */
+pa_status pa_decode_balanced_partials(
+    const void* query, void* key_cache, void* value_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+    int32_t num_blocks, float scale, int32_t grid, void* workspace,
+    size_t workspace_bytes, const void* key, const void* value,
+    int32_t* slot_mapping, hipStream_t stream);
+pa_status pa_decode_balanced_reduce(void* out, const void* workspace,
+                                    size_t workspace_bytes,
+                                    const int32_t* context_lens,
+                                    int32_t num_seqs, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_size,
+                                    int32_t max_blocks_per_seq,
+                                    int32_t block_size, int32_t grid,
+                                    int32_t* slot_mapping, hipStream_t stream);
 size_t pa_balanced_workspace_size(int32_t num_seqs, int32_t num_heads,
                                   int32_t num_kv_heads, int32_t head_size,
                                   int32_t grid);
@@ -225,6 +255,34 @@ pa_status pa_decode_balanced(void* out, const void* query,
                              int32_t num_blocks, float scale, int32_t grid,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/*
+ * pa_decode_step -- one whole decode step in two kernels: for every
+ * sequence i the token at position p = context_lens[i] - 1 is appended and
+ * then attended to, exactly as pa_slot_mapping + pa_cache_write +
+ * pa_decode_balanced would ([BOOK] §4.5: write this step's K/V by slot,
+ * then read the history by block table).
+ *   key, value    fp16 [num_seqs, num_kv_heads, head_size]: this step's
+ *                 K/V rows, copied bit-exactly to slot
+ *                 block_tables[i, p / block_size] * block_size +
+ *                 p % block_size of key_cache / value_cache (skipped if that
+ *                 block id is outside [0, num_blocks)).
+ *   slot_mapping  int32 [num_seqs] output, or NULL: the slot written per
+ *                 sequence (-1 where skipped or context_lens[i] <= 0).
+ *   Other arguments as pa_decode_balanced.  Preconditions of pa_decode and
+ *   pa_cache_write; sequences with context_lens[i] <= 0 append nothing and
+ *   get zeros.
+ */
+pa_status pa_decode_step(void* out, const void* query, const void* key,
+                         const void* value, void* key_cache, void* value_cache,
+                         int32_t* slot_mapping, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs,
+                         int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size,
+                         int32_t num_blocks, float scale, int32_t grid,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 #ifdef __cplusplus
 }

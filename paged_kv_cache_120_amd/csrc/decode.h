@@ -26,6 +26,12 @@ struct DecodeArgs {
   int num_seqs;              // balanced split
   int64_t* bal_total;        // [1]  sum of padded lengths (per kv head)
   int64_t* bal_prefix;       // [S]  exclusive prefix of padded lengths
+  // fused step (all null unless the kernel also appends this step's token):
+  // the token at position context_len-1 is taken from new_key/new_value
+  // ([S, H_kv, D]), stored into its slot, and its slot written to slot_out
+  const _Float16* new_key;
+  const _Float16* new_value;
+  int* slot_out;
   float scale;
 };
 
@@ -37,6 +43,7 @@ struct BalancedReduceArgs {
   const int* context_lens;
   const int64_t* total;
   const int64_t* prefix;
+  int* slot_out;             // fused step: -1 for sequences with no token
   int num_heads;
   int num_kv_heads;
   int grid;

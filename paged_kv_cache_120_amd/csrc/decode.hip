@@ -76,6 +76,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(
                    ok ? (uint32_t)valid * row_stride : 0u);
 }
 
+// Fused append: store this step's K/V row of head kvh (token `last` of the
+// sequence) into its slot, bit for bit, and record the slot.  Called by the
+// one range that holds token `last`; lanes 0 .. D/8-1 of wave 0 each move 16
+// bytes.  A slot outside the pool is skipped, as in the cache write.
+template <int D, int B>
+__device__ __forceinline__ void append_token(const DecodeArgs& a, int kvh,
+                                             int seq, int last) {
+  if (threadIdx.x >= D / 8) return;
+  const int blk = a.block_tables[(size_t)seq * a.max_blocks_per_seq + last / B];
+  const long long slot = (long long)blk * B + last % B;
+  const bool ok = blk >= 0 && blk < a.num_blocks;
+  if (kvh == 0 && threadIdx.x == 0 && a.slot_out)
+    a.slot_out[seq] = ok ? (int)slot : -1;
+  if (!ok) return;
+  const size_t src = ((size_t)seq * a.num_kv_heads + kvh) * D + threadIdx.x * 8;
+  const size_t dst = (size_t)slot * a.num_kv_heads * D + (size_t)kvh * D +
+                     threadIdx.x * 8;
+  _Float16* kc = const_cast<_Float16*>(reinterpret_cast<const _Float16*>(a.key_cache));
+  _Float16* vc = const_cast<_Float16*>(reinterpret_cast<const _Float16*>(a.value_cache));
+  *reinterpret_cast<u32x4*>(kc + dst) = *reinterpret_cast<const u32x4*>(a.new_key + src);
+  *reinterpret_cast<u32x4*>(vc + dst) = *reinterpret_cast<const u32x4*>(a.new_value + src);
+}
+
 // Final cross-wave merge.  Each wave left (m, l) per head and acc[head][d] in
 // LDS; every thread folds one (head, channel) and hands the result to `sink`
 // as (head in group, channel, max in base-2 units, sum, unnormalised out).
@@ -126,15 +149,18 @@ struct ValuPath {
     float l[kWaves][G];
   };
 
-  // t0 must be a multiple of RPI (callers pass multiples of 16)
+  // t0 must be a multiple of RPI (callers pass multiples of 16).  `last` is
+  // the position of this step's appended token if it lies in [t0, t1) and
+  // the step is fused, else -1.
   template <class Sink>
   __device__ static void run(const DecodeArgs& a, Smem& sm, int kvh, int seq,
-                             int t0, int t1, Sink& sink) {
+                             int t0, int t1, int last, Sink& sink) {
     const int H = a.num_heads;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane / LPR;
     const int c = lane % LPR;
+    if (last >= 0) append_token<D, B>(a, kvh, seq, last);
 
     u32x4 qv[G];
 #pragma unroll
@@ -173,6 +199,16 @@ struct ValuPath {
                                      a.num_blocks), off);
         vv[j] = load16(block_rsrc<B>(vbase, blk, lb, t1, row_stride, blk_bytes,
                                      a.num_blocks), off);
+      }
+      if (last >= 0 && base + TB > last) {     // the appended token's row
+        const size_t src = ((size_t)seq * a.num_kv_heads + kvh) * D + c * 8;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          if (base + j * RPI + r == last) {
+            kk[j] = *reinterpret_cast<const u32x4*>(a.new_key + src);
+            vv[j] = *reinterpret_cast<const u32x4*>(a.new_value + src);
+          }
+        }
       }
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
@@ -280,15 +316,16 @@ struct MfmaPath {
     float l[kWaves][G];
   };
 
-  // t0 must be a multiple of 16
+  // t0 must be a multiple of 16; `last` as for ValuPath::run
   template <class Sink>
   __device__ static void run(const DecodeArgs& a, Smem& sm, int kvh, int seq,
-                             int t0, int t1, Sink& sink) {
+                             int t0, int t1, int last, Sink& sink) {
     const int H = a.num_heads;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;                  // token row (A) / head (B, D)
     const int grp = lane >> 4;                  // lane group 0..3
+    if (last >= 0) append_token<D, B>(a, kvh, seq, last);
 
     f16x8 qb[KK];
 #pragma unroll
@@ -334,6 +371,20 @@ struct MfmaPath {
         for (int kk = 0; kk < KK; ++kk) {
           kr[mt][kk] = load16(rk, off + kk * 64);
           vr[mt][kk] = load16(rv, off + kk * 64);
+        }
+      }
+      if (last >= 0 && base + TB > last) {     // the appended token's row
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if (base + mt * 16 + col == last) {
+            const size_t src =
+                ((size_t)seq * a.num_kv_heads + kvh) * D + grp * 8;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+              kr[mt][kk] = *reinterpret_cast<const u32x4*>(a.new_key + src + kk * 32);
+              vr[mt][kk] = *reinterpret_cast<const u32x4*>(a.new_value + src + kk * 32);
+            }
+          }
         }
       }
 
@@ -470,7 +521,8 @@ __global__ __launch_bounds__(256) void partition_kernel(DecodeArgs a) {
       a.out[((size_t)seq * H + h) * D + d] = (_Float16)(O / L);
     }
   };
-  Path::run(a, sm, kvh, seq, t0, t1, sink);
+  const int last = (a.new_key && t1 == n) ? n - 1 : -1;
+  Path::run(a, sm, kvh, seq, t0, t1, last, sink);
 }
 
 // One workgroup of D threads per (query head, sequence): fold the fixed
@@ -523,23 +575,34 @@ __device__ __forceinline__ int64_t balanced_chunk(int64_t total, int grid) {
   return (c + 15) & ~(int64_t)15;
 }
 
-// Inclusive scan over the 256 threads of a workgroup (LDS buffer `buf`).
-__device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* buf) {
-  buf[threadIdx.x] = v;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int64_t u = threadIdx.x >= (unsigned)off ? buf[threadIdx.x - off] : 0;
-    __syncthreads();
-    buf[threadIdx.x] += u;
-    __syncthreads();
+// Inclusive scan over the 256 threads of a workgroup: shuffles within each
+// wave, then the wave totals through LDS.  `tot` receives the grand total.
+__device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* wave_sum,
+                                              int64_t& tot) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t u = __shfl_up(v, off);
+    if (lane >= off) v += u;
   }
-  return buf[threadIdx.x];
+  if (lane == 63) wave_sum[w] = v;
+  __syncthreads();
+  int64_t before = 0;
+  tot = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    before += i < w ? wave_sum[i] : 0;
+    tot += wave_sum[i];
+  }
+  __syncthreads();
+  return v + before;
 }
 
 template <class Path, int D, int B, int G>
 __global__ __launch_bounds__(256) void balanced_kernel(DecodeArgs a) {
   __shared__ typename Path::Smem sm;
-  __shared__ int64_t scan[256];
+  __shared__ int64_t wave_sum[kWaves];
   __shared__ int64_t found_start;
   __shared__ int found_seq;
   const int S = a.num_seqs;
@@ -547,22 +610,24 @@ __global__ __launch_bounds__(256) void balanced_kernel(DecodeArgs a) {
   const int max_tok = a.max_blocks_per_seq * B;
   const int w = blockIdx.x;
 
-  // padded length per kv head, prefix over sequences, 256 at a time; the
-  // first workgroup records the prefix and the total for the reduce, every
-  // workgroup finds the sequence holding its first flat position
+  // Padded lengths, 256 sequences per pass: their per-kv-head prefix (kept by
+  // the first workgroup for the reduce), the total, and the sequence whose
+  // flat span holds this workgroup's first position.  One pass when S <= 256.
   if (threadIdx.x == 0) found_seq = -1;
-  int64_t run = 0;                       // per-kv-head prefix before chunk
   int64_t total_per_kvh = 0;
+  int64_t my_len = 0, my_inc = 0;          // this thread's sequence (pass 0)
   for (int s0 = 0; s0 < S; s0 += 256) {
     const int si = s0 + (int)threadIdx.x;
     const int64_t len = si < S ? padded_len(a.context_lens[si], max_tok) : 0;
-    const int64_t inc = block_scan(len, scan);
-    const int64_t chunk_sum = scan[255];
-    if (w == 0 && si < S) a.bal_prefix[si] = run + inc - len;
-    __syncthreads();
-    run += chunk_sum;
+    int64_t chunk = 0;
+    const int64_t inc = block_scan(len, wave_sum, chunk);
+    if (w == 0 && si < S) a.bal_prefix[si] = total_per_kvh + inc - len;
+    if (s0 == 0) {
+      my_len = len;
+      my_inc = inc;
+    }
+    total_per_kvh += chunk;
   }
-  total_per_kvh = run;
   if (w == 0 && threadIdx.x == 0) a.bal_total[0] = total_per_kvh;
   const int64_t total = total_per_kvh * Hkv;
   const int64_t C = balanced_chunk(total, gridDim.x);
@@ -570,20 +635,28 @@ __global__ __launch_bounds__(256) void balanced_kernel(DecodeArgs a) {
   if (total == 0 || start >= total) return;
   const int64_t end = start + C < total ? start + C : total;
 
-  run = 0;
-  for (int s0 = 0; s0 < S; s0 += 256) {
-    const int si = s0 + (int)threadIdx.x;
-    const int64_t len = si < S ? padded_len(a.context_lens[si], max_tok) * Hkv : 0;
-    const int64_t inc = block_scan(len, scan);
-    const int64_t chunk_sum = scan[255];
-    // the one sequence whose flat span [run+inc-len, run+inc) holds start
-    if (len > 0 && run + inc - len <= start && start < run + inc) {
-      found_seq = si;
-      found_start = run + inc - len;
+  if (S <= 256) {
+    // flat span of sequence si: [(inc - len) * H_kv, inc * H_kv)
+    if (my_len > 0 && (my_inc - my_len) * Hkv <= start && start < my_inc * Hkv) {
+      found_seq = (int)threadIdx.x;
+      found_start = (my_inc - my_len) * Hkv;
     }
     __syncthreads();
-    if (found_seq >= 0) break;
-    run += chunk_sum;
+  } else {
+    int64_t run = 0;
+    for (int s0 = 0; s0 < S; s0 += 256) {
+      const int si = s0 + (int)threadIdx.x;
+      const int64_t len = si < S ? padded_len(a.context_lens[si], max_tok) * Hkv : 0;
+      int64_t chunk = 0;
+      const int64_t inc = block_scan(len, wave_sum, chunk);
+      if (len > 0 && run + inc - len <= start && start < run + inc) {
+        found_seq = si;
+        found_start = run + inc - len;
+      }
+      __syncthreads();
+      if (found_seq >= 0) break;
+      run += chunk;
+    }
   }
   int s = found_seq;
   int64_t E = found_start;               // flat start of sequence s
@@ -614,7 +687,8 @@ __global__ __launch_bounds__(256) void balanced_kernel(DecodeArgs a) {
         }
         a.ws_out[pi * D + d] = O;
       };
-      Path::run(a, sm, kvh, s, ta, tv, sink);
+      const int last = (a.new_key && tv == n) ? n - 1 : -1;
+      Path::run(a, sm, kvh, s, ta, tv, last, sink);
     }
     pos = seg_end;
     if (pos == E + (int64_t)Hkv * np) {
@@ -642,6 +716,7 @@ __global__ __launch_bounds__(D) void balanced_reduce_kernel(BalancedReduceArgs a
   _Float16* o = a.out + ((size_t)seq * H + h) * D + d;
   if (n <= 0) {
     *o = (_Float16)0.f;
+    if (a.slot_out && h == 0 && d == 0) a.slot_out[seq] = -1;
     return;
   }
   const int64_t np = (int64_t)((n + 15) & ~15);

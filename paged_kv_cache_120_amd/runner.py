@@ -1,8 +1,10 @@
 """Drive one decode step through the library on device tensors.
 
 A step is: copy-on-write block copies (if any), the slot mapping of the new
-tokens, the cache write, then decode -- single-pass (``pa_decode``) or split
-(``pa_decode_splitk`` + ``pa_decode_reduce``).  Inputs are plain arrays (a
+tokens, the cache write, then decode -- single-pass (``pa_decode``), split
+(``pa_decode_splitk`` + ``pa_decode_reduce``) or balanced
+(``pa_decode_balanced``); or, mode "fused", copies then ``pa_decode_step``
+(slot mapping, cache write and balanced decode in two kernels).  Inputs are plain arrays (a
 workload object with the attributes used below); this module only uploads
 them and calls the binding, so every step runs in the library's kernels.
 """
@@ -16,7 +18,8 @@ import torch
 
 from . import (pa_balanced_grid, pa_balanced_workspace_size, pa_cache_write,
                pa_copy_blocks, pa_decode, pa_decode_balanced, pa_decode_reduce,
-               pa_decode_splitk, pa_slot_mapping, pa_splitk_workspace_size)
+               pa_decode_splitk, pa_decode_step, pa_slot_mapping,
+               pa_splitk_workspace_size)
 
 
 def _t(a, dev, dtype=None):
@@ -145,7 +148,20 @@ def decode_step(step: DeviceStep, mode: str = "splitk", stream=None) -> None:
         raise ValueError(mode)
 
 
+def fused_step(step: DeviceStep, stream=None) -> None:
+    """COW copies (if any), then pa_decode_step: append + balanced decode."""
+    run_phase(step.copies, step.pool, step.block_size, stream=stream)
+    wr = step.write
+    pa_decode_step(step.out, step.query, wr.key, wr.value, step.key_cache,
+                   step.value_cache, step.block_tables, step.context_lens,
+                   step.scale, step.grid, step.bal_workspace,
+                   slot_mapping=wr.slots, stream=stream)
+
+
 def full_step(step: DeviceStep, mode: str = "splitk", stream=None) -> None:
+    if mode == "fused":
+        fused_step(step, stream=stream)
+        return
     write_step(step, stream=stream)
     decode_step(step, mode=mode, stream=stream)
 
@@ -160,4 +176,5 @@ def split_views(step: DeviceStep, S: int, H: int, D: int, M: int, B: int, P: int
 
 
 __all__: List[str] = ["DeviceStep", "upload", "apply_history", "write_step",
-                      "decode_step", "full_step", "run_phase", "split_views"]
+                      "decode_step", "fused_step", "full_step", "run_phase",
+                      "split_views"]

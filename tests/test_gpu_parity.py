@@ -72,7 +72,15 @@ SMALL = ["c1", "c1_page_tables", "c2_small", "c3_small", "c4_small", "c4_r0_smal
          "c5_b32_small", "c5_b64_small"]
 
 
-MODES = ["single", "splitk", "balanced"]
+MODES = ["single", "splitk", "balanced", "fused"]
+
+
+def decode_only(runner, st, mode):
+    """Decode with the step's K/V already written (fused: written again)."""
+    if mode == "fused":
+        runner.fused_step(st)
+    else:
+        runner.decode_step(st, mode)
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -112,13 +120,14 @@ def test_split_partials_match_oracle(name):
 @pytest.mark.parametrize("name,mode", [("c1", "splitk"), ("c2", "splitk"), ("c2", "single"),
                                        ("c2", "balanced"), ("c3", "splitk"),
                                        ("c3", "balanced"), ("c4", "splitk"),
-                                       ("c4", "balanced")])
+                                       ("c4", "balanced"), ("c2", "fused"),
+                                       ("c3", "fused"), ("c4", "fused")])
 def test_parity_full(name, mode):
     print(f"[parity-full] {name} {mode}", flush=True)
     check_all(workloads.make(name), mode)
 
 
-@pytest.mark.parametrize("mode", ["splitk", "balanced"])
+@pytest.mark.parametrize("mode", ["splitk", "balanced", "fused"])
 @pytest.mark.parametrize("name", ["c5_b32", "c5_b64"])
 def test_parity_full_long_context_sampled(name, mode):
     print(f"[parity-full] {name} {mode} (sampled heads)", flush=True)
@@ -180,7 +189,7 @@ def test_zero_context_gives_zeros(mode):
     ctx = w.context_lens.copy()
     ctx[2] = 0
     st.context_lens.copy_(torch.from_numpy(ctx))
-    runner.decode_step(st, mode)
+    decode_only(runner, st, mode)
     torch.cuda.synchronize()
     out = st.out.cpu().numpy().astype(np.float64)
     assert (out[2] == 0).all()
@@ -206,7 +215,7 @@ def test_permutation_invariance_bitwise():
             st.pool = newpool
             st.block_tables = torch.from_numpy(perm[w.block_tables].astype(np.int32)).cuda()
         for mode in MODES:
-            runner.decode_step(st, mode)
+            decode_only(runner, st, mode)
             torch.cuda.synchronize()
             outs.append(st.out.cpu().numpy().copy())
     k = len(MODES)
@@ -240,6 +249,25 @@ def test_shared_prefix_equals_private_copies_bitwise():
     assert (st.out.cpu().numpy().view(np.uint16) == shared.view(np.uint16)).all()
 
 
+def test_fused_step_slot_output_for_empty_sequences():
+    pa, runner = _gpu()
+    w = workloads.make("c2_small")
+    st = runner.upload(w)
+    runner.apply_history(w, st)
+    ctx = w.context_lens.copy()
+    ctx[1] = 0
+    st.context_lens.copy_(torch.from_numpy(ctx))
+    st.write.slots.fill_(12345)
+    runner.fused_step(st)
+    torch.cuda.synchronize()
+    got = st.write.slots.cpu().numpy()
+    ref = oracle.slot_mapping(w.step_write.table, w.step_write.seq, w.step_write.pos,
+                              w.block_size)
+    assert got[1] == -1
+    keep = [i for i in range(w.num_seqs) if i != 1]
+    assert (got[keep] == ref[keep]).all()
+
+
 @pytest.mark.parametrize("grid", [1, 3, 17, 200, 5000])
 @pytest.mark.parametrize("name", ["c3_small", "c2_small", "c5_b64_small"])
 def test_balanced_any_grid(name, grid):
@@ -268,7 +296,7 @@ def test_repeat_calls_deterministic():
     for mode in MODES:
         st = run_gpu(w, mode)
         a = st.out.cpu().numpy().copy()
-        runner.decode_step(st, mode)
+        decode_only(runner, st, mode)
         torch.cuda.synchronize()
         assert (a.view(np.uint16) == st.out.cpu().numpy().view(np.uint16)).all(), mode
 
