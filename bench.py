@@ -60,9 +60,10 @@ def split_kernel_bytes(w) -> int:
     return kv_bytes(w) + S * H * D * 2 + table + parts
 
 
-def balanced_ranges(w, grid: int) -> int:
-    """Number of (workgroup, sequence, kv head) ranges with valid tokens in
-    the balanced decode (each writes one partial state per query head)."""
+def balanced_split_ranges(w, grid: int) -> int:
+    """Ranges of the balanced decode that belong to (sequence, kv head)
+    pairs cut across several workgroups: each stores one partial state per
+    query head, which the pair's last workgroup reads back to merge."""
     M = w.max_blocks_per_seq * w.block_size
     n = np.minimum(w.context_lens.astype(np.int64), M)
     pad = np.where(n > 0, (n + 15) // 16 * 16, 0)
@@ -79,22 +80,23 @@ def balanced_ranges(w, grid: int) -> int:
             continue
         for kvh in range(Hkv):
             F = int(prefix[i]) * Hkv + kvh * int(pad[i])
-            for wg in range(F // C, (F + int(pad[i]) - 1) // C + 1):
-                if max(wg * C, F) - F < n[i]:
-                    count += 1
+            k = (F + int(n[i]) - 1) // C - F // C + 1
+            if k > 1:
+                count += k
     return count
 
 
 def balanced_kernel_bytes(w, grid: int, fused: bool) -> int:
-    """Algorithmic bytes of one balanced partials launch: KV rows, query,
-    table entries, partial states written, and (fused step) this step's K/V
-    rows read and written plus the slots."""
+    """Algorithmic bytes of one balanced-kernel launch: KV rows, query, table
+    entries, output, partial states of cut pairs (written, then read by the
+    merging workgroup) and, for the fused step, this step's K/V rows (read
+    and written) and the slots."""
     S, H, D = w.query.shape
     n = w.context_lens.astype(np.int64)
     table = int(((n + w.block_size - 1) // w.block_size).sum()) * 4
-    parts = balanced_ranges(w, grid) * w.group * (D + 2) * 4
+    parts = 2 * balanced_split_ranges(w, grid) * w.group * (D + 2) * 4
     extra = (2 * 2 * S * w.num_kv_heads * D * 2 + S * 4) if fused else 0
-    return kv_bytes(w) + S * H * D * 2 + table + parts + extra
+    return kv_bytes(w) + 2 * S * H * D * 2 + table + parts + extra
 
 
 def single_kernel_bytes(w) -> int:
@@ -255,65 +257,49 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # pass 2: the same steps, events bracketing the dominant kernel
+    # pass 2: the dominant kernel alone, launched back to back over the same
+    # rotated inputs, between one pair of events on the launch stream
     import paged_kv_cache_120_amd as pa
 
-    def dominant(st, e0, e1):
-        if args.mode == "fused":
-            runner.run_phase(st.copies, st.pool, st.block_size)
-            wr = st.write
-            e0.record()
-            pa.pa_decode_balanced_partials(st.query, st.key_cache, st.value_cache,
-                                           st.block_tables, st.context_lens, st.scale,
-                                           st.grid, st.bal_workspace, key=wr.key,
-                                           value=wr.value, slot_mapping=wr.slots)
-            e1.record()
-            pa.pa_decode_balanced_reduce(st.out, st.bal_workspace, st.context_lens,
-                                         st.key_cache.shape[2], st.block_tables.shape[1],
-                                         st.block_size, st.grid, slot_mapping=wr.slots)
-            return
-        runner.write_step(st)
-        e0.record()
+    def dominant(st):
         if args.mode == "splitk":
             pa.pa_decode_splitk(st.query, st.key_cache, st.value_cache, st.block_tables,
                                 st.context_lens, st.scale, st.partition_size, st.workspace)
-            e1.record()
-            pa.pa_decode_reduce(st.out, st.workspace, st.context_lens,
-                                st.block_tables.shape[1], st.block_size, st.partition_size)
-        elif args.mode == "balanced":
-            pa.pa_decode_balanced_partials(st.query, st.key_cache, st.value_cache,
-                                           st.block_tables, st.context_lens, st.scale,
-                                           st.grid, st.bal_workspace)
-            e1.record()
-            pa.pa_decode_balanced_reduce(st.out, st.bal_workspace, st.context_lens,
-                                         st.key_cache.shape[2], st.block_tables.shape[1],
-                                         st.block_size, st.grid)
         else:
-            pa.pa_decode(st.out, st.query, st.key_cache, st.value_cache, st.block_tables,
-                         st.context_lens, st.scale)
-            e1.record()
+            runner.decode_step(st, "fused_only" if args.mode == "fused" else args.mode)
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    for i in range(min(args.warmup, 4)):
+        dominant(steps[i % R])
+    e2 = torch.cuda.Event(enable_timing=True)
+    e3 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    e2.record()
     for i in range(args.steps):
-        dominant(steps[i % R], *evs[i])
+        dominant(steps[i % R])
+    e3.record()
     torch.cuda.synchronize()
-    kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kms = e2.elapsed_time(e3) / args.steps
+    # leave the outputs of a full step for the parity check
+    runner.full_step(steps[(args.steps - 1) % R], mode=args.mode)
+    torch.cuda.synchronize()
 
     calib = None
     if args.calibrate:
-        free = np.flatnonzero(w.ref_cnt == 0)
-        k = min(args.calibrate, len(free) // 2)
-        if k > 0:
-            src = torch.from_numpy(free[:k].astype(np.int32)).to(dev)
-            dst = torch.from_numpy(free[k:2 * k].astype(np.int32)).to(dev)
-            torch.cuda.synchronize()
-            pa.pa_copy_blocks(steps[0].key_cache, steps[0].value_cache, src, dst)
-            torch.cuda.synchronize()
-            blk = w.block_size * w.num_kv_heads * w.head_size * 2
-            calib = {"kernel": "copy_blocks_kernel", "pairs": int(k),
-                     "read_bytes": int(2 * k * blk), "write_bytes": int(2 * k * blk)}
+        # a plain copy of known size for scaling HBM counters: pa_copy_blocks
+        # of K contiguous blocks onto the next K in a scratch pool of this
+        # layer's block shape (K and V halves), outside the timed region
+        k = int(args.calibrate)
+        cal = torch.zeros((2, 2 * k) + tuple(steps[0].pool.shape[2:]),
+                          dtype=torch.float16, device=dev)
+        src = torch.arange(0, k, dtype=torch.int32, device=dev)
+        dst = torch.arange(k, 2 * k, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        pa.pa_copy_blocks(cal[0], cal[1], src, dst)
+        torch.cuda.synchronize()
+        blk = w.block_size * w.num_kv_heads * w.head_size * 2
+        calib = {"kernel": "copy_blocks_kernel", "pairs": k,
+                 "read_bytes": int(2 * k * blk), "write_bytes": int(2 * k * blk)}
+        del cal
 
     kvb = kv_bytes(w)
     if args.mode == "splitk":
@@ -323,6 +309,8 @@ def main(argv=None) -> int:
     else:
         kb = balanced_kernel_bytes(w, steps[0].grid, args.mode == "fused")
         kname = "balanced_kernel" + (" (fused append)" if args.mode == "fused" else "")
+    if args.mode == "single":
+        kname = "partition_kernel (single pass)"
     achieved = kb / (kms * 1e-3) / 1e9
     value = kvb / (ms_step * 1e-3) / 1e9
 

@@ -191,57 +191,32 @@ pa_status pa_decode_reduce(void* out, const void* workspace,
 /*
  * Balanced split-KV decode: the same result as pa_decode (within the same
  * tolerance; the summation order differs), with the work divided evenly
- * instead of by fixed partitions.  The KV work of all (sequence, kv head)
- * pairs is laid end to end -- sequence-major, then kv head, then token, each
- * sequence padded to a multiple of 16 tokens -- and cut into `grid` equal
- * slices, one per workgroup; a workgroup writes one partial softmax state
- * (max, sum, unnormalised output; the form of [BOOK] §4.6) for every pair its
- * slice touches, and a second kernel merges each pair's states with the
- * §4.6 recurrence.  With `grid` = pa_balanced_grid(...) every workgroup is
+ * instead of by sequence or fixed partition, in ONE kernel.  The KV work of
+ * all (sequence, kv head) pairs is laid end to end -- sequence-major, then
+ * kv head, then token, each sequence padded to a multiple of 16 tokens --
+ * and cut into `grid` equal slices, one per workgroup.  A pair inside one
+ * slice is finished there; a pair cut across k slices leaves k partial
+ * softmax states (max, sum, unnormalised output: the form of [BOOK] §4.6),
+ * and whichever of its workgroups finishes last merges them with the §4.6
+ * recurrence.  With `grid` = pa_balanced_grid(...) every workgroup is
  * resident from the start, so none waits and none straggles.
  *
  * pa_balanced_grid: workgroups of the balanced kernel that the current
  *   device holds at once for this shape (0 if unsupported or unknown).
  * pa_balanced_workspace_size: bytes of device workspace for `grid`
- *   workgroups (0 on bad arguments).  Layout: [total int64][prefix int64 x
- *   num_seqs] padded to 16 bytes, then fp32 max [rows], sum [rows], out
- *   [rows, head_size] with rows = (grid + num_seqs*num_kv_heads) * group.
+ *   workgroups (0 on bad arguments).  Layout: int32 counters
+ *   [num_seqs * num_kv_heads] padded to 16 bytes, then fp32 max [rows],
+ *   sum [rows], out [rows, head_size] with rows = (grid + num_seqs *
+ *   num_kv_heads) * group.
+ *   The counters must be zero before the first call (zero-fill the whole
+ *   workspace once); every completed call leaves them zero.  Calls that
+ *   share a workspace must not overlap.
  * pa_decode_balanced: arguments as pa_decode plus grid (> 0) and the
- *   workspace (16-byte aligned, >= pa_balanced_workspace_size).  Enqueues
- *   two kernels on `stream`.  Same preconditions and guards as pa_decode.
+ *   workspace (16-byte aligned, >= pa_balanced_workspace_size).  Same
+ *   preconditions and guards as pa_decode.
  */
 int32_t pa_balanced_grid(int32_t num_heads, int32_t num_kv_heads,
                          int32_t head_size, int32_t block_size);
-
-/*
- * The two launches of the balanced decode, for callers that schedule (or
- * time) them separately; pa_decode_balanced and pa_decode_step below are
- * these two in order on one stream.
- * pa_decode_balanced_partials: the per-range states.  key / value (fp16
- *   [num_seqs, num_kv_heads, head_size], both or neither) make it also
- *   append this step's token as pa_decode_step does; key_cache /
- *   value_cache are then written, else only read.  slot_mapping (int32
- *   [num_seqs] or NULL) receives the slots written.
- * pa_decode_balanced_reduce: merges the states into out; needs the same
- *   context_lens, shapes, grid and workspace; writes -1 to slot_mapping (if
- *   given) for sequences with context_lens[i] <= 0.
- */
-pa_status pa_decode_balanced_partials(
-    const void* query, void* key_cache, void* value_cache,
-    const int32_t* block_tables, int32_t max_blocks_per_seq,
-    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-    int32_t num_blocks, float scale, int32_t grid, void* workspace,
-    size_t workspace_bytes, const void* key, const void* value,
-    int32_t* slot_mapping, hipStream_t stream);
-pa_status pa_decode_balanced_reduce(void* out, const void* workspace,
-                                    size_t workspace_bytes,
-                                    const int32_t* context_lens,
-                                    int32_t num_seqs, int32_t num_heads,
-                                    int32_t num_kv_heads, int32_t head_size,
-                                    int32_t max_blocks_per_seq,
-                                    int32_t block_size, int32_t grid,
-                                    int32_t* slot_mapping, hipStream_t stream);
 size_t pa_balanced_workspace_size(int32_t num_seqs, int32_t num_heads,
                                   int32_t num_kv_heads, int32_t head_size,
                                   int32_t grid);
@@ -257,7 +232,7 @@ pa_status pa_decode_balanced(void* out, const void* query,
                              hipStream_t stream);
 
 /*
- * pa_decode_step -- one whole decode step in two kernels: for every
+ * pa_decode_step -- one whole decode step in one kernel: for every
  * sequence i the token at position p = context_lens[i] - 1 is appended and
  * then attended to, exactly as pa_slot_mapping + pa_cache_write +
  * pa_decode_balanced would ([BOOK] §4.5: write this step's K/V by slot,
@@ -269,9 +244,9 @@ pa_status pa_decode_balanced(void* out, const void* query,
  *                 block id is outside [0, num_blocks)).
  *   slot_mapping  int32 [num_seqs] output, or NULL: the slot written per
  *                 sequence (-1 where skipped or context_lens[i] <= 0).
- *   Other arguments as pa_decode_balanced.  Preconditions of pa_decode and
- *   pa_cache_write; sequences with context_lens[i] <= 0 append nothing and
- *   get zeros.
+ *   Other arguments as pa_decode_balanced (same workspace rules).
+ *   Preconditions of pa_decode and pa_cache_write; sequences with
+ *   context_lens[i] <= 0 append nothing and get zeros.
  */
 pa_status pa_decode_step(void* out, const void* query, const void* key,
                          const void* value, void* key_cache, void* value_cache,

@@ -19,8 +19,7 @@ __all__ = [
     "pa_slot_mapping", "pa_cache_write", "pa_copy_blocks", "pa_decode",
     "pa_splitk_workspace_size", "pa_decode_splitk", "pa_decode_reduce",
     "pa_balanced_grid", "pa_balanced_workspace_size", "pa_decode_balanced",
-    "pa_decode_step", "pa_decode_balanced_partials", "pa_decode_balanced_reduce",
-    "STATUS",
+    "pa_decode_step", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,11 +62,6 @@ def _load() -> ctypes.CDLL:
         "pa_balanced_workspace_size": (sz, [i32, i32, i32, i32, i32]),
         "pa_decode_balanced": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
                                               i32, i32, i32, f32, i32, vp, sz, vp]),
-        "pa_decode_balanced_partials": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, i32, i32,
-                                                       i32, i32, i32, i32, f32, i32, vp,
-                                                       sz, vp, vp, vp, vp]),
-        "pa_decode_balanced_reduce": (ctypes.c_int, [vp, vp, sz, vp, i32, i32, i32, i32,
-                                                     i32, i32, i32, vp, vp]),
         "pa_decode_step": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32,
                                           i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]),
     }
@@ -264,8 +258,9 @@ def pa_decode_reduce(out, workspace, context_lens, max_blocks_per_seq: int,
 def pa_decode_balanced(out, query, key_cache, value_cache, block_tables,
                        context_lens, scale: float, grid: int, workspace,
                        stream=None) -> None:
-    """Balanced split-KV decode (two kernels); workspace: a contiguous device
-    tensor of at least pa_balanced_workspace_size(...) bytes."""
+    """Balanced split-KV decode (one kernel); workspace: a contiguous device
+    tensor of at least pa_balanced_workspace_size(...) bytes, zero-filled
+    before its first use (each call leaves its counters at zero)."""
     torch = _torch()
     (q, kc, vc, bt, cl), (S, H, Hkv, D, B, nb, M) = _decode_common(
         query, key_cache, value_cache, block_tables, context_lens)
@@ -299,37 +294,3 @@ def pa_decode_step(out, query, key, value, key_cache, value_cache, block_tables,
         _dev(value, torch.float16, "value", 3), kc, vc, sm, bt, M, cl, S, H, Hkv, D,
         B, nb, float(scale), int(grid), ws, nbytes, _stream(stream)))
 
-
-def pa_decode_balanced_partials(query, key_cache, value_cache, block_tables,
-                                context_lens, scale: float, grid: int, workspace,
-                                key=None, value=None, slot_mapping=None,
-                                stream=None) -> None:
-    """First launch of the balanced decode (optionally appending key/value)."""
-    torch = _torch()
-    (q, kc, vc, bt, cl), (S, H, Hkv, D, B, nb, M) = _decode_common(
-        query, key_cache, value_cache, block_tables, context_lens)
-    kp = None if key is None else _dev(key, torch.float16, "key", 3)
-    vp_ = None if value is None else _dev(value, torch.float16, "value", 3)
-    sm = None if slot_mapping is None else _dev(slot_mapping, torch.int32,
-                                                "slot_mapping", 1)
-    ws = _dev(workspace, workspace.dtype, "workspace")
-    nbytes = workspace.numel() * workspace.element_size()
-    _check("pa_decode_balanced_partials", _lib().pa_decode_balanced_partials(
-        q, kc, vc, bt, M, cl, S, H, Hkv, D, B, nb, float(scale), int(grid), ws,
-        nbytes, kp, vp_, sm, _stream(stream)))
-
-
-def pa_decode_balanced_reduce(out, workspace, context_lens, num_kv_heads: int,
-                              max_blocks_per_seq: int, block_size: int, grid: int,
-                              slot_mapping=None, stream=None) -> None:
-    """Second launch of the balanced decode: merge the states into out."""
-    torch = _torch()
-    S, H, D = out.shape
-    sm = None if slot_mapping is None else _dev(slot_mapping, torch.int32,
-                                                "slot_mapping", 1)
-    ws = _dev(workspace, workspace.dtype, "workspace")
-    nbytes = workspace.numel() * workspace.element_size()
-    _check("pa_decode_balanced_reduce", _lib().pa_decode_balanced_reduce(
-        _dev(out, torch.float16, "out", 3), ws, nbytes,
-        _dev(context_lens, torch.int32, "context_lens", 1), S, H, int(num_kv_heads), D,
-        int(max_blocks_per_seq), int(block_size), int(grid), sm, _stream(stream)))

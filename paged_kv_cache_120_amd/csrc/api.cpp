@@ -280,10 +280,10 @@ int32_t pa_balanced_grid(int32_t num_heads, int32_t num_kv_heads,
   return pa::balanced_grid(head_size, block_size, num_heads / num_kv_heads);
 }
 
-// [total int64][prefix int64 x S] padded to 16 bytes, then max, sum (fp32
-// [rows]) and out (fp32 [rows, D]) with rows = (grid + S*H_kv) * g.
-static size_t balanced_header_bytes(int32_t num_seqs) {
-  return ((size_t)(1 + num_seqs) * 8 + 15) & ~(size_t)15;
+// [counters int32 x S*H_kv] padded to 16 bytes, then max, sum (fp32 [rows])
+// and out (fp32 [rows, D]) with rows = (grid + S*H_kv) * g.
+static size_t balanced_header_bytes(int32_t num_seqs, int32_t num_kv_heads) {
+  return ((size_t)num_seqs * num_kv_heads * 4 + 15) & ~(size_t)15;
 }
 
 size_t pa_balanced_workspace_size(int32_t num_seqs, int32_t num_heads,
@@ -294,17 +294,20 @@ size_t pa_balanced_workspace_size(int32_t num_seqs, int32_t num_heads,
     return 0;
   const uint64_t rows = ((uint64_t)grid + (uint64_t)num_seqs * num_kv_heads) *
                         (uint64_t)(num_heads / num_kv_heads);
-  return balanced_header_bytes(num_seqs) + (size_t)(rows * 8 + rows * head_size * 4);
+  return balanced_header_bytes(num_seqs, num_kv_heads) +
+         (size_t)(rows * 8 + rows * head_size * 4);
 }
 
-pa_status pa_decode_balanced_partials(
-    const void* query, void* key_cache, void* value_cache,
-    const int32_t* block_tables, int32_t max_blocks_per_seq,
-    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-    int32_t num_blocks, float scale, int32_t grid, void* workspace,
-    size_t workspace_bytes, const void* key, const void* value,
-    int32_t* slot_mapping, hipStream_t stream) {
+static pa_status balanced_impl(void* out, const void* query, void* key_cache,
+                               void* value_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_size, int32_t block_size,
+                               int32_t num_blocks, float scale, int32_t grid,
+                               void* workspace, size_t workspace_bytes,
+                               const void* key, const void* value,
+                               int32_t* slot_mapping, hipStream_t stream) {
   pa_status st = check_decode(query, key_cache, value_cache, block_tables,
                               max_blocks_per_seq, context_lens, num_seqs,
                               num_heads, num_kv_heads, head_size, block_size,
@@ -312,9 +315,9 @@ pa_status pa_decode_balanced_partials(
   if (st != PA_OK) return st;
   if (grid <= 0 || grid > (1 << 20)) return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
-  if (!workspace) return PA_ERR_NULL;
-  if ((key == nullptr) != (value == nullptr)) return PA_ERR_NULL;
-  if (!aligned(workspace, 16) || (key && (!aligned(key, 16) || !aligned(value, 16))) ||
+  if (!out || !workspace) return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(workspace, 16) ||
+      (key && (!aligned(key, 16) || !aligned(value, 16))) ||
       (slot_mapping && !aligned(slot_mapping, 4)))
     return PA_ERR_ALIGN;
   if (workspace_bytes < pa_balanced_workspace_size(num_seqs, num_heads,
@@ -323,9 +326,10 @@ pa_status pa_decode_balanced_partials(
   const int32_t g = num_heads / num_kv_heads;
   const size_t rows = ((size_t)grid + (size_t)num_seqs * num_kv_heads) * g;
   char* ws = static_cast<char*>(workspace);
-  int64_t* total = reinterpret_cast<int64_t*>(ws);
-  float* fmax = reinterpret_cast<float*>(ws + balanced_header_bytes(num_seqs));
+  float* fmax = reinterpret_cast<float*>(
+      ws + balanced_header_bytes(num_seqs, num_kv_heads));
   pa::DecodeArgs a = {};
+  a.out = static_cast<_Float16*>(out);
   a.ws_max = fmax;
   a.ws_sum = fmax + rows;
   a.ws_out = fmax + 2 * rows;
@@ -339,60 +343,13 @@ pa_status pa_decode_balanced_partials(
   a.num_kv_heads = num_kv_heads;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
-  a.bal_total = total;
-  a.bal_prefix = total + 1;
+  a.bal_count = reinterpret_cast<int*>(ws);
   a.new_key = static_cast<const _Float16*>(key);
   a.new_value = static_cast<const _Float16*>(value);
-  a.slot_out = key ? slot_mapping : nullptr;
+  a.slot_out = slot_mapping;
   a.split = 1;
   a.scale = scale;
   return hip_status(pa::launch_balanced(a, head_size, block_size, g, grid, stream));
-}
-
-pa_status pa_decode_balanced_reduce(void* out, const void* workspace,
-                                    size_t workspace_bytes,
-                                    const int32_t* context_lens,
-                                    int32_t num_seqs, int32_t num_heads,
-                                    int32_t num_kv_heads, int32_t head_size,
-                                    int32_t max_blocks_per_seq,
-                                    int32_t block_size, int32_t grid,
-                                    int32_t* slot_mapping, hipStream_t stream) {
-  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_seqs > 65535 ||
-      num_heads > 65535 || num_heads % num_kv_heads != 0 ||
-      max_blocks_per_seq <= 0 || block_size <= 0 || grid <= 0 ||
-      grid > (1 << 20) || (int64_t)max_blocks_per_seq * block_size >= (1ll << 31))
-    return PA_ERR_SHAPE;
-  if (!supported_head(head_size) || !supported_block(block_size) ||
-      !supported_group(num_heads / num_kv_heads))
-    return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PA_OK;
-  if (!out || !workspace || !context_lens) return PA_ERR_NULL;
-  if (!aligned(out, 16) || !aligned(workspace, 16) || !aligned(context_lens, 4) ||
-      (slot_mapping && !aligned(slot_mapping, 4)))
-    return PA_ERR_ALIGN;
-  if (workspace_bytes < pa_balanced_workspace_size(num_seqs, num_heads,
-                                                   num_kv_heads, head_size, grid))
-    return PA_ERR_WORKSPACE;
-  const int32_t g = num_heads / num_kv_heads;
-  const size_t rows = ((size_t)grid + (size_t)num_seqs * num_kv_heads) * g;
-  const char* ws = static_cast<const char*>(workspace);
-  const int64_t* total = reinterpret_cast<const int64_t*>(ws);
-  const float* fmax =
-      reinterpret_cast<const float*>(ws + balanced_header_bytes(num_seqs));
-  pa::BalancedReduceArgs r = {};
-  r.out = static_cast<_Float16*>(out);
-  r.ws_max = fmax;
-  r.ws_sum = fmax + rows;
-  r.ws_out = fmax + 2 * rows;
-  r.context_lens = context_lens;
-  r.total = total;
-  r.prefix = total + 1;
-  r.slot_out = slot_mapping;
-  r.num_heads = num_heads;
-  r.num_kv_heads = num_kv_heads;
-  r.grid = grid;
-  r.max_tokens = max_blocks_per_seq * block_size;
-  return hip_status(pa::launch_balanced_reduce(r, head_size, num_seqs, stream));
 }
 
 pa_status pa_decode_balanced(void* out, const void* query, const void* key_cache,
@@ -405,17 +362,12 @@ pa_status pa_decode_balanced(void* out, const void* query, const void* key_cache
                              int32_t num_blocks, float scale, int32_t grid,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream) {
-  if (num_seqs > 0 && !out) return PA_ERR_NULL;
-  pa_status st = pa_decode_balanced_partials(
-      query, const_cast<void*>(key_cache), const_cast<void*>(value_cache),
-      block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
-      num_kv_heads, head_size, block_size, num_blocks, scale, grid, workspace,
-      workspace_bytes, nullptr, nullptr, nullptr, stream);
-  if (st != PA_OK || num_seqs == 0) return st;
-  return pa_decode_balanced_reduce(out, workspace, workspace_bytes, context_lens,
-                                   num_seqs, num_heads, num_kv_heads, head_size,
-                                   max_blocks_per_seq, block_size, grid, nullptr,
-                                   stream);
+  return balanced_impl(out, query, const_cast<void*>(key_cache),
+                       const_cast<void*>(value_cache), block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                       num_kv_heads, head_size, block_size, num_blocks, scale,
+                       grid, workspace, workspace_bytes, nullptr, nullptr,
+                       nullptr, stream);
 }
 
 pa_status pa_decode_step(void* out, const void* query, const void* key,
@@ -428,17 +380,12 @@ pa_status pa_decode_step(void* out, const void* query, const void* key,
                          int32_t num_blocks, float scale, int32_t grid,
                          void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
-  if (num_seqs > 0 && (!out || !key || !value)) return PA_ERR_NULL;
-  pa_status st = pa_decode_balanced_partials(
-      query, key_cache, value_cache, block_tables, max_blocks_per_seq,
-      context_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
-      num_blocks, scale, grid, workspace, workspace_bytes, key, value,
-      slot_mapping, stream);
-  if (st != PA_OK || num_seqs == 0) return st;
-  return pa_decode_balanced_reduce(out, workspace, workspace_bytes, context_lens,
-                                   num_seqs, num_heads, num_kv_heads, head_size,
-                                   max_blocks_per_seq, block_size, grid,
-                                   slot_mapping, stream);
+  if (num_seqs > 0 && (!key || !value)) return PA_ERR_NULL;
+  return balanced_impl(out, query, key_cache, value_cache, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                       num_kv_heads, head_size, block_size, num_blocks, scale,
+                       grid, workspace, workspace_bytes, key, value,
+                       slot_mapping, stream);
 }
 
 }  // extern "C"

@@ -24,8 +24,7 @@ struct DecodeArgs {
   int max_partitions;        // Pmax (split mode)
   int split;
   int num_seqs;              // balanced split
-  int64_t* bal_total;        // [1]  sum of padded lengths (per kv head)
-  int64_t* bal_prefix;       // [S]  exclusive prefix of padded lengths
+  int* bal_count;            // [S*H_kv] range counters, zero between calls
   // fused step (all null unless the kernel also appends this step's token):
   // the token at position context_len-1 is taken from new_key/new_value
   // ([S, H_kv, D]), stored into its slot, and its slot written to slot_out
@@ -35,20 +34,6 @@ struct DecodeArgs {
   float scale;
 };
 
-struct BalancedReduceArgs {
-  _Float16* out;
-  const float* ws_max;
-  const float* ws_sum;
-  const float* ws_out;
-  const int* context_lens;
-  const int64_t* total;
-  const int64_t* prefix;
-  int* slot_out;             // fused step: -1 for sequences with no token
-  int num_heads;
-  int num_kv_heads;
-  int grid;
-  int max_tokens;            // M * B
-};
 
 struct ReduceArgs {
   _Float16* out;
@@ -68,8 +53,6 @@ hipError_t launch_reduce(const ReduceArgs& a, int head_size, int num_seqs,
                          hipStream_t stream);
 hipError_t launch_balanced(const DecodeArgs& a, int head_size, int block_size,
                            int group, int grid, hipStream_t stream);
-hipError_t launch_balanced_reduce(const BalancedReduceArgs& a, int head_size,
-                                  int num_seqs, hipStream_t stream);
 // workgroups of the balanced kernel resident at once on the current device
 // (0 if it cannot be determined)
 int balanced_grid(int head_size, int block_size, int group);

@@ -16,9 +16,9 @@
 //                       pass) or one fixed partition (split-KV);
 //   balanced_kernel  -- a grid sized to the workgroups the chip holds at
 //                       once; each takes an equal slice of all the KV work
-//                       (possibly several ranges) and writes one partial
-//                       state per range;
-//   reduce_kernel / balanced_reduce_kernel -- merge partial states with the
+//                       (possibly several ranges); the last range of a split
+//                       pair to finish merges its partial states;
+//   reduce_kernel    -- merges the fixed partitions of split-KV with the
 //                       §4.6 recurrence.
 //
 // Common to both bodies: K/V rows are read with 16-byte buffer loads whose
@@ -560,11 +560,30 @@ __global__ __launch_bounds__(D) void reduce_kernel(ReduceArgs a) {
 // Flat work order: sequence-major, then kv head, then token, every sequence's
 // length padded to a multiple of 16 (padded_len).  With T the flat total and
 // C = ceil(T / grid) rounded up to 16, workgroup w owns flat positions
-// [w*C, (w+1)*C).  The part of pair q = seq*H_kv + kvh inside workgroup w is
-// one range; its state goes to slot w + q.  Along the flat order w and q
-// never decrease and at least one grows at every range boundary, so slots
-// are distinct and below grid + S*H_kv.  Pairs of one sequence are adjacent,
-// so neighbouring workgroups read neighbouring heads of the same token rows.
+// [w*C, (w+1)*C).  Pairs of one sequence are adjacent, so neighbouring
+// workgroups read neighbouring heads of the same token rows.
+//
+// The part of pair q = seq*H_kv + kvh inside workgroup w is one range.  A
+// pair whose valid tokens [F, F+n) (F = its flat start) fall in a single
+// slice is finished in place.  Otherwise each of its k ranges stores its
+// state in slot w + q (distinct: along the flat order w and q never decrease
+// and one grows at every range boundary, so slots stay below grid + S*H_kv),
+// then counts itself in cnt[q].  The range that brings the count to k folds
+// the k states with the online-softmax recurrence, writes the output and
+// resets cnt[q] to zero for the next call.  Nothing waits on another
+// workgroup.
+// Partial states cross XCDs (each has its own L2), so they are stored and
+// loaded with system-coherent accesses that bypass L2 (sc0 sc1) instead of
+// fencing whole caches; a writer waits for its stores to be acknowledged
+// before the range is counted with a system-scope atomic.
+__device__ __forceinline__ void publish(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float fetch(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 __device__ __forceinline__ int64_t padded_len(int n, int max_tok) {
   n = n < max_tok ? n : max_tok;
   return n <= 0 ? 0 : (int64_t)((n + 15) & ~15);
@@ -605,30 +624,36 @@ __global__ __launch_bounds__(256) void balanced_kernel(DecodeArgs a) {
   __shared__ int64_t wave_sum[kWaves];
   __shared__ int64_t found_start;
   __shared__ int found_seq;
+  __shared__ int merge_here;
   const int S = a.num_seqs;
+  const int H = a.num_heads;
   const int Hkv = a.num_kv_heads;
   const int max_tok = a.max_blocks_per_seq * B;
   const int w = blockIdx.x;
 
-  // Padded lengths, 256 sequences per pass: their per-kv-head prefix (kept by
-  // the first workgroup for the reduce), the total, and the sequence whose
-  // flat span holds this workgroup's first position.  One pass when S <= 256.
+  // Padded lengths, 256 sequences per pass: the total and the sequence whose
+  // flat span holds this workgroup's first position (one pass if S <= 256).
+  // The first workgroup also clears the outputs of empty sequences.
   if (threadIdx.x == 0) found_seq = -1;
   int64_t total_per_kvh = 0;
   int64_t my_len = 0, my_inc = 0;          // this thread's sequence (pass 0)
   for (int s0 = 0; s0 < S; s0 += 256) {
     const int si = s0 + (int)threadIdx.x;
-    const int64_t len = si < S ? padded_len(a.context_lens[si], max_tok) : 0;
+    const int ns = si < S ? a.context_lens[si] : 1;
+    const int64_t len = si < S ? padded_len(ns, max_tok) : 0;
+    if (w == 0 && ns <= 0) {
+      if (a.slot_out) a.slot_out[si] = -1;
+      u32x4* o = reinterpret_cast<u32x4*>(a.out + (size_t)si * H * D);
+      for (int k = 0; k < H * D / 8; ++k) o[k] = (u32x4){0u, 0u, 0u, 0u};
+    }
     int64_t chunk = 0;
     const int64_t inc = block_scan(len, wave_sum, chunk);
-    if (w == 0 && si < S) a.bal_prefix[si] = total_per_kvh + inc - len;
     if (s0 == 0) {
       my_len = len;
       my_inc = inc;
     }
     total_per_kvh += chunk;
   }
-  if (w == 0 && threadIdx.x == 0) a.bal_total[0] = total_per_kvh;
   const int64_t total = total_per_kvh * Hkv;
   const int64_t C = balanced_chunk(total, gridDim.x);
   const int64_t start = (int64_t)w * C;
@@ -678,17 +703,56 @@ __global__ __launch_bounds__(256) void balanced_kernel(DecodeArgs a) {
     const int tb = ta + (int)(seg_end - pos);
     const int tv = tb < n ? tb : n;
     if (ta < tv) {
-      const int64_t slot = (int64_t)w + (int64_t)s * Hkv + kvh;
-      auto sink = [&](int gi, int d, float mx, float L, float O) {
-        const size_t pi = (size_t)slot * G + gi;
-        if (d == 0) {
-          a.ws_max[pi] = mx * kLn2;
-          a.ws_sum[pi] = L;
-        }
-        a.ws_out[pi * D + d] = O;
-      };
+      const int64_t F = E + (int64_t)kvh * np;       // flat start of the pair
+      const int64_t w0 = F / C;
+      const int64_t wl = (F + n - 1) / C;             // slice of the last token
+      const int64_t q = (int64_t)s * Hkv + kvh;
       const int last = (a.new_key && tv == n) ? n - 1 : -1;
-      Path::run(a, sm, kvh, s, ta, tv, last, sink);
+      const size_t orow = ((size_t)s * H + (size_t)kvh * G) * D;
+      if (w0 == wl) {
+        auto sink = [&](int gi, int d, float, float L, float O) {
+          a.out[orow + (size_t)gi * D + d] = (_Float16)(O / L);
+        };
+        Path::run(a, sm, kvh, s, ta, tv, last, sink);
+      } else {
+        const int64_t slot = (int64_t)w + q;
+        auto sink = [&](int gi, int d, float mx, float L, float O) {
+          const size_t pi = (size_t)slot * G + gi;
+          if (d == 0) {
+            publish(a.ws_max + pi, mx * kLn2);
+            publish(a.ws_sum + pi, L);
+          }
+          publish(a.ws_out + pi * D + d, O);
+        };
+        Path::run(a, sm, kvh, s, ta, tv, last, sink);
+        // every thread's state stores acknowledged, then count this range
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0)
+          merge_here = __hip_atomic_fetch_add(a.bal_count + q, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_SYSTEM) ==
+                       (int)(wl - w0);
+        __syncthreads();
+        if (merge_here) {
+          for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+            const int gi = idx / D;
+            const int d = idx % D;
+            float mx = -INFINITY, L = 0.f, O = 0.f;
+            for (int64_t wr = w0; wr <= wl; ++wr) {
+              const size_t pi = (size_t)(wr + q) * G + gi;
+              const float mp = fetch(a.ws_max + pi);
+              const float mn = fmaxf(mx, mp);
+              const float fa = fast_exp2((mx - mn) * kLog2e);   // 0 at first
+              const float fb = fast_exp2((mp - mn) * kLog2e);
+              L = L * fa + fetch(a.ws_sum + pi) * fb;
+              O = O * fa + fetch(a.ws_out + pi * D + d) * fb;
+              mx = mn;
+            }
+            a.out[orow + idx] = (_Float16)(O / L);
+          }
+          if (threadIdx.x == 0) a.bal_count[q] = 0;    // ready for next call
+        }
+      }
     }
     pos = seg_end;
     if (pos == E + (int64_t)Hkv * np) {
@@ -696,52 +760,6 @@ __global__ __launch_bounds__(256) void balanced_kernel(DecodeArgs a) {
       ++s;
     }
   }
-}
-
-// Merge of the balanced ranges of one (query head, sequence): the ranges of
-// pair q are those of the workgroups whose flat slice meets [F, F + padded),
-// F = prefix*H_kv + kvh*padded; a range holding only padding tokens was
-// never written and is skipped (so are all later ones).
-template <int D>
-__global__ __launch_bounds__(D) void balanced_reduce_kernel(BalancedReduceArgs a) {
-  const int h = blockIdx.x;
-  const int seq = blockIdx.y;
-  const int d = threadIdx.x;
-  const int H = a.num_heads;
-  const int G = H / a.num_kv_heads;
-  const int kvh = h / G;
-  const int gi = h - kvh * G;
-  int n = a.context_lens[seq];
-  n = n < a.max_tokens ? n : a.max_tokens;
-  _Float16* o = a.out + ((size_t)seq * H + h) * D + d;
-  if (n <= 0) {
-    *o = (_Float16)0.f;
-    if (a.slot_out && h == 0 && d == 0) a.slot_out[seq] = -1;
-    return;
-  }
-  const int64_t np = (int64_t)((n + 15) & ~15);
-  const int64_t total = a.total[0] * a.num_kv_heads;
-  const int64_t C = balanced_chunk(total, a.grid);
-  const int64_t F = a.prefix[seq] * a.num_kv_heads + (int64_t)kvh * np;
-  const int64_t q = (int64_t)seq * a.num_kv_heads + kvh;
-  const int64_t w0 = F / C;
-  const int64_t w1 = (F + np - 1) / C;
-  float mx = -INFINITY;
-  for (int64_t w = w0; w <= w1; ++w) {
-    const int64_t lo = (w * C > F ? w * C : F) - F;
-    if (lo >= n) break;
-    mx = fmaxf(mx, a.ws_max[(size_t)(w + q) * G + gi]);
-  }
-  float S = 0.f, O = 0.f;
-  for (int64_t w = w0; w <= w1; ++w) {
-    const int64_t lo = (w * C > F ? w * C : F) - F;
-    if (lo >= n) break;
-    const size_t pi = (size_t)(w + q) * G + gi;
-    const float f = fast_exp2((a.ws_max[pi] - mx) * kLog2e);
-    S += a.ws_sum[pi] * f;
-    O += a.ws_out[pi * D + d] * f;
-  }
-  *o = (_Float16)(O / S);
 }
 
 // ---------------------------------------------------------------------------
@@ -848,20 +866,6 @@ hipError_t launch_reduce(const ReduceArgs& a, int head_size, int num_seqs,
       return hipGetLastError();
     case 128:
       hipLaunchKernelGGL(reduce_kernel<128>, grid, dim3(128), 0, stream, a);
-      return hipGetLastError();
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_balanced_reduce(const BalancedReduceArgs& a, int head_size,
-                                  int num_seqs, hipStream_t stream) {
-  dim3 grid(a.num_heads, num_seqs);
-  switch (head_size) {
-    case 64:
-      hipLaunchKernelGGL(balanced_reduce_kernel<64>, grid, dim3(64), 0, stream, a);
-      return hipGetLastError();
-    case 128:
-      hipLaunchKernelGGL(balanced_reduce_kernel<128>, grid, dim3(128), 0, stream, a);
       return hipGetLastError();
   }
   return hipErrorInvalidValue;

@@ -4,7 +4,7 @@ A step is: copy-on-write block copies (if any), the slot mapping of the new
 tokens, the cache write, then decode -- single-pass (``pa_decode``), split
 (``pa_decode_splitk`` + ``pa_decode_reduce``) or balanced
 (``pa_decode_balanced``); or, mode "fused", copies then ``pa_decode_step``
-(slot mapping, cache write and balanced decode in two kernels).  Inputs are plain arrays (a
+(slot mapping, cache write and balanced decode in one kernel).  Inputs are plain arrays (a
 workload object with the attributes used below); this module only uploads
 them and calls the binding, so every step runs in the library's kernels.
 """
@@ -113,7 +113,7 @@ def upload(w, device: str = "cuda", pool: Optional[torch.Tensor] = None) -> Devi
         copies=_dev_phase(w.step_copies, dev), write=_dev_phase(w.step_write, dev),
         workspace=torch.empty(max(ws, 16), dtype=torch.uint8, device=dev),
         grid=grid,
-        bal_workspace=torch.empty(max(bws, 16), dtype=torch.uint8, device=dev))
+        bal_workspace=torch.zeros(max(bws, 16), dtype=torch.uint8, device=dev))
 
 
 def apply_history(w, step: DeviceStep, stream=None) -> None:
@@ -133,6 +133,12 @@ def decode_step(step: DeviceStep, mode: str = "splitk", stream=None) -> None:
     if mode == "single":
         pa_decode(step.out, step.query, step.key_cache, step.value_cache,
                   step.block_tables, step.context_lens, step.scale, stream=stream)
+    elif mode == "fused_only":         # pa_decode_step without the COW copies
+        wr = step.write
+        pa_decode_step(step.out, step.query, wr.key, wr.value, step.key_cache,
+                       step.value_cache, step.block_tables, step.context_lens,
+                       step.scale, step.grid, step.bal_workspace,
+                       slot_mapping=wr.slots, stream=stream)
     elif mode == "balanced":
         pa_decode_balanced(step.out, step.query, step.key_cache, step.value_cache,
                            step.block_tables, step.context_lens, step.scale,
@@ -151,11 +157,7 @@ def decode_step(step: DeviceStep, mode: str = "splitk", stream=None) -> None:
 def fused_step(step: DeviceStep, stream=None) -> None:
     """COW copies (if any), then pa_decode_step: append + balanced decode."""
     run_phase(step.copies, step.pool, step.block_size, stream=stream)
-    wr = step.write
-    pa_decode_step(step.out, step.query, wr.key, wr.value, step.key_cache,
-                   step.value_cache, step.block_tables, step.context_lens,
-                   step.scale, step.grid, step.bal_workspace,
-                   slot_mapping=wr.slots, stream=stream)
+    decode_step(step, "fused_only", stream=stream)
 
 
 def full_step(step: DeviceStep, mode: str = "splitk", stream=None) -> None:

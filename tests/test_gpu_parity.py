@@ -281,10 +281,13 @@ def test_balanced_any_grid(name, grid):
     runner.write_step(st)
     nbytes = pa.pa_balanced_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads,
                                            w.head_size, grid)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    pa.pa_decode_balanced(st.out, st.query, st.key_cache, st.value_cache,
-                          st.block_tables, st.context_lens, st.scale, grid, ws)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for _ in range(2):        # the second call reuses the counters the first reset
+        pa.pa_decode_balanced(st.out, st.query, st.key_cache, st.value_cache,
+                              st.block_tables, st.context_lens, st.scale, grid, ws)
     torch.cuda.synchronize()
+    hdr = w.num_seqs * w.num_kv_heads
+    assert (ws[: hdr * 4].view(torch.int32) == 0).all(), "counters not reset"
     kc, vc = oracle_pool(w, oracle)
     ref = oracle.decode(w.query, kc, vc, w.block_tables, w.context_lens, w.scale)
     assert_attention_close(st.out.cpu().numpy(), ref, f"{name} grid {grid}")
