@@ -618,8 +618,17 @@ __device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* wave_sum,
   return v + before;
 }
 
+#ifndef PA_BAL_WPE
+#define PA_BAL_WPE 0
+#endif
+#if PA_BAL_WPE
+#define PA_BAL_ATTR __attribute__((amdgpu_waves_per_eu(PA_BAL_WPE)))
+#else
+#define PA_BAL_ATTR
+#endif
+
 template <class Path, int D, int B, int G>
-__global__ __launch_bounds__(256) void balanced_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) PA_BAL_ATTR void balanced_kernel(DecodeArgs a) {
   __shared__ typename Path::Smem sm;
   __shared__ int64_t wave_sum[kWaves];
   __shared__ int64_t found_start;
@@ -770,10 +779,22 @@ __global__ __launch_bounds__(256) void balanced_kernel(DecodeArgs a) {
 // vector-ALU body; measured on MI355X: 8 is best for groups of 1-2, 4 for a
 // group of 4 (fewer registers, one more wave per SIMD).  A group of 8 runs
 // on the matrix cores.
+#ifndef PA_VALU_NJ_G4
+#define PA_VALU_NJ_G4 2
+#endif
+#ifndef PA_MFMA_G4
+#define PA_MFMA_G4 0
+#endif
 template <int D, int B, int G>
 struct PathFor {
-  using type = ValuPath<D, B, G, (G >= 4 ? 4 : 8)>;
+  using type = ValuPath<D, B, G, (G >= 4 ? PA_VALU_NJ_G4 : 8)>;
 };
+#if PA_MFMA_G4
+template <int D, int B>
+struct PathFor<D, B, 4> {
+  using type = MfmaPath<D, B, 4>;
+};
+#endif
 template <int D, int B>
 struct PathFor<D, B, 8> {
   using type = MfmaPath<D, B, 8>;
