@@ -9,6 +9,7 @@ namespace pa {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -67,6 +68,11 @@ __device__ __forceinline__ float group_sum(float v) {
 // place (v.y, v.z, v.w) reads element x instead.
 __device__ __forceinline__ f16x2 as_h2(unsigned w) {
   return __builtin_bit_cast(f16x2, w);
+}
+
+// One 32-bit word as fp32 (the word must arrive as a scalar, as for as_h2)
+__device__ __forceinline__ float as_f32(unsigned w) {
+  return __builtin_bit_cast(float, w);
 }
 
 // Eight fp16 products of two 16-byte chunks accumulated in fp32

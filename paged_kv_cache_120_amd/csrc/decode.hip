@@ -35,7 +35,8 @@ namespace pa {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
 
 // Physical block ids of logical blocks [win, win + 64) of one sequence, one
 // per lane; entries at or past `end` are never read from the table.
@@ -141,6 +142,9 @@ struct ValuPath {
   static constexpr int LPR = D / 8;       // lanes per token row
   static constexpr int RPI = 64 / LPR;    // token rows per wave load
   static constexpr int TB = RPI * NJ;     // tokens per wave batch
+  // waves per SIMD the balanced kernel is register-limited to (1: no
+  // limit); groups of 1 and 4 fit in 128 VGPRs, 4 waves, without spilling
+  static constexpr int kMinWaves = (G == 1 || G == 4) ? 4 : 1;
   static_assert(B % RPI == 0, "a load must not straddle two blocks");
 
   struct Smem {
@@ -284,28 +288,31 @@ struct ValuPath {
 // Matrix-core range body (g = 8)
 // ---------------------------------------------------------------------------
 //
-// Per wave, a batch is MT tiles of 16 tokens.  With the 16x16x32 fp16 MFMA
-// (lane l holds A[l%16][8(l/16)+i], B[8(l/16)+i][l%16], D[4(l/16)+i][l%16]):
-//   S^T (16 tokens x 16 heads) = K (A: a 16-byte load of token l%16, channels
-//        32kk + 8(l/16)..) x Q^T (B: the group's query heads, zero past g),
-//        D/32 MFMAs per tile;
-//   O^T (16 channels x 16 heads) += V^T (A) x P^T (B), D/16 MFMAs per pair of
-//        tiles.
-// P^T needs no data movement: a lane's eight S^T values (4 tokens of each of
-// two tiles, one head) are exactly the eight reduction slots it supplies to
-// B, provided V^T's reduction slots use the same token order.  V^T is the
-// transposed V tile, so V goes through LDS: each lane stores its 16-byte
-// rows, then gathers its column with 2-byte reads; rows are padded by 8 bytes
-// so the four lane groups of a read hit disjoint banks.  Every per-head
-// quantity (running max, sum, rescale factor) lives in the lanes owning that
-// head's column, and O^T's rows are channels, so the rescale is lane-local.
+// Per wave, a batch is MT tiles of 16 tokens (one at D = 128, which keeps
+// the kernel within 128 VGPRs: four waves per SIMD).  Two MFMA shapes:
+//   S^T (16 tokens x 16 heads) = K x Q^T with the 16x16x32 fp16 MFMA (lane l
+//        holds A[l%16][8(l/16)+i], B[8(l/16)+i][l%16], D[4(l/16)+i][l%16]):
+//        A is a 16-byte load of token l%16, channels 32kk + 8(l/16)..; B is
+//        the group's query heads (zero past g); D/32 MFMAs per tile;
+//   O^T (16 channels x 16 heads) += V^T x P^T with the 16x16x16 fp16 MFMA
+//        (lane l holds A[l%16][4(l/16)+i], B[4(l/16)+i][l%16]), D/16 MFMAs
+//        per tile.
+// P^T needs no data movement: the four S^T values a lane holds (tokens
+// 4(l/16)+i of head l%16) are exactly its B slots.  V^T is the transposed V
+// tile, so V goes through LDS: each lane stores its 16-byte rows, then
+// gathers its column (4 tokens of one channel) with 2-byte reads; rows are
+// padded by 8 bytes so the four lane groups of a read hit disjoint banks.
+// Every per-head quantity (running max, sum, rescale factor) lives in the
+// lanes owning that head's column, and O^T's rows are channels, so the
+// rescale is lane-local.
 template <int D, int B, int G>
 struct MfmaPath {
-  static constexpr int MT = D == 128 ? 2 : 4;   // 16-token tiles per batch
+  static constexpr int MT = D == 128 ? 1 : 2;   // 16-token tiles per batch
   static constexpr int TB = 16 * MT;
   static constexpr int KK = D / 32;             // MFMA k-steps over channels
   static constexpr int DT = D / 16;             // channel tiles of O^T
   static constexpr int VS = D + 4;              // padded LDS row (halves)
+  static constexpr int kMinWaves = 4;           // 128 VGPRs: 4 waves per SIMD
   static_assert(B % 16 == 0, "a tile must not straddle two blocks");
   static_assert(G <= 16, "one MFMA column per query head");
 
@@ -439,26 +446,19 @@ struct MfmaPath {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
 
-      // O^T += V^T P^T, one k-step of 32 tokens per pair of tiles
+      // O^T += V^T P^T, one k-step of 16 tokens per tile
 #pragma unroll
-      for (int pr = 0; pr < MT / 2; ++pr) {
-        f16x8 pb;
+      for (int mt = 0; mt < MT; ++mt) {
+        f16x4 pb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[i] = (_Float16)sc[2 * pr][i];
-          pb[4 + i] = (_Float16)sc[2 * pr + 1][i];
-        }
-        const _Float16* vrow0 = vw + (pr * 32 + grp * 4) * VS + col;
-        const _Float16* vrow1 = vrow0 + 16 * VS;
+        for (int i = 0; i < 4; ++i) pb[i] = (_Float16)sc[mt][i];
+        const _Float16* vrow = vw + (mt * 16 + grp * 4) * VS + col;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          f16x8 va;
+          f16x4 va;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            va[i] = vrow0[i * VS + dt * 16];
-            va[4 + i] = vrow1[i * VS + dt * 16];
-          }
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o[dt], 0, 0, 0);
+          for (int i = 0; i < 4; ++i) va[i] = vrow[i * VS + dt * 16];
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, o[dt], 0, 0, 0);
         }
       }
     }
@@ -490,7 +490,7 @@ struct MfmaPath {
 // sequence, so every XCD gets a share of each partition index; partition 0
 // of every sequence is dispatched first, later (possibly empty) ones last.
 template <class Path, int D, int B, int G>
-__global__ __launch_bounds__(256) void partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void partition_kernel(DecodeArgs a) {
   __shared__ typename Path::Smem sm;
   const int kvh = blockIdx.x;
   const int seq = blockIdx.y;
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(256) void partition_kernel(DecodeArgs a) {
   const int t0 = p * a.partition_size;
   if (n <= 0 || t0 >= n) {
     if (!a.split && p == 0) {
-      for (int idx = threadIdx.x; idx < G * D; idx += 256)
+      for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
         a.out[((size_t)seq * H + (size_t)kvh * G) * D + idx] = (_Float16)0.f;
     }
     return;
@@ -584,6 +584,9 @@ __device__ __forceinline__ float fetch(const float* p) {
                            __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// partial states a merging range loads before folding them
+constexpr int kMergeBatch = 8;
+
 __device__ __forceinline__ int64_t padded_len(int n, int max_tok) {
   n = n < max_tok ? n : max_tok;
   return n <= 0 ? 0 : (int64_t)((n + 15) & ~15);
@@ -618,17 +621,11 @@ __device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* wave_sum,
   return v + before;
 }
 
-#ifndef PA_BAL_WPE
-#define PA_BAL_WPE 0
-#endif
-#if PA_BAL_WPE
-#define PA_BAL_ATTR __attribute__((amdgpu_waves_per_eu(PA_BAL_WPE)))
-#else
-#define PA_BAL_ATTR
-#endif
 
 template <class Path, int D, int B, int G>
-__global__ __launch_bounds__(256) PA_BAL_ATTR void balanced_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(Path::kMinWaves))) void balanced_kernel(
+    DecodeArgs a) {
   __shared__ typename Path::Smem sm;
   __shared__ int64_t wave_sum[kWaves];
   __shared__ int64_t found_start;
@@ -646,7 +643,7 @@ __global__ __launch_bounds__(256) PA_BAL_ATTR void balanced_kernel(DecodeArgs a)
   if (threadIdx.x == 0) found_seq = -1;
   int64_t total_per_kvh = 0;
   int64_t my_len = 0, my_inc = 0;          // this thread's sequence (pass 0)
-  for (int s0 = 0; s0 < S; s0 += 256) {
+  for (int s0 = 0; s0 < S; s0 += kThreads) {
     const int si = s0 + (int)threadIdx.x;
     const int ns = si < S ? a.context_lens[si] : 1;
     const int64_t len = si < S ? padded_len(ns, max_tok) : 0;
@@ -669,7 +666,7 @@ __global__ __launch_bounds__(256) PA_BAL_ATTR void balanced_kernel(DecodeArgs a)
   if (total == 0 || start >= total) return;
   const int64_t end = start + C < total ? start + C : total;
 
-  if (S <= 256) {
+  if (S <= kThreads) {
     // flat span of sequence si: [(inc - len) * H_kv, inc * H_kv)
     if (my_len > 0 && (my_inc - my_len) * Hkv <= start && start < my_inc * Hkv) {
       found_seq = (int)threadIdx.x;
@@ -678,7 +675,7 @@ __global__ __launch_bounds__(256) PA_BAL_ATTR void balanced_kernel(DecodeArgs a)
     __syncthreads();
   } else {
     int64_t run = 0;
-    for (int s0 = 0; s0 < S; s0 += 256) {
+    for (int s0 = 0; s0 < S; s0 += kThreads) {
       const int si = s0 + (int)threadIdx.x;
       const int64_t len = si < S ? padded_len(a.context_lens[si], max_tok) * Hkv : 0;
       int64_t chunk = 0;
@@ -743,18 +740,36 @@ __global__ __launch_bounds__(256) PA_BAL_ATTR void balanced_kernel(DecodeArgs a)
                        (int)(wl - w0);
         __syncthreads();
         if (merge_here) {
-          for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+          for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
             const int gi = idx / D;
             const int d = idx % D;
             float mx = -INFINITY, L = 0.f, O = 0.f;
-            for (int64_t wr = w0; wr <= wl; ++wr) {
-              const size_t pi = (size_t)(wr + q) * G + gi;
-              const float mp = fetch(a.ws_max + pi);
-              const float mn = fmaxf(mx, mp);
+            // kMergeBatch ranges' states in flight at once, then folded
+            for (int64_t w1 = w0; w1 <= wl; w1 += kMergeBatch) {
+              float mp[kMergeBatch], lp[kMergeBatch], op[kMergeBatch];
+#pragma unroll
+              for (int k = 0; k < kMergeBatch; ++k) {
+                const int64_t wr = w1 + k <= wl ? w1 + k : wl;
+                const size_t pi = (size_t)(wr + q) * G + gi;
+                mp[k] = fetch(a.ws_max + pi);
+                lp[k] = fetch(a.ws_sum + pi);
+                op[k] = fetch(a.ws_out + pi * D + d);
+              }
+              float mn = mx;
+#pragma unroll
+              for (int k = 0; k < kMergeBatch; ++k) {
+                if (w1 + k > wl) mp[k] = -INFINITY;      // past the last range
+                mn = fmaxf(mn, mp[k]);
+              }
               const float fa = fast_exp2((mx - mn) * kLog2e);   // 0 at first
-              const float fb = fast_exp2((mp - mn) * kLog2e);
-              L = L * fa + fetch(a.ws_sum + pi) * fb;
-              O = O * fa + fetch(a.ws_out + pi * D + d) * fb;
+              L *= fa;
+              O *= fa;
+#pragma unroll
+              for (int k = 0; k < kMergeBatch; ++k) {
+                const float fb = fast_exp2((mp[k] - mn) * kLog2e);
+                L += lp[k] * fb;
+                O += op[k] * fb;
+              }
               mx = mn;
             }
             a.out[orow + idx] = (_Float16)(O / L);
@@ -776,25 +791,14 @@ __global__ __launch_bounds__(256) PA_BAL_ATTR void balanced_kernel(DecodeArgs a)
 // ---------------------------------------------------------------------------
 
 // Loads in flight per wave batch (16-byte K and V loads per lane) for the
-// vector-ALU body; measured on MI355X: 8 is best for groups of 1-2, 4 for a
-// group of 4 (fewer registers, one more wave per SIMD).  A group of 8 runs
-// on the matrix cores.
-#ifndef PA_VALU_NJ_G4
-#define PA_VALU_NJ_G4 2
-#endif
-#ifndef PA_MFMA_G4
-#define PA_MFMA_G4 0
-#endif
+// vector-ALU body; measured on MI355X: 8 is best for groups of 1-2, 2 for a
+// group of 4 (fewer registers, four waves per SIMD).  A group of 8 runs on
+// the matrix cores; for a group of 4 the matrix-core body measured slower
+// than the vector one (3.7-3.9 vs 4.0-4.3 TB/s on the GQA-4 workload).
 template <int D, int B, int G>
 struct PathFor {
-  using type = ValuPath<D, B, G, (G >= 4 ? PA_VALU_NJ_G4 : 8)>;
+  using type = ValuPath<D, B, G, (G >= 4 ? 2 : 8)>;
 };
-#if PA_MFMA_G4
-template <int D, int B>
-struct PathFor<D, B, 4> {
-  using type = MfmaPath<D, B, 4>;
-};
-#endif
 template <int D, int B>
 struct PathFor<D, B, 8> {
   using type = MfmaPath<D, B, 8>;
@@ -808,14 +812,14 @@ static hipError_t run_op(Op op, const DecodeArgs* a, dim3 grid,
   using P = typename PathFor<D, B, G>::type;
   switch (op) {
     case Op::kPartition:
-      hipLaunchKernelGGL((partition_kernel<P, D, B, G>), grid, dim3(256), 0, st, *a);
+      hipLaunchKernelGGL((partition_kernel<P, D, B, G>), grid, dim3(kThreads), 0, st, *a);
       return hipGetLastError();
     case Op::kBalanced:
-      hipLaunchKernelGGL((balanced_kernel<P, D, B, G>), grid, dim3(256), 0, st, *a);
+      hipLaunchKernelGGL((balanced_kernel<P, D, B, G>), grid, dim3(kThreads), 0, st, *a);
       return hipGetLastError();
     case Op::kOccupancy:
       return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          occ, reinterpret_cast<const void*>(&balanced_kernel<P, D, B, G>), 256, 0);
+          occ, reinterpret_cast<const void*>(&balanced_kernel<P, D, B, G>), kThreads, 0);
   }
   return hipErrorInvalidValue;
 }
