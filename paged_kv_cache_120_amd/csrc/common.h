@@ -92,6 +92,13 @@ __device__ __forceinline__ float half_at(u32x4 v, int e) {
   return (float)as_h2(w)[e & 1];
 }
 
+// v_readlane of an fp32 value (the builtin takes and returns int, so the
+// bits are moved, not converted)
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);   // v_exp_f32; exp2(-inf) = 0
 }

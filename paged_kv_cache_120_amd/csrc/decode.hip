@@ -35,6 +35,12 @@ namespace pa {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Online softmax with a lazy reference (base-2 units): scores are
+// exponentiated against a reference that moves only when a batch max
+// exceeds it by more than kSlack, so weights stay <= 2^kSlack and the
+// rescale of the accumulators is skipped for almost every batch; the state
+// is brought to the true max once, at the end of a range.
+constexpr float kSlack = 8.f;
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 
@@ -181,18 +187,20 @@ struct ValuPath {
     const char* vbase = a.value_cache + (size_t)kvh * D * 2;
     const float sl2 = a.scale * kLog2e;
 
-    float m[G], l[G], acc[G][8];
+    // m: the reference the state is kept relative to; mt: the true max
+    float m[G], mt[G], l[G], acc[G][8];
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
       m[gi] = -INFINITY;
+      mt[gi] = -INFINITY;
       l[gi] = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[gi][e] = 0.f;
     }
 
-    for (int base = t0 + wave * TB; base < t1; base += kWaves * TB) {
+    // loads of one batch into (kk, vv), including the appended token's row
+    auto issue = [&](int base, u32x4 (&kk)[NJ], u32x4 (&vv)[NJ]) {
       bw.cover(base / B, (base + TB - 1) / B, lane);
-      u32x4 kk[NJ], vv[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int tok0 = base + j * RPI;   // wave-uniform
@@ -214,6 +222,9 @@ struct ValuPath {
           }
         }
       }
+    };
+    // scores, softmax state and P.V of one loaded batch
+    auto consume = [&](int base, const u32x4 (&kk)[NJ], const u32x4 (&vv)[NJ]) {
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
         float s[NJ];
@@ -225,26 +236,48 @@ struct ValuPath {
           s[j] = tok < t1 ? d * sl2 : -INFINITY;
           bm = fmaxf(bm, s[j]);
         }
-        const float mn = fmaxf(m[gi], bm);
-        const float sh = mn == -INFINITY ? 0.f : mn;
-        const float al = fast_exp2(m[gi] - sh);
+        // the reference moves (and the state is rescaled) only when a
+        // batch max exceeds it by more than kSlack
+        mt[gi] = fmaxf(mt[gi], bm);
+        if (__builtin_amdgcn_ballot_w64(bm > m[gi] + kSlack)) {
+          const float mn = fmaxf(m[gi], mt[gi]);
+          const float al = fast_exp2(m[gi] - (mn == -INFINITY ? 0.f : mn));
+          l[gi] *= al;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[gi][e] *= al;
+          m[gi] = mn;
+        }
+        const float sh = m[gi] == -INFINITY ? 0.f : m[gi];
         float ps = 0.f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           s[j] = fast_exp2(s[j] - sh);
           ps += s[j];
         }
-        l[gi] = l[gi] * al + ps;
-        m[gi] = mn;
+        l[gi] += ps;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float x = acc[gi][e] * al;
+          float x = acc[gi][e];
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
             x = __builtin_fmaf(s[j], half_at(vv[j], e), x);
           acc[gi][e] = x;
         }
       }
+    };
+    for (int base = t0 + wave * TB; base < t1; base += kWaves * TB) {
+      u32x4 kk[NJ], vv[NJ];
+      issue(base, kk, vv);
+      consume(base, kk, vv);
+    }
+    // state relative to the true running max from here on
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const float f = mt[gi] == -INFINITY ? 1.f : fast_exp2(m[gi] - mt[gi]);
+      l[gi] *= f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[gi][e] *= f;
+      m[gi] = mt[gi];
     }
 
     // merge the row groups of the wave (lanes sharing channel chunk c)
@@ -354,7 +387,8 @@ struct MfmaPath {
     const char* vbase = a.value_cache + (size_t)kvh * D * 2;
     const float sl2 = a.scale * kLog2e;
 
-    float m = -INFINITY;                        // running max of head `col`
+    float m = -INFINITY;                        // reference of head `col`
+    float mt = -INFINITY;                       // its true running max
     float l = 0.f;                              // this lane's share of the sum
     f32x4 o[DT];
 #pragma unroll
@@ -430,21 +464,25 @@ struct MfmaPath {
         for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[mt][i]);
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float mn = fmaxf(m, bm);
-      const float sh = mn == -INFINITY ? 0.f : mn;
-      const float al = fast_exp2(m - sh);
-      m = mn;
-      float ps = 0.f;
+      // lazy reference: rescale only when the batch max exceeds it by more
+      // than kSlack (weights stay <= 2^kSlack, well inside fp16)
+      mt = fmaxf(mt, bm);
+      if (__builtin_amdgcn_ballot_w64(bm > m + kSlack)) {
+        const float mn = fmaxf(m, mt);
+        const float al = fast_exp2(m - (mn == -INFINITY ? 0.f : mn));
+        l *= al;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
+        m = mn;
+      }
+      const float sh = m == -INFINITY ? 0.f : m;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           sc[mt][i] = fast_exp2(sc[mt][i] - sh);
-          ps += sc[mt][i];
+          l += sc[mt][i];
         }
-      l = l * al + ps;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
 
       // O^T += V^T P^T, one k-step of 16 tokens per tile
 #pragma unroll
@@ -463,7 +501,15 @@ struct MfmaPath {
       }
     }
 
-    // the sum over the 4 lane groups; then merge the waves through LDS
+    // state relative to the true max; the sum over the 4 lane groups; then
+    // merge the waves through LDS
+    {
+      const float f = mt == -INFINITY ? 1.f : fast_exp2(m - mt);
+      l *= f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= f;
+      m = mt;
+    }
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (col < G) {
