@@ -198,6 +198,72 @@ def load_traffic(args, root: str):
         return None
 
 
+HOST_LINK_PEAK_GBS = 64.0     # PCIe 5.0 x16, one direction (nominal)
+
+
+def swap_bench(args, w, dev) -> int:
+    """Swap (pa_swap_blocks) of every block the batch's tables reference:
+    device pool -> pinned host pool, then back into the device pool, each
+    timed over --steps launches with HIP events on the launch stream.  The
+    last swap-in is checked bit-exact against the device pool it came from."""
+    import torch
+    import paged_kv_cache_120_amd as pa
+    from paged_kv_cache_120_amd import runner
+    st = runner.upload(w, dev)
+    runner.apply_history(w, st)
+    torch.cuda.synchronize()
+    B = w.block_size
+    used = sorted({int(b) for i, n in enumerate(w.context_lens)
+                   for b in w.block_tables[i, :(int(n) + B - 1) // B]})
+    nu = len(used)
+    blk = B * w.num_kv_heads * w.head_size * 2                  # bytes per block half
+    host = torch.empty((2, nu) + tuple(st.pool.shape[2:]), dtype=torch.float16,
+                       pin_memory=True)
+    back = torch.empty_like(st.pool)
+    dev_ids = torch.tensor(used, dtype=torch.int32, device=dev)
+    host_ids = torch.arange(nu, dtype=torch.int32, device=dev)
+
+    def timed(fn):
+        for _ in range(min(args.warmup, 3)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_out = timed(lambda: pa.pa_swap_blocks(st.pool[0], st.pool[1], host[0], host[1],
+                                             dev_ids, host_ids))
+    ms_in = timed(lambda: pa.pa_swap_blocks(host[0], host[1], back[0], back[1],
+                                            host_ids, dev_ids))
+    idx = dev_ids.long()
+    exact = torch.equal(back[:, idx].view(torch.int16), st.pool[:, idx].view(torch.int16))
+    nbytes = 2 * nu * blk
+    gbs_out = nbytes / (ms_out * 1e-3) / 1e9
+    gbs_in = nbytes / (ms_in * 1e-3) / 1e9
+    rec = {
+        "metric": "paged KV block swap GB/s (device <-> pinned host)",
+        "value": round(2 * nbytes / ((ms_out + ms_in) * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_out + ms_in, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "name": args.config,
+                   "blocks": nu, "bytes_each_way": nbytes},
+        "swap_out_gbs": round(gbs_out, 2), "swap_in_gbs": round(gbs_in, 2),
+        "swap_out_ms": round(ms_out, 4), "swap_in_ms": round(ms_in, 4),
+        "round_trip_bit_exact": exact,
+        "roofline": {"bound": "host-link", "achieved": round(max(gbs_out, gbs_in), 2),
+                     "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(max(gbs_out, gbs_in) / HOST_LINK_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "swap_blocks_kernel"},
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,9 +271,11 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="fused",
-                    choices=["fused", "balanced", "splitk", "single"],
-                    help="fused: pa_decode_step (append + balanced decode, 2 kernels); "
-                         "balanced/splitk/single: slot mapping + cache write + that decode")
+                    choices=["fused", "balanced", "splitk", "single", "swap"],
+                    help="fused: pa_decode_step (append + balanced decode, one kernel); "
+                         "balanced/splitk/single: slot mapping + cache write + that decode; "
+                         "swap: pa_swap_blocks of the batch's blocks to pinned host memory "
+                         "and back (its own JSON line)")
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--partition", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -230,6 +298,8 @@ def main(argv=None) -> int:
     w.partition_size = args.partition
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.mode == "swap":
+        return swap_bench(args, w, dev)
 
     steps = []
     base = runner.upload(w, dev)

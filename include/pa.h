@@ -110,6 +110,33 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache,
                          int32_t head_size, hipStream_t stream);
 
 /*
+ * pa_swap_blocks -- batched block moves between two pools ([P5] §4.4: the
+ * physical blocks of a paused request are moved out to CPU memory to free
+ * device memory, and back before it resumes).  For each pair k, physical
+ * block src_ids[k] of (src_key_cache, src_value_cache) is copied
+ * bit-exactly to block dst_ids[k] of (dst_key_cache, dst_value_cache).
+ *   Pools       fp16 [num_blocks, block_size, num_kv_heads, head_size] each
+ *               (the two halves of a (2, nb, ...) pool); either pool may be
+ *               device memory or pinned host memory mapped for the device
+ *               (hipHostMalloc / torch pin_memory), so one call swaps out
+ *               (device -> host) or in (host -> device).
+ *   src_ids, dst_ids  int32 [num_pairs], device-accessible; a pair with an
+ *               id outside [0, src_num_blocks) or [0, dst_num_blocks) is
+ *               skipped.
+ *   One kernel on `stream` moves all pairs; the host must not touch the
+ *   host pool until the stream has passed the call.
+ *   Precondition: the dst blocks are distinct and do not overlap the src
+ *   blocks being read.
+ */
+pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
+                         int32_t src_num_blocks, void* dst_key_cache,
+                         void* dst_value_cache, int32_t dst_num_blocks,
+                         const int32_t* src_ids, const int32_t* dst_ids,
+                         int32_t num_pairs, int32_t block_size,
+                         int32_t num_kv_heads, int32_t head_size,
+                         hipStream_t stream);
+
+/*
  * pa_decode -- single-pass paged decode attention ([BOOK] §4.5, §4.6).
  *   For sequence i and query head h (kv head h / (num_heads/num_kv_heads)):
  *     out[i,h,:] = sum_t softmax_t(scale * <query[i,h,:], K_t>) * V_t

@@ -31,7 +31,7 @@ import numpy as np
 __all__ = [
     "kv_cache_shape", "kv_bytes_per_token", "block_bytes", "blocks_needed",
     "slots_reserved", "padding_slots", "slot_mapping", "cache_write",
-    "copy_blocks", "apply_phases", "gather_kv", "decode", "decode_heads",
+    "copy_blocks", "swap_blocks", "apply_phases", "gather_kv", "decode", "decode_heads",
     "partials", "merge",
 ]
 
@@ -127,6 +127,23 @@ def copy_blocks(key_cache: np.ndarray, value_cache: np.ndarray, src, dst) -> Non
     for a, b in zip(src, dst):
         kc[int(b)] = kc[int(a)]
         vc[int(b)] = vc[int(a)]
+
+
+def swap_blocks(src_key_cache: np.ndarray, src_value_cache: np.ndarray,
+                dst_key_cache: np.ndarray, dst_value_cache: np.ndarray,
+                src_ids, dst_ids) -> None:
+    """Block swap between two pools ([P5] §4.4: the physical blocks of a
+    paused request move out to CPU memory and back): block src_ids[k] of the
+    source pool (K and V) becomes block dst_ids[k] of the destination pool.
+    Pairs with an id outside either pool are skipped."""
+    sk, sv = src_key_cache.view(np.uint16), src_value_cache.view(np.uint16)
+    dk, dv = dst_key_cache.view(np.uint16), dst_value_cache.view(np.uint16)
+    for a, b in zip(src_ids, dst_ids):
+        a, b = int(a), int(b)
+        if not (0 <= a < sk.shape[0] and 0 <= b < dk.shape[0]):
+            continue
+        dk[b] = sk[a]
+        dv[b] = sv[a]
 
 
 def apply_phases(key_cache: np.ndarray, value_cache: np.ndarray, phases,

@@ -16,7 +16,7 @@ from typing import Optional, Tuple
 
 __all__ = [
     "PaError", "lib", "library_path", "pa_status_str", "pa_kv_cache_shape",
-    "pa_slot_mapping", "pa_cache_write", "pa_copy_blocks", "pa_decode",
+    "pa_slot_mapping", "pa_cache_write", "pa_copy_blocks", "pa_swap_blocks", "pa_decode",
     "pa_splitk_workspace_size", "pa_decode_splitk", "pa_decode_reduce",
     "pa_balanced_grid", "pa_balanced_workspace_size", "pa_decode_balanced",
     "pa_decode_step", "STATUS",
@@ -51,6 +51,8 @@ def _load() -> ctypes.CDLL:
         "pa_slot_mapping": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, i32, i32, vp]),
         "pa_cache_write": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]),
         "pa_copy_blocks": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]),
+        "pa_swap_blocks": (ctypes.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32,
+                                          i32, vp]),
         "pa_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
                                      i32, i32, f32, vp]),
         "pa_splitk_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
@@ -151,6 +153,23 @@ def _dev(t, dtype, name: str, ndim: Optional[int] = None) -> int:
     return t.data_ptr()
 
 
+def _mapped(t, dtype, name: str, ndim: Optional[int] = None) -> int:
+    """A device tensor, or a pinned host tensor (its memory is mapped for the
+    device at the same address on ROCm)."""
+    torch = _torch()
+    if isinstance(t, torch.Tensor) and t.device.type == "cpu":
+        if not t.is_pinned():
+            raise ValueError(f"{name}: a host tensor must be pinned (pin_memory=True)")
+        if t.dtype != dtype:
+            raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+        if ndim is not None and t.dim() != ndim:
+            raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+        return t.data_ptr()
+    return _dev(t, dtype, name, ndim)
+
+
 def _check(func: str, status: int) -> None:
     if status != 0:
         raise PaError(func, status)
@@ -198,6 +217,28 @@ def pa_copy_blocks(key_cache, value_cache, src, dst, stream=None) -> None:
         _dev(value_cache, torch.float16, "value_cache", 4),
         _dev(src, torch.int32, "src", 1), _dev(dst, torch.int32, "dst", 1),
         src.numel(), nb, B, Hkv, D, _stream(stream)))
+
+
+def pa_swap_blocks(src_key_cache, src_value_cache, dst_key_cache, dst_value_cache,
+                   src_ids, dst_ids, stream=None) -> None:
+    """Block src_ids[k] of the source pool to block dst_ids[k] of the
+    destination pool (either pool on the device or in pinned host memory)."""
+    torch = _torch()
+    snb, B, Hkv, D = src_key_cache.shape
+    dnb = dst_key_cache.shape[0]
+    if tuple(dst_key_cache.shape[1:]) != (B, Hkv, D) or \
+            src_value_cache.shape != src_key_cache.shape or \
+            dst_value_cache.shape != dst_key_cache.shape:
+        raise ValueError("pa_swap_blocks: pool block shapes differ")
+    if src_ids.shape != dst_ids.shape:
+        raise ValueError("pa_swap_blocks: src_ids/dst_ids shapes differ")
+    _check("pa_swap_blocks", _lib().pa_swap_blocks(
+        _mapped(src_key_cache, torch.float16, "src_key_cache", 4),
+        _mapped(src_value_cache, torch.float16, "src_value_cache", 4), snb,
+        _mapped(dst_key_cache, torch.float16, "dst_key_cache", 4),
+        _mapped(dst_value_cache, torch.float16, "dst_value_cache", 4), dnb,
+        _dev(src_ids, torch.int32, "src_ids", 1), _dev(dst_ids, torch.int32, "dst_ids", 1),
+        src_ids.numel(), B, Hkv, D, _stream(stream)))
 
 
 def _decode_common(query, key_cache, value_cache, block_tables, context_lens):

@@ -142,6 +142,31 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache,
                                            num_pairs, num_blocks, cpb, stream));
 }
 
+pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
+                         int32_t src_num_blocks, void* dst_key_cache,
+                         void* dst_value_cache, int32_t dst_num_blocks,
+                         const int32_t* src_ids, const int32_t* dst_ids,
+                         int32_t num_pairs, int32_t block_size,
+                         int32_t num_kv_heads, int32_t head_size,
+                         hipStream_t stream) {
+  if (num_pairs < 0 || src_num_blocks <= 0 || dst_num_blocks <= 0 ||
+      block_size <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+      head_size % 8 != 0)
+    return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_key_cache || !src_value_cache || !dst_key_cache ||
+      !dst_value_cache || !src_ids || !dst_ids)
+    return PA_ERR_NULL;
+  if (!aligned(src_key_cache, 16) || !aligned(src_value_cache, 16) ||
+      !aligned(dst_key_cache, 16) || !aligned(dst_value_cache, 16) ||
+      !aligned(src_ids, 4) || !aligned(dst_ids, 4))
+    return PA_ERR_ALIGN;
+  const int64_t cpb = (int64_t)block_size * num_kv_heads * head_size / 8;
+  return hip_status(pa::launch_swap_blocks(
+      src_key_cache, src_value_cache, src_num_blocks, dst_key_cache,
+      dst_value_cache, dst_num_blocks, src_ids, dst_ids, num_pairs, cpb, stream));
+}
+
 pa_status pa_decode(void* out, const void* query, const void* key_cache,
                     const void* value_cache, const int32_t* block_tables,
                     int32_t max_blocks_per_seq, const int32_t* context_lens,

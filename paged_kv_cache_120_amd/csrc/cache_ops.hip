@@ -1,10 +1,11 @@
 // Write side of the paged KV cache for gfx950: slot mapping, the per-token
-// cache write and copy-on-write block copies.
+// cache write, copy-on-write block copies and block swaps between pools.
 //
 // vLLM book ch.4 "PagedAttention：虚拟内存的启示" §4.4.3 (slot_mapping) and
 // §4.3.2 / §4.5 (1) (reshape_and_cache: write each new token's K/V rows to
 // its slot); "PagedAttention：KV Cache的虚拟内存" copy-on-write paragraph and
-// "PagedAttention原理（下）" §4.3 (copy the shared block, then repoint).
+// "PagedAttention原理（下）" §4.3 (copy the shared block, then repoint) and
+// §4.4 (move the blocks of a paused request out to CPU memory and back).
 //
 // All three move whole 16-byte chunks; consecutive lanes touch consecutive
 // chunks of a token row (cache write) or of a block (copy), so every wave
@@ -65,6 +66,29 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
   }
 }
 
+// Block moves between two pools (device memory or pinned host memory the
+// device maps): block src[k] of (sk, sv) to block dst[k] of (dk, dv).  Each
+// workgroup row streams one pair; with host memory on either side the moves
+// go over the host link, 1 KiB per wave instruction.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    const u32x4* __restrict__ sk, const u32x4* __restrict__ sv, int snb,
+    u32x4* __restrict__ dk, u32x4* __restrict__ dv, int dnb,
+    const int* __restrict__ src, const int* __restrict__ dst, int pairs,
+    long long cpb) {
+  for (int k = blockIdx.y; k < pairs; k += gridDim.y) {
+    const int a = src[k];
+    const int b = dst[k];
+    if ((unsigned)a >= (unsigned)snb || (unsigned)b >= (unsigned)dnb) continue;
+    const size_t sa = (size_t)a * cpb;
+    const size_t sb = (size_t)b * cpb;
+    for (long long cc = (long long)blockIdx.x * 256 + threadIdx.x; cc < cpb;
+         cc += (long long)gridDim.x * 256) {
+      dk[sb + cc] = sk[sa + cc];
+      dv[sb + cc] = sv[sa + cc];
+    }
+  }
+}
+
 static int clamp_grid(long long want, int cap) {
   if (want < 1) return 1;
   return want > cap ? cap : (int)want;
@@ -96,6 +120,16 @@ hipError_t launch_copy_blocks(void* kc, void* vc, const int* src,
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream,
                      (u32x4*)kc, (u32x4*)vc, src, dst, pairs, nb,
                      (long long)cpb);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(const void* sk, const void* sv, int snb, void* dk,
+                              void* dv, int dnb, const int* src, const int* dst,
+                              int pairs, int64_t cpb, hipStream_t stream) {
+  dim3 grid(clamp_grid((cpb + 255) / 256, 64), clamp_grid(pairs, 65535));
+  hipLaunchKernelGGL(swap_blocks_kernel, grid, dim3(256), 0, stream,
+                     (const u32x4*)sk, (const u32x4*)sv, snb, (u32x4*)dk,
+                     (u32x4*)dv, dnb, src, dst, pairs, (long long)cpb);
   return hipGetLastError();
 }
 

@@ -68,5 +68,9 @@ hipError_t launch_cache_write(const void* key, const void* value, void* kc,
 hipError_t launch_copy_blocks(void* kc, void* vc, const int* src,
                               const int* dst, int pairs, int num_blocks,
                               int64_t chunks_per_block, hipStream_t stream);
+hipError_t launch_swap_blocks(const void* sk, const void* sv, int snb, void* dk,
+                              void* dv, int dnb, const int* src, const int* dst,
+                              int pairs, int64_t chunks_per_block,
+                              hipStream_t stream);
 
 }  // namespace pa

@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
     syms = header_symbols()
     for name in ["pa_cache_write", "pa_decode", "pa_decode_splitk", "pa_decode_reduce",
                  "pa_splitk_workspace_size", "pa_status_str", "pa_kv_cache_shape",
-                 "pa_slot_mapping", "pa_copy_blocks"]:
+                 "pa_slot_mapping", "pa_copy_blocks", "pa_swap_blocks"]:
         assert name in syms
 
 
@@ -118,6 +118,14 @@ def test_cache_op_validation(pa):
     assert L.pa_copy_blocks(FAKE, FAKE, None, FAKE, 2, 10, 16, 2, 128, None) == 1
     assert L.pa_copy_blocks(FAKE, FAKE, FAKE, FAKE, 0, 10, 16, 2, 128, None) == 0
     assert L.pa_copy_blocks(FAKE, FAKE, FAKE, FAKE, 2, 10, 16, 2, 100, None) == 2
+    sw = L.pa_swap_blocks
+    assert sw(FAKE, FAKE, 10, FAKE, FAKE, 20, FAKE, FAKE, 0, 16, 2, 128, None) == 0
+    assert sw(FAKE, None, 10, FAKE, FAKE, 20, FAKE, FAKE, 3, 16, 2, 128, None) == 1
+    assert sw(FAKE, FAKE, 10, FAKE, FAKE, 20, FAKE, None, 3, 16, 2, 128, None) == 1
+    assert sw(FAKE, FAKE, 0, FAKE, FAKE, 20, FAKE, FAKE, 3, 16, 2, 128, None) == 2
+    assert sw(FAKE, FAKE, 10, FAKE, FAKE, 20, FAKE, FAKE, -1, 16, 2, 128, None) == 2
+    assert sw(FAKE, FAKE, 10, FAKE, FAKE, 20, FAKE, FAKE, 3, 16, 2, 100, None) == 2
+    assert sw(FAKE, FAKE, 10, FAKE + 8, FAKE, 20, FAKE, FAKE, 3, 16, 2, 128, None) == 4
 
 
 def test_binding_rejects_host_tensors(pa):

@@ -340,6 +340,59 @@ def test_copy_blocks_parity():
     assert (g[0] == kc).all() and (g[1] == vc).all()
 
 
+def test_swap_blocks_pinned_host_round_trip_bitwise():
+    """Swap ([P5] §4.4) through pa_swap_blocks: the used blocks go to a
+    pinned host pool bit-exactly (oracle swap_blocks; an out-of-range pair is
+    skipped), come back into a NaN-filled device pool under new ids, and the
+    decode over it is bit-identical to the decode over the original pool
+    with the tables relabelled."""
+    pa, runner = _gpu()
+    w = workloads.make("c3_small")
+    st = runner.upload(w)
+    runner.apply_history(w, st)
+    runner.write_step(st)
+    torch.cuda.synchronize()
+    B = w.block_size
+    used = sorted({int(b) for i, n in enumerate(w.context_lens)
+                   for b in w.block_tables[i, :(int(n) + B - 1) // B]})
+    nu = len(used)
+    host = torch.zeros((2, nu + 2) + tuple(st.pool.shape[2:]), dtype=torch.float16,
+                       pin_memory=True)
+    src = torch.tensor(used + [w.num_blocks + 5], dtype=torch.int32, device="cuda")
+    dst = torch.tensor(list(range(nu)) + [nu], dtype=torch.int32, device="cuda")
+    pa.pa_swap_blocks(st.pool[0], st.pool[1], host[0], host[1], src, dst)
+    torch.cuda.synchronize()
+    kc, vc = oracle_pool(w, oracle)
+    hk = np.zeros(tuple(host.shape[1:]), np.uint16)
+    hv = np.zeros_like(hk)
+    oracle.swap_blocks(kc, vc, hk, hv, used + [w.num_blocks + 5], list(range(nu)) + [nu])
+    h = host.numpy().view(np.uint16)
+    assert (h[0] == hk).all() and (h[1] == hv).all()
+
+    for mode in MODES:
+        decode_only(runner, st, mode)
+    torch.cuda.synchronize()
+    ref = {}
+    for mode in MODES:
+        decode_only(runner, st, mode)
+        torch.cuda.synchronize()
+        ref[mode] = st.out.cpu().numpy().view(np.uint16).copy()
+    new_ids = [w.num_blocks - 1 - j for j in range(nu)]
+    pool2 = torch.full_like(st.pool, float("nan"))
+    pa.pa_swap_blocks(host[0], host[1], pool2[0], pool2[1],
+                      torch.arange(nu, dtype=torch.int32, device="cuda"),
+                      torch.tensor(new_ids, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    relabel = np.arange(w.num_blocks)
+    relabel[used] = new_ids
+    st.pool = pool2
+    st.block_tables = torch.from_numpy(relabel[w.block_tables].astype(np.int32)).cuda()
+    for mode in MODES:
+        decode_only(runner, st, mode)
+        torch.cuda.synchronize()
+        assert (st.out.cpu().numpy().view(np.uint16) == ref[mode]).all(), mode
+
+
 def test_slot_mapping_parity_and_guards():
     pa, runner = _gpu()
     rng = np.random.default_rng(8)

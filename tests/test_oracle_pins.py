@@ -190,6 +190,47 @@ def test_copy_blocks():
         assert (kc[b] == k0[b]).all() and (vc[b] == v0[b]).all()
 
 
+def test_swap_blocks_moves_exactly_the_addressed_blocks():
+    """[P5] §4.4 swap: block bytes arrive unchanged (NaN payloads included),
+    nothing else in either pool changes, out-of-range pairs are skipped."""
+    rng = np.random.default_rng(2)
+    sk = rng.integers(0, 1 << 16, (5, 4, 2, 8), dtype=np.uint16)
+    sv = rng.integers(0, 1 << 16, (5, 4, 2, 8), dtype=np.uint16)
+    sk[3, 0, 0, :4] = [0x7E01, 0xFC00, 0x7C00, 0x8001]
+    dk = np.zeros((7, 4, 2, 8), np.uint16)
+    dv = np.zeros((7, 4, 2, 8), np.uint16)
+    s0k, s0v = sk.copy(), sv.copy()
+    oracle.swap_blocks(sk, sv, dk, dv, [3, 0, 4, 9], [6, 1, 2, 0])   # (9 -> 0) skipped
+    assert (sk == s0k).all() and (sv == s0v).all()
+    for a, b in ((3, 6), (0, 1), (4, 2)):
+        assert (dk[b] == s0k[a]).all() and (dv[b] == s0v[a]).all()
+    for b in (0, 3, 4, 5):
+        assert not dk[b].any() and not dv[b].any()
+
+
+def test_swap_out_and_in_round_trip_preserves_attention():
+    """Blocks swapped out to a second pool and back in under new ids give
+    the same decode once the tables are relabelled (paging does not change
+    the math, [GUST] 常见误解): bit-identical in the oracle."""
+    w = workloads.make("c1")
+    kc, vc = oracle_pool(w, oracle)
+    ref = oracle.decode(w.query, kc, vc, w.block_tables, w.context_lens, w.scale)
+    used = sorted({int(b) for i, n in enumerate(w.context_lens)
+                   for b in w.block_tables[i, :(int(n) + w.block_size - 1) // w.block_size]})
+    host_k = np.zeros((len(used),) + kc.shape[1:], np.uint16)
+    host_v = np.zeros_like(host_k)
+    oracle.swap_blocks(kc, vc, host_k, host_v, used, range(len(used)))
+    new_ids = [w.num_blocks - 1 - j for j in range(len(used))]
+    k2 = np.full_like(kc.view(np.uint16), 0x7E00)                     # NaN everywhere else
+    v2 = np.full_like(k2, 0x7E00)
+    oracle.swap_blocks(host_k, host_v, k2, v2, range(len(used)), new_ids)
+    relabel = {a: b for a, b in zip(used, new_ids)}
+    bt = np.vectorize(lambda x: relabel.get(int(x), int(x)))(w.block_tables).astype(np.int32)
+    out = oracle.decode(w.query, k2.view(np.float16), v2.view(np.float16), bt,
+                        w.context_lens, w.scale)
+    assert (out == ref).all()
+
+
 # ----------------------------------------------------------------------------
 # attention values
 # ----------------------------------------------------------------------------
