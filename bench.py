@@ -40,6 +40,10 @@ WORKLOADS = {
     "c4": "prefix sharing + COW: 16 prompts x 4 samples, 1024+r shared, tails U[0,512], 40/40 heads, D128, B16",
     "c5_b32": "long-context split-KV: 8 seqs ctx U[32768,131072], 64/8 heads, D128, B32",
     "c5_b64": "long-context split-KV: 8 seqs ctx U[32768,131072], 64/8 heads, D128, B64",
+    "c2_spec4": "speculative verify, 4 query tokens per seq: Llama-2-13B layer, 32 seqs "
+                "ctx U[4,2048], 40/40 heads, D128, B16",
+    "c3_spec4": "speculative verify, 4 query tokens per seq: GQA 32/8 heads, 64 seqs ctx "
+                "lognormal(700,1) in [4,8192], D128, B16",
 }
 
 
@@ -264,6 +268,118 @@ def swap_bench(args, w, dev) -> int:
     return 0
 
 
+def multi_kernel_bytes(w) -> int:
+    """Algorithmic bytes of one pa_decode_multi: the K/V of exactly
+    context_len tokens per sequence (once), the query rows read and output
+    rows written, the table entries, and the per-(row, head, partition)
+    states written by the partitions and read by the reduce."""
+    Q, H, D = w.query.shape
+    n = w.context_lens.astype(np.int64)
+    cu = w.info["cu_seqlens_q"]
+    P = w.partition_size
+    table = int(((n + w.block_size - 1) // w.block_size).sum()) * 4
+    parts = 0
+    for i in range(w.num_seqs):
+        T = int(cu[i + 1] - cu[i])
+        pos = int(n[i]) - T + np.arange(T)
+        parts += int((pos // P + 1).sum())
+    return kv_bytes(w) + 2 * Q * H * D * 2 + table + 2 * parts * H * (D + 2) * 4
+
+
+def multi_bench(args, w, dev) -> int:
+    """Steps of several query tokens per sequence: slot mapping + cache write
+    of every sequence's chunk, then pa_decode_multi (partitions + reduce)."""
+    import torch
+    import paged_kv_cache_120_amd as pa
+    from paged_kv_cache_120_amd import runner
+    base = runner.upload_multi(w, dev)
+    runner.apply_history(w, base)
+    steps = [base] + [runner.upload_multi(w, dev, pool=base.pool.clone())
+                      for _ in range(1, max(1, args.rotate))]
+    torch.cuda.synchronize()
+    R = len(steps)
+
+    def full(st):
+        runner.write_step(st)
+        runner.multi_step(st)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(steps[i % R])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            fn(steps[i % R])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_step = timed(full)
+    kms = timed(runner.multi_step)
+    full(steps[(args.steps - 1) % R])
+    torch.cuda.synchronize()
+    Q = int(w.query.shape[0])
+    kvb = kv_bytes(w)
+    kb = multi_kernel_bytes(w)
+    achieved = kb / (kms * 1e-3) / 1e9
+    rec = {
+        "metric": "paged multi-token (speculative verify) KV GB/s + query tokens/s",
+        "value": round(kvb / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "name": args.config,
+                   "num_seqs": w.num_seqs, "query_tokens": Q, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_size": w.head_size,
+                   "block_size": w.block_size, "partition_size": w.partition_size,
+                   "total_context_tokens": int(w.context_lens.sum()),
+                   "rotated_pool_copies": R, "seed": w.seed},
+        "accumulate": "f32", "kv_bytes_per_step": kvb,
+        "query_tokens_per_s": round(Q / (ms_step * 1e-3), 1),
+        "pct_hbm_peak": round(100 * kvb / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "multi_kernel + multi_reduce_kernel",
+                     "kernel_ms": round(kms, 5), "algorithmic_bytes": kb},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        gpu = steps[(args.steps - 1) % R].out.cpu().numpy().astype(np.float64)
+        kc, vc = w.pool_init[0].copy(), w.pool_init[1].copy()
+        oracle.apply_phases(kc, vc, list(w.history), w.block_size)
+        cu = w.info["cu_seqlens_q"]
+        try:
+            from threadpoolctl import threadpool_limits
+            ctx = threadpool_limits(1)
+        except Exception:                               # pragma: no cover
+            ctx = None
+        t0 = time.perf_counter()
+        done, rows = 0, 0
+        while time.perf_counter() - t0 < 10.0 and done < w.num_seqs:
+            oracle.apply_phases(kc, vc, [w.step_write], w.block_size)
+            i = done
+            o = oracle.decode_multi(w.query[cu[i]:cu[i + 1]], kc, vc, w.block_tables[i:i + 1],
+                                    np.array([0, cu[i + 1] - cu[i]], np.int32),
+                                    w.context_lens[i:i + 1], w.scale)
+            err = np.abs(gpu[cu[i]:cu[i + 1]] - o)
+            ok = bool(((err <= 2e-3) | (err <= 1e-2 * np.abs(o))).all())
+            rec.setdefault("parity", {"rows_checked": 0, "within_tolerance": True})
+            rec["parity"]["rows_checked"] += int(cu[i + 1] - cu[i])
+            rec["parity"]["within_tolerance"] &= ok
+            rows += int(cu[i + 1] - cu[i])
+            done += 1
+        el = time.perf_counter() - t0
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+        rec["cpu_baseline"] = {"value": round(rows / el, 3), "unit": "query tokens/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{done} sequences' query chunks ({rows} rows), "
+                                         f"float64 NumPy, 1 BLAS thread"}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,11 +387,12 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="fused",
-                    choices=["fused", "balanced", "splitk", "single", "swap"],
+                    choices=["fused", "balanced", "splitk", "single", "swap", "multi"],
                     help="fused: pa_decode_step (append + balanced decode, one kernel); "
                          "balanced/splitk/single: slot mapping + cache write + that decode; "
                          "swap: pa_swap_blocks of the batch's blocks to pinned host memory "
-                         "and back (its own JSON line)")
+                         "and back (its own JSON line); multi: cache write of each "
+                         "sequence's query chunk + pa_decode_multi (the *_spec4 configs)")
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--partition", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -300,6 +417,12 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     if args.mode == "swap":
         return swap_bench(args, w, dev)
+    if args.mode == "multi" or "cu_seqlens_q" in w.info:
+        if args.mode != "multi" or "cu_seqlens_q" not in w.info:
+            print("--mode multi goes with a multi-token config (c2_spec4, c3_spec4)",
+                  file=sys.stderr)
+            return 2
+        return multi_bench(args, w, dev)
 
     steps = []
     base = runner.upload(w, dev)

@@ -32,7 +32,7 @@ __all__ = [
     "kv_cache_shape", "kv_bytes_per_token", "block_bytes", "blocks_needed",
     "slots_reserved", "padding_slots", "slot_mapping", "cache_write",
     "copy_blocks", "swap_blocks", "apply_phases", "gather_kv", "decode", "decode_heads",
-    "partials", "merge",
+    "partials", "merge", "decode_multi",
 ]
 
 
@@ -300,4 +300,41 @@ def merge(m, s, O, context_lens, partition_size: int) -> np.ndarray:
                 Oa = Oa * np.exp(ma - mn) + Ob * np.exp(mb - mn)
                 ma = mn
             out[i, h] = Oa / sa
+    return out
+
+
+# ----------------------------------------------------------------------------
+# several query tokens per sequence
+# ----------------------------------------------------------------------------
+
+def decode_multi(query, key_cache, value_cache, block_tables, cu_seqlens_q,
+                 context_lens, scale: float) -> np.ndarray:
+    """Attention of several new query tokens per request over the same block
+    tables ([BOOK] §4.5 (2): the backend gets the query tokens of every
+    request delimited by cu_seqlens_q, the keys per request (seqused_k, here
+    context_lens) and block_table).  Sequence i owns query rows
+    cu[i] .. cu[i+1]-1, the last T_i = cu[i+1] - cu[i] of its n_i tokens
+    (written first, read after -- [BOOK] §4.5 (1)); row r = cu[i] + j is at
+    position p = n_i - T_i + j and attends to keys t = 0 .. p only (causal).
+    Two-pass softmax per row in float64; returns [Q, H, D]."""
+    q = np.asarray(query).view(np.float16)
+    Q, H, D = q.shape
+    Hkv = np.asarray(key_cache).shape[2]
+    g = H // Hkv
+    cu = np.asarray(cu_seqlens_q)
+    out = np.empty((Q, H, D), np.float64)
+    for i in range(len(context_lens)):
+        n = int(context_lens[i])
+        a, b = int(cu[i]), int(cu[i + 1])
+        T = b - a
+        if T == 0:
+            continue
+        assert 1 <= T <= n, "each query token needs its key in the cache"
+        K, V = gather_kv(key_cache, value_cache, block_tables[i], n)
+        for j in range(T):
+            p = n - T + j
+            for h in range(H):
+                out[a + j, h] = _two_pass_softmax_attention(
+                    q[a + j, h:h + 1].astype(np.float64), K[:p + 1, h // g],
+                    V[:p + 1, h // g], float(scale))[0]
     return out

@@ -19,7 +19,7 @@ __all__ = [
     "pa_slot_mapping", "pa_cache_write", "pa_copy_blocks", "pa_swap_blocks", "pa_decode",
     "pa_splitk_workspace_size", "pa_decode_splitk", "pa_decode_reduce",
     "pa_balanced_grid", "pa_balanced_workspace_size", "pa_decode_balanced",
-    "pa_decode_step", "STATUS",
+    "pa_decode_step", "pa_multi_workspace_size", "pa_decode_multi", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +60,9 @@ def _load() -> ctypes.CDLL:
                                             i32, i32, f32, i32, vp, sz, vp]),
         "pa_decode_reduce": (ctypes.c_int, [vp, vp, sz, vp, i32, i32, i32, i32, i32,
                                             i32, vp]),
+        "pa_multi_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
+        "pa_decode_multi": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, i32,
+                                           i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]),
         "pa_balanced_grid": (i32, [i32, i32, i32, i32]),
         "pa_balanced_workspace_size": (sz, [i32, i32, i32, i32, i32]),
         "pa_decode_balanced": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
@@ -281,6 +284,41 @@ def pa_decode_splitk(query, key_cache, value_cache, block_tables, context_lens,
     _check("pa_decode_splitk", _lib().pa_decode_splitk(
         q, kc, vc, bt, M, cl, S, H, Hkv, D, B, nb, float(scale),
         int(partition_size), ws, nbytes, _stream(stream)))
+
+
+def pa_multi_workspace_size(num_q_tokens: int, num_heads: int, head_size: int,
+                            max_blocks_per_seq: int, block_size: int,
+                            partition_size: int) -> int:
+    return int(_lib().pa_multi_workspace_size(num_q_tokens, num_heads, head_size,
+                                           max_blocks_per_seq, block_size,
+                                           partition_size))
+
+
+def pa_decode_multi(out, query, key_cache, value_cache, block_tables, cu_seqlens_q,
+                    context_lens, max_q_per_seq: int, scale: float,
+                    partition_size: int, workspace, stream=None) -> None:
+    """Several query tokens per sequence (rows cu_seqlens_q[i] ..
+    cu_seqlens_q[i+1]-1 are the last tokens of sequence i), causal within
+    the chunk.  query/out fp16 [num_q_tokens, H, D]."""
+    torch = _torch()
+    Q, H, D = query.shape
+    nb, B, Hkv, D2 = key_cache.shape
+    S = context_lens.shape[0]
+    if D2 != D or tuple(value_cache.shape) != (nb, B, Hkv, D) or \
+            tuple(out.shape) != (Q, H, D):
+        raise ValueError("pa_decode_multi: inconsistent shapes")
+    if block_tables.shape[0] != S or cu_seqlens_q.shape != (S + 1,):
+        raise ValueError("pa_decode_multi: block_tables / cu_seqlens_q do not match")
+    ws = _dev(workspace, workspace.dtype, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("pa_decode_multi", _lib().pa_decode_multi(
+        _dev(out, torch.float16, "out", 3), _dev(query, torch.float16, "query", 3),
+        _dev(key_cache, torch.float16, "key_cache", 4),
+        _dev(value_cache, torch.float16, "value_cache", 4),
+        _dev(block_tables, torch.int32, "block_tables", 2), block_tables.shape[1],
+        _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q", 1), Q, int(max_q_per_seq),
+        _dev(context_lens, torch.int32, "context_lens", 1), S, H, Hkv, D, B, nb,
+        float(scale), int(partition_size), ws, nbytes, _stream(stream)))
 
 
 def pa_decode_reduce(out, workspace, context_lens, max_blocks_per_seq: int,

@@ -260,6 +260,84 @@ pa_status pa_decode_splitk(const void* query, const void* key_cache,
                                       num_heads / num_kv_heads, grid, stream));
 }
 
+size_t pa_multi_workspace_size(int32_t num_q_tokens, int32_t num_heads,
+                               int32_t head_size, int32_t max_blocks_per_seq,
+                               int32_t block_size, int32_t partition_size) {
+  return pa_splitk_workspace_size(num_q_tokens, num_heads, head_size,
+                                  max_blocks_per_seq, block_size,
+                                  partition_size);
+}
+
+pa_status pa_decode_multi(void* out, const void* query, const void* key_cache,
+                          const void* value_cache, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq,
+                          const int32_t* cu_seqlens_q, int32_t num_q_tokens,
+                          int32_t max_q_per_seq, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_heads,
+                          int32_t num_kv_heads, int32_t head_size,
+                          int32_t block_size, int32_t num_blocks, float scale,
+                          int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  pa_status st = check_decode(query, key_cache, value_cache, block_tables,
+                              max_blocks_per_seq, context_lens, num_seqs,
+                              num_heads, num_kv_heads, head_size, block_size,
+                              num_blocks, scale);
+  if (st != PA_OK) return st;
+  if (num_q_tokens < 0 || max_q_per_seq <= 0 || num_heads > 65535 ||
+      partition_size <= 0 || partition_size % block_size != 0)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_q_tokens == 0) return PA_OK;
+  const int32_t g = num_heads / num_kv_heads;
+  const int64_t tiles = (max_q_per_seq + 16 / g - 1) / (16 / g);
+  const int64_t pm = max_partitions(max_blocks_per_seq, block_size, partition_size);
+  if (pm > 65535 || (int64_t)num_seqs * tiles > 65535 || num_q_tokens > 65535)
+    return PA_ERR_SHAPE;                      // grid.z, grid.y
+  if (!out || !cu_seqlens_q || !workspace) return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(workspace, 16) || !aligned(cu_seqlens_q, 4))
+    return PA_ERR_ALIGN;
+  if (workspace_bytes < pa_multi_workspace_size(num_q_tokens, num_heads,
+                                                head_size, max_blocks_per_seq,
+                                                block_size, partition_size))
+    return PA_ERR_WORKSPACE;
+  const size_t rows = (size_t)num_q_tokens * num_heads * pm;
+  pa::DecodeArgs a = {};
+  a.ws_max = static_cast<float*>(workspace);
+  a.ws_sum = a.ws_max + rows;
+  a.ws_out = a.ws_sum + rows;
+  a.query = static_cast<const _Float16*>(query);
+  a.key_cache = static_cast<const char*>(key_cache);
+  a.value_cache = static_cast<const char*>(value_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.partition_size = partition_size;
+  a.max_partitions = (int)pm;
+  a.split = 1;
+  a.scale = scale;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.q_tiles = (int)tiles;
+  a.num_q_tokens = num_q_tokens;
+  dim3 grid(num_kv_heads, (unsigned)(num_seqs * tiles), (unsigned)pm);
+  st = hip_status(pa::launch_multi(a, head_size, block_size, g, grid, stream));
+  if (st != PA_OK) return st;
+  pa::ReduceArgs r = {};
+  r.out = static_cast<_Float16*>(out);
+  r.ws_max = a.ws_max;
+  r.ws_sum = a.ws_sum;
+  r.ws_out = a.ws_out;
+  r.context_lens = context_lens;
+  r.num_heads = num_heads;
+  r.max_partitions = (int)pm;
+  r.partition_size = partition_size;
+  r.max_tokens = max_blocks_per_seq * block_size;
+  r.cu_seqlens_q = cu_seqlens_q;
+  r.num_seqs = num_seqs;
+  return hip_status(pa::launch_multi_reduce(r, head_size, num_q_tokens, stream));
+}
+
 pa_status pa_decode_reduce(void* out, const void* workspace,
                            size_t workspace_bytes,
                            const int32_t* context_lens, int32_t num_seqs,

@@ -32,6 +32,10 @@ struct DecodeArgs {
   const _Float16* new_value;
   int* slot_out;
   float scale;
+  // multi-token queries: query row offsets [S+1] and query tiles per sequence
+  const int* cu_seqlens_q;
+  int q_tiles;
+  int num_q_tokens;
 };
 
 
@@ -45,12 +49,18 @@ struct ReduceArgs {
   int max_partitions;
   int partition_size;
   int max_tokens;            // M * B
+  const int* cu_seqlens_q;   // multi-token reduce: [S+1]
+  int num_seqs;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int head_size, int block_size,
                          int group, dim3 grid, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_size, int num_seqs,
                          hipStream_t stream);
+hipError_t launch_multi(const DecodeArgs& a, int head_size, int block_size,
+                        int group, dim3 grid, hipStream_t stream);
+hipError_t launch_multi_reduce(const ReduceArgs& a, int head_size,
+                               int num_q_tokens, hipStream_t stream);
 hipError_t launch_balanced(const DecodeArgs& a, int head_size, int block_size,
                            int group, int grid, hipStream_t stream);
 // workgroups of the balanced kernel resident at once on the current device

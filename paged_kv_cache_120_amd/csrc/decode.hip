@@ -347,7 +347,7 @@ struct MfmaPath {
   static constexpr int VS = D + 4;              // padded LDS row (halves)
   static constexpr int kMinWaves = 4;           // 128 VGPRs: 4 waves per SIMD
   static_assert(B % 16 == 0, "a tile must not straddle two blocks");
-  static_assert(G <= 16, "one MFMA column per query head");
+  static_assert(G <= 16, "one MFMA column per query row");
 
   struct Smem {
     _Float16 vs[kWaves][TB][VS];
@@ -356,14 +356,27 @@ struct MfmaPath {
     float l[kWaves][G];
   };
 
-  // t0 must be a multiple of 16; `last` as for ValuPath::run
+  // t0 must be a multiple of 16; `last` as for ValuPath::run.  Column c
+  // (c < G) is query head kvh*G + c of sequence seq.
   template <class Sink>
   __device__ static void run(const DecodeArgs& a, Smem& sm, int kvh, int seq,
                              int t0, int t1, int last, Sink& sink) {
-    const int H = a.num_heads;
+    const int col = threadIdx.x & 15;
+    const int64_t qoff =
+        col < G ? ((int64_t)seq * a.num_heads + (int64_t)kvh * G + col) * D : -1;
+    run_cols(a, sm, kvh, seq, t0, t1, last, sink, qoff, 0x7fffffff);
+  }
+
+  // The same over columns given by the caller: this lane's column reads the
+  // query row at element offset qoff (-1: an unused column, zero query) and
+  // attends to keys t <= lim only (the causal limit of a query token).
+  template <class Sink>
+  __device__ static void run_cols(const DecodeArgs& a, Smem& sm, int kvh,
+                                  int seq, int t0, int t1, int last, Sink& sink,
+                                  int64_t qoff, int lim) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int col = lane & 15;                  // token row (A) / head (B, D)
+    const int col = lane & 15;                  // token row (A) / column (B, D)
     const int grp = lane >> 4;                  // lane group 0..3
     if (last >= 0) append_token<D, B>(a, kvh, seq, last);
 
@@ -371,10 +384,8 @@ struct MfmaPath {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (col < G)
-        v = *reinterpret_cast<const u32x4*>(
-            a.query + ((size_t)seq * H + (size_t)kvh * G + col) * D + kk * 32 +
-            grp * 8);
+      if (qoff >= 0)
+        v = *reinterpret_cast<const u32x4*>(a.query + qoff + kk * 32 + grp * 8);
       qb[kk] = __builtin_bit_cast(f16x8, v);
     }
 
@@ -441,7 +452,7 @@ struct MfmaPath {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = base + mt * 16 + grp * 4 + i;
-          sc[mt][i] = tok < t1 ? acc[i] * sl2 : -INFINITY;
+          sc[mt][i] = (tok < t1 && tok <= lim) ? acc[i] * sl2 : -INFINITY;
         }
       }
 
@@ -595,6 +606,102 @@ __global__ __launch_bounds__(D) void reduce_kernel(ReduceArgs a) {
     const float f = fast_exp2((a.ws_max[base + p] - mx) * kLog2e);
     S += a.ws_sum[base + p] * f;
     O += a.ws_out[(base + p) * D + d] * f;
+  }
+  *o = (_Float16)(O / S);
+}
+
+// ---------------------------------------------------------------------------
+// Multi-token queries over the same tables (speculative verify, chunked
+// prefill)
+// ---------------------------------------------------------------------------
+//
+// Sequence i has T_i = cu_seqlens_q[i+1] - cu_seqlens_q[i] query tokens, the
+// last T_i of its n_i cached tokens: query token j sits at position
+// n_i - T_i + j and attends to keys t <= that position (causal within the
+// chunk).  The matrix-core body runs with 16 columns = (query token, head)
+// pairs: 16/g consecutive query tokens x the g heads of one kv head, so one
+// workgroup reads each K/V byte of its key range once for all of them.
+// Grid (kv heads, sequences x query tiles, partitions); every (query row,
+// head, partition) state goes to the workspace and multi_reduce_kernel folds
+// the partitions of each row.
+template <int D, int B, int G>
+__global__ __launch_bounds__(kThreads) void multi_kernel(DecodeArgs a) {
+  using Path = MfmaPath<D, B, 16>;
+  constexpr int QT = 16 / G;                   // query tokens per tile
+  __shared__ typename Path::Smem sm;
+  const int kvh = blockIdx.x;
+  const int seq = blockIdx.y / a.q_tiles;
+  const int tile = blockIdx.y % a.q_tiles;
+  const int p = blockIdx.z;
+  const int H = a.num_heads;
+  const int q0 = a.cu_seqlens_q[seq];
+  const int T = a.cu_seqlens_q[seq + 1] - q0;
+  const int max_tok = a.max_blocks_per_seq * B;
+  int n = a.context_lens[seq];
+  n = n < max_tok ? n : max_tok;
+  const int j0 = tile * QT;
+  if (T <= 0 || j0 >= T || n <= 0 || q0 < 0) return;
+  int nq = T - j0 < QT ? T - j0 : QT;          // query tokens in this tile
+  // rows past num_q_tokens (offsets that break the precondition) are skipped
+  if (q0 + j0 + nq > a.num_q_tokens) nq = a.num_q_tokens - q0 - j0;
+  if (nq <= 0) return;
+  const int pos0 = n - T + j0;                 // position of its first token
+  const int lim_max = pos0 + nq - 1;           // last key the tile reads
+  const int t0 = p * a.partition_size;
+  if (lim_max < 0 || t0 > lim_max) return;
+  const int t1 = t0 + a.partition_size < lim_max + 1 ? t0 + a.partition_size
+                                                     : lim_max + 1;
+  const int col = threadIdx.x & 15;
+  const int qj = col / G;
+  const bool ok = qj < nq && pos0 + qj >= 0;
+  const int64_t qoff =
+      ok ? (((int64_t)q0 + j0 + qj) * H + (int64_t)kvh * G + col % G) * D : -1;
+  auto sink = [&](int c, int d, float mx, float L, float O) {
+    if (c / G >= nq) return;
+    const size_t r = (size_t)q0 + j0 + c / G;
+    const size_t pi = (r * H + (size_t)kvh * G + c % G) * a.max_partitions + p;
+    if (d == 0) {
+      a.ws_max[pi] = mx * kLn2;
+      a.ws_sum[pi] = L;
+    }
+    a.ws_out[pi * D + d] = O;
+  };
+  Path::run_cols(a, sm, kvh, seq, t0, t1, -1, sink, qoff, ok ? pos0 + qj : -1);
+}
+
+// One workgroup of D threads per (query head, query row): fold the
+// partitions that hold the row's keys 0 .. pos (its causal limit).
+template <int D>
+__global__ __launch_bounds__(D) void multi_reduce_kernel(ReduceArgs a) {
+  const int h = blockIdx.x;
+  const int r = blockIdx.y;
+  const int d = threadIdx.x;
+  const int H = a.num_heads;
+  int lo = 0, hi = a.num_seqs - 1;              // sequence holding row r
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.cu_seqlens_q[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  const int T = a.cu_seqlens_q[lo + 1] - a.cu_seqlens_q[lo];
+  int n = a.context_lens[lo];
+  n = n < a.max_tokens ? n : a.max_tokens;
+  const int pos = n - T + (r - a.cu_seqlens_q[lo]);
+  _Float16* o = a.out + ((size_t)r * H + h) * D + d;
+  if (n <= 0 || pos < 0) {
+    *o = (_Float16)0.f;
+    return;
+  }
+  int np = pos / a.partition_size + 1;
+  np = np < a.max_partitions ? np : a.max_partitions;
+  const size_t base = ((size_t)r * H + h) * a.max_partitions;
+  float mx = -INFINITY;
+  for (int q = 0; q < np; ++q) mx = fmaxf(mx, a.ws_max[base + q]);
+  float S = 0.f, O = 0.f;
+  for (int q = 0; q < np; ++q) {
+    const float f = fast_exp2((a.ws_max[base + q] - mx) * kLog2e);
+    S += a.ws_sum[base + q] * f;
+    O += a.ws_out[(base + q) * D + d] * f;
   }
   *o = (_Float16)(O / S);
 }
@@ -850,7 +957,7 @@ struct PathFor<D, B, 8> {
   using type = MfmaPath<D, B, 8>;
 };
 
-enum class Op { kPartition, kBalanced, kOccupancy };
+enum class Op { kPartition, kBalanced, kOccupancy, kMulti };
 
 template <int D, int B, int G>
 static hipError_t run_op(Op op, const DecodeArgs* a, dim3 grid,
@@ -866,6 +973,9 @@ static hipError_t run_op(Op op, const DecodeArgs* a, dim3 grid,
     case Op::kOccupancy:
       return hipOccupancyMaxActiveBlocksPerMultiprocessor(
           occ, reinterpret_cast<const void*>(&balanced_kernel<P, D, B, G>), kThreads, 0);
+    case Op::kMulti:
+      hipLaunchKernelGGL((multi_kernel<D, B, G>), grid, dim3(kThreads), 0, st, *a);
+      return hipGetLastError();
   }
   return hipErrorInvalidValue;
 }
@@ -926,6 +1036,26 @@ int balanced_grid(int head_size, int block_size, int group) {
                nullptr, &per_cu) != hipSuccess)
     return 0;
   return per_cu > 0 ? per_cu * cus : 0;
+}
+
+hipError_t launch_multi(const DecodeArgs& a, int head_size, int block_size,
+                        int group, dim3 grid, hipStream_t stream) {
+  return dispatch(Op::kMulti, head_size, block_size, group, &a, grid, stream,
+                  nullptr);
+}
+
+hipError_t launch_multi_reduce(const ReduceArgs& a, int head_size,
+                               int num_q_tokens, hipStream_t stream) {
+  dim3 grid(a.num_heads, num_q_tokens);
+  switch (head_size) {
+    case 64:
+      hipLaunchKernelGGL(multi_reduce_kernel<64>, grid, dim3(64), 0, stream, a);
+      return hipGetLastError();
+    case 128:
+      hipLaunchKernelGGL(multi_reduce_kernel<128>, grid, dim3(128), 0, stream, a);
+      return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, int head_size, int num_seqs,

@@ -4,7 +4,9 @@ A step is: copy-on-write block copies (if any), the slot mapping of the new
 tokens, the cache write, then decode -- single-pass (``pa_decode``), split
 (``pa_decode_splitk`` + ``pa_decode_reduce``) or balanced
 (``pa_decode_balanced``); or, mode "fused", copies then ``pa_decode_step``
-(slot mapping, cache write and balanced decode in one kernel).  Inputs are plain arrays (a
+(slot mapping, cache write and balanced decode in one kernel).  With several
+query tokens per sequence (``upload_multi``), ``multi_step`` runs
+``pa_decode_multi`` after the same writes.  Inputs are plain arrays (a
 workload object with the attributes used below); this module only uploads
 them and calls the binding, so every step runs in the library's kernels.
 """
@@ -17,9 +19,9 @@ import numpy as np
 import torch
 
 from . import (pa_balanced_grid, pa_balanced_workspace_size, pa_cache_write,
-               pa_copy_blocks, pa_decode, pa_decode_balanced, pa_decode_reduce,
-               pa_decode_splitk, pa_decode_step, pa_slot_mapping,
-               pa_splitk_workspace_size)
+               pa_copy_blocks, pa_decode, pa_decode_balanced, pa_decode_multi,
+               pa_decode_reduce, pa_decode_splitk, pa_decode_step,
+               pa_multi_workspace_size, pa_slot_mapping, pa_splitk_workspace_size)
 
 
 def _t(a, dev, dtype=None):
@@ -89,6 +91,30 @@ def run_phase(ph, pool, block_size: int, stream=None) -> None:
         return
     pa_slot_mapping(ph.slots, ph.table, ph.seq, ph.pos, block_size, stream=stream)
     pa_cache_write(ph.key, ph.value, pool[0], pool[1], ph.slots, stream=stream)
+
+
+def upload_multi(w, device: str = "cuda", pool: Optional[torch.Tensor] = None) -> DeviceStep:
+    """As upload, for a workload with several query tokens per sequence
+    (``w.info["cu_seqlens_q"]``): adds the row offsets, the largest per-
+    sequence query count and the multi-token workspace."""
+    st = upload(w, device, pool)
+    dev = st.pool.device
+    cu = w.info["cu_seqlens_q"]
+    st.cu_seqlens_q = _t(cu, dev)
+    st.max_q = int(max(1, int(np.diff(cu).max(initial=1))))
+    Q, H, D = w.query.shape
+    nbytes = pa_multi_workspace_size(Q, H, D, w.max_blocks_per_seq, w.block_size,
+                                     w.partition_size)
+    st.multi_workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    return st
+
+
+def multi_step(step: DeviceStep, stream=None) -> None:
+    """Attention of the step's query rows (their K/V already written)."""
+    pa_decode_multi(step.out, step.query, step.key_cache, step.value_cache,
+                    step.block_tables, step.cu_seqlens_q, step.context_lens,
+                    step.max_q, step.scale, step.partition_size,
+                    step.multi_workspace, stream=stream)
 
 
 def upload(w, device: str = "cuda", pool: Optional[torch.Tensor] = None) -> DeviceStep:

@@ -393,6 +393,82 @@ def test_swap_blocks_pinned_host_round_trip_bitwise():
         assert (st.out.cpu().numpy().view(np.uint16) == ref[mode]).all(), mode
 
 
+MULTI_SMALL = ["c1_prefill", "c2_small_spec4", "c3_small_spec4", "c3_small_chunk64",
+               "c5_b32_small_spec2"]
+
+
+def run_multi(w):
+    pa, runner = _gpu()
+    st = runner.upload_multi(w)
+    runner.apply_history(w, st)
+    runner.write_step(st)
+    runner.multi_step(st)
+    torch.cuda.synchronize()
+    return st
+
+
+@pytest.mark.parametrize("name", MULTI_SMALL + ["c2_spec4", "c3_spec4"])
+def test_multi_token_parity(name):
+    """pa_decode_multi (causal within each sequence's query chunk) against
+    oracle.decode_multi on every row and head; the pool after the chunk's
+    cache write is bit-exact."""
+    print(f"[multi] {name}", flush=True)
+    w = workloads.make(name)
+    st = run_multi(w)
+    kc, vc = oracle_pool(w, oracle)
+    g = st.pool.cpu().numpy().view(np.uint16)
+    assert (g[0] == kc).all() and (g[1] == vc).all()
+    ref = oracle.decode_multi(w.query, kc, vc, w.block_tables, w.info["cu_seqlens_q"],
+                              w.context_lens, w.scale)
+    assert_attention_close(st.out.cpu().numpy(), ref, f"{name}/multi")
+
+
+def test_multi_token_zero_length_sequence_and_partition_sizes():
+    """A sequence with no query rows contributes none and leaves its
+    neighbours' rows exact; results agree across partition sizes."""
+    pa, runner = _gpu()
+    w = workloads.make("c2_small_spec4")
+    st = run_multi(w)
+    cu = w.info["cu_seqlens_q"]
+    keep = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in range(w.num_seqs) if i != 1])
+    q2 = w.query[keep]
+    T = np.diff(cu).copy()
+    T[1] = 0
+    cu2 = np.concatenate([[0], np.cumsum(T)]).astype(np.int32)
+    kc, vc = oracle_pool(w, oracle)
+    ref = oracle.decode_multi(q2, kc, vc, w.block_tables, cu2, w.context_lens, w.scale)
+    for P in (16, 512, 2048):
+        out = torch.empty((len(keep),) + tuple(st.out.shape[1:]), dtype=torch.float16,
+                          device="cuda")
+        ws = torch.empty(pa.pa_multi_workspace_size(len(keep), w.num_heads, w.head_size,
+                                                    w.max_blocks_per_seq, w.block_size, P),
+                         dtype=torch.uint8, device="cuda")
+        pa.pa_decode_multi(out, torch.from_numpy(q2).cuda(), st.key_cache, st.value_cache,
+                           st.block_tables, torch.from_numpy(cu2).cuda(), st.context_lens,
+                           4, w.scale, P, ws)
+        torch.cuda.synchronize()
+        assert_attention_close(out.cpu().numpy(), ref, f"zero-length seq, P={P}")
+
+
+def test_multi_token_one_row_per_sequence_matches_decode():
+    """With one query row per sequence pa_decode_multi computes decode: the
+    same oracle bar as pa_decode on the decode workload."""
+    pa, runner = _gpu()
+    w = workloads.make("c3_small")
+    st = run_gpu(w, "splitk")
+    cu = torch.arange(w.num_seqs + 1, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(st.out)
+    ws = torch.empty(pa.pa_multi_workspace_size(w.num_seqs, w.num_heads, w.head_size,
+                                                w.max_blocks_per_seq, w.block_size, 512),
+                     dtype=torch.uint8, device="cuda")
+    pa.pa_decode_multi(out, st.query, st.key_cache, st.value_cache, st.block_tables, cu,
+                       st.context_lens, 1, w.scale, 512, ws)
+    torch.cuda.synchronize()
+    kc, vc = oracle_pool(w, oracle)
+    ref = oracle.decode(w.query, kc, vc, w.block_tables, w.context_lens, w.scale)
+    assert_attention_close(out.cpu().numpy(), ref, "multi with T=1")
+
+
 def test_slot_mapping_parity_and_guards():
     pa, runner = _gpu()
     rng = np.random.default_rng(8)

@@ -484,3 +484,104 @@ def test_shared_prefix_equals_private_copies():
         assert (rows == rows[0]).all()
     # ... and the partial prefix block was copied for all but one sample
     assert w.info["hist_copies"] + w.info["step_copies"] == 3 * w.info["prompts"]
+
+
+# ----------------------------------------------------------------------------
+# several query tokens per sequence (decode_multi)
+# ----------------------------------------------------------------------------
+
+def _multi_inputs(name):
+    w = workloads.make(name)
+    kc, vc = oracle_pool(w, oracle)
+    return w, kc, vc, w.info["cu_seqlens_q"]
+
+
+def test_multi_one_token_per_sequence_is_decode():
+    """T_i = 1 reduces to the decode definition."""
+    w = workloads.make("c3_small")
+    kc, vc = oracle_pool(w, oracle)
+    cu = np.arange(w.num_seqs + 1, dtype=np.int32)
+    a = oracle.decode_multi(w.query, kc, vc, w.block_tables, cu, w.context_lens, w.scale)
+    b = oracle.decode(w.query, kc, vc, w.block_tables, w.context_lens, w.scale)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-14)
+
+
+def test_multi_brute_force_causal_loops():
+    """Pure-Python loops with the causal limit written out, over contiguous
+    K/V assembled from the token rows (no pool, no table)."""
+    w = workloads.make("c1_prefill")
+    kc, vc = oracle_pool(w, oracle)
+    cu = w.info["cu_seqlens_q"]
+    got = oracle.decode_multi(w.query, kc, vc, w.block_tables, cu, w.context_lens, w.scale)
+    kv = contiguous_kv(w)
+    q = w.query.astype(np.float64)
+    g = w.group
+    for i, (K, V) in enumerate(kv):
+        n = len(K)
+        T = int(cu[i + 1] - cu[i])
+        for j in (0, T // 2, T - 1):
+            pos = n - T + j
+            for h in (0, w.num_heads - 1):
+                ref = brute_force(q[cu[i] + j, h], K[:pos + 1, h // g].astype(np.float64),
+                                  V[:pos + 1, h // g].astype(np.float64), w.scale)
+                assert np.allclose(got[cu[i] + j, h], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_multi_matches_sdpa_with_explicit_causal_mask():
+    """torch scaled_dot_product_attention (float64, CPU) with the
+    bottom-right causal mask built explicitly, over contiguous K/V."""
+    w = workloads.make("c3_small_chunk64")
+    kc, vc = oracle_pool(w, oracle)
+    cu = w.info["cu_seqlens_q"]
+    got = oracle.decode_multi(w.query, kc, vc, w.block_tables, cu, w.context_lens, w.scale)
+    g = w.group
+    for i, (K, V) in enumerate(contiguous_kv(w)):
+        n = len(K)
+        T = int(cu[i + 1] - cu[i])
+        q = torch.from_numpy(w.query[cu[i]:cu[i + 1]].astype(np.float64)).transpose(0, 1)
+        Kt = torch.from_numpy(K.astype(np.float64)).transpose(0, 1).repeat_interleave(g, 0)
+        Vt = torch.from_numpy(V.astype(np.float64)).transpose(0, 1).repeat_interleave(g, 0)
+        pos = torch.arange(n - T, n)[:, None]
+        mask = torch.arange(n)[None, :] <= pos                      # [T, n]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q, Kt, Vt, attn_mask=mask, scale=w.scale).transpose(0, 1).numpy()
+        assert np.allclose(got[cu[i]:cu[i + 1]], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_multi_prefill_first_row_is_first_value():
+    """Whole-prompt prefill: the first token attends only to itself, so its
+    output is V_0 exactly."""
+    w, kc, vc, cu = _multi_inputs("c1_prefill")
+    got = oracle.decode_multi(w.query, kc, vc, w.block_tables, cu, w.context_lens, w.scale)
+    for i in range(w.num_seqs):
+        assert int(cu[i + 1] - cu[i]) == int(w.context_lens[i])
+        K, V = oracle.gather_kv(kc, vc, w.block_tables[i], int(w.context_lens[i]))
+        for h in range(w.num_heads):
+            assert (got[cu[i], h] == V[0, h // w.group]).all()
+
+
+def test_multi_rows_ignore_later_keys():
+    """Causality: rewriting the K/V of positions after a row's own leaves
+    that row bit-identical (and changes the last row)."""
+    w, kc, vc, cu = _multi_inputs("c2_small_spec4")
+    a = oracle.decode_multi(w.query, kc, vc, w.block_tables, cu, w.context_lens, w.scale)
+    kc2, vc2 = kc.copy(), vc.copy()
+    B = w.block_size
+    for i in range(w.num_seqs):
+        n = int(w.context_lens[i])
+        T = int(cu[i + 1] - cu[i])
+        if T < 2:
+            continue
+        t = n - 1                                       # the chunk's last position
+        b = int(w.block_tables[i, t // B])
+        kc2.view(np.uint16)[b, t % B] ^= 0x1234
+        vc2.view(np.uint16)[b, t % B] ^= 0x0F0F
+    b2 = oracle.decode_multi(w.query, kc2, vc2, w.block_tables, cu, w.context_lens, w.scale)
+    changed = False
+    for i in range(w.num_seqs):
+        T = int(cu[i + 1] - cu[i])
+        if T < 2:
+            continue
+        assert (a[cu[i]:cu[i + 1] - 1] == b2[cu[i]:cu[i + 1] - 1]).all()
+        changed |= not (a[cu[i + 1] - 1] == b2[cu[i + 1] - 1]).all()
+    assert changed

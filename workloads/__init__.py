@@ -270,6 +270,31 @@ PRESETS: Dict[str, dict] = {
                          lens=_lens_uniform(1500, 5000),
                          pool=("choice_scale", 1.25), max_context=131072,
                          key_outliers=(0.01, 8.0), seed=1017),
+    # ---- several query tokens per sequence (the last q_len of each) ----
+    # speculative verify of 4 draft tokens at the Llama-2-13B and GQA shapes
+    "c2_spec4": dict(S=32, H=40, Hkv=40, D=128, B=16, lens=_lens_uniform(4, 2048),
+                     pool=("freelist_nb", 4000), max_context=2048, q_len=4, seed=1021),
+    "c3_spec4": dict(S=64, H=32, Hkv=8, D=128, B=16,
+                     lens=_lens_lognormal(700, 1.0, 4, 8192),
+                     pool=("choice_scale", 1.25), max_context=8192, q_len=4, seed=1022),
+    # reduced sizes: verify, a 64-token prefill chunk, whole-prompt prefill
+    "c1_prefill": dict(S=3, H=4, Hkv=4, D=64, B=16, lens=_lens_fixed([25, 47, 12]),
+                       pool=("choice_nb", 64), max_context=2048, q_len=2048, seed=1023),
+    "c2_small_spec4": dict(S=6, H=40, Hkv=40, D=128, B=16, lens=_lens_uniform(1, 2048),
+                           pool=("freelist_nb", 1000), max_context=2048, q_len=4,
+                           seed=1024),
+    "c3_small_spec4": dict(S=10, H=32, Hkv=8, D=128, B=16,
+                           lens=_lens_lognormal(700, 1.0, 1, 8192),
+                           pool=("choice_scale", 1.25), max_context=8192, q_len=4,
+                           seed=1025),
+    "c3_small_chunk64": dict(S=6, H=32, Hkv=8, D=128, B=16,
+                             lens=_lens_uniform(40, 1500),
+                             pool=("choice_scale", 1.25), max_context=8192, q_len=64,
+                             seed=1026),
+    "c5_b32_small_spec2": dict(S=3, H=64, Hkv=8, D=128, B=32,
+                               lens=_lens_uniform(1500, 5000),
+                               pool=("choice_scale", 1.25), max_context=131072,
+                               key_outliers=(0.01, 8.0), q_len=2, seed=1027),
 }
 
 
@@ -346,26 +371,35 @@ def _make_plain(name: str, spec: dict, seed: int, garbage: str) -> Workload:
         ref = fl.ref
     _fill_unused(tables, used, ref, rng)
 
-    # history: positions 0..n-2 of every sequence; step: position n-1
-    hist_seq = np.repeat(np.arange(S, dtype=np.int32), lens - 1)
-    hist_pos = np.concatenate([np.arange(n - 1, dtype=np.int32) for n in lens]) \
+    # history: positions 0..n-1-Tq of every sequence; step: the last Tq
+    # positions (Tq = 1 for decode; min(q_len, n) for multi-token queries)
+    qn = np.minimum(lens, int(spec.get("q_len", 1))).astype(np.int64)
+    hist_seq = np.repeat(np.arange(S, dtype=np.int32), lens - qn)
+    hist_pos = np.concatenate([np.arange(n - t, dtype=np.int32) for n, t in zip(lens, qn)]) \
         if S else np.zeros(0, np.int32)
     T = int(hist_seq.size)
+    Q = int(qn.sum())
     hk = normal_f16(seed, "hist_key", (T, Hkv, D))
     hv = normal_f16(seed, "hist_value", (T, Hkv, D))
-    sk = normal_f16(seed, "step_key", (S, Hkv, D))
-    sv = normal_f16(seed, "step_value", (S, Hkv, D))
+    sk = normal_f16(seed, "step_key", (Q, Hkv, D))
+    sv = normal_f16(seed, "step_value", (Q, Hkv, D))
     if "key_outliers" in spec:
         frac, mult = spec["key_outliers"]
         for tag, arr in (("hist_outl", hk), ("step_outl", sk)):
             r = np.random.default_rng(_seedseq(seed, tag))
             mask = r.random(arr.shape[:2]) < frac
             arr[mask] = (arr[mask].astype(np.float32) * np.float32(mult)).astype(np.float16)
-    q = normal_f16(seed, "query", (S, H, D))
+    q = normal_f16(seed, "query", (Q, H, D))
     pool = garbage_u16(seed, "pool", (2, nb, B, Hkv, D), finite=(garbage == "finite"))
 
-    step = WritePhase(tables, np.arange(S, dtype=np.int32),
-                      (lens - 1).astype(np.int32), sk, sv)
+    step_seq = np.repeat(np.arange(S, dtype=np.int32), qn)
+    step_pos = np.concatenate([np.arange(n - t, n, dtype=np.int32) for n, t in zip(lens, qn)]) \
+        if S else np.zeros(0, np.int32)
+    step = WritePhase(tables, step_seq, step_pos, sk, sv)
+    info = {"blocks_needed_total": need}
+    if "q_len" in spec:
+        info["q_lens"] = qn.astype(np.int32)
+        info["cu_seqlens_q"] = np.concatenate([[0], np.cumsum(qn)]).astype(np.int32)
     hist = [WritePhase(tables, hist_seq, hist_pos, hk, hv)]
     return Workload(
         name=name, seed=seed, num_seqs=S, num_heads=H, num_kv_heads=Hkv,
@@ -374,7 +408,7 @@ def _make_plain(name: str, spec: dict, seed: int, garbage: str) -> Workload:
         context_lens=lens.astype(np.int32), block_tables=tables, query=q,
         pool_init=pool, history=hist, step_copies=None, step_write=step,
         blocks_used=used.astype(np.int32), ref_cnt=ref.astype(np.int32),
-        info={"blocks_needed_total": need},
+        info=info,
     )
 
 
