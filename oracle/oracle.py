@@ -32,7 +32,9 @@ __all__ = [
     "kv_cache_shape", "kv_bytes_per_token", "block_bytes", "blocks_needed",
     "slots_reserved", "padding_slots", "slot_mapping", "cache_write",
     "copy_blocks", "swap_blocks", "apply_phases", "gather_kv", "decode", "decode_heads",
-    "partials", "merge", "decode_multi",
+    "partials", "merge", "decode_multi", "fp8_e4m3_value", "fp8_e4m3_decode",
+    "fp8_e4m3_encode", "fp8_quantize_rows", "cache_write_fp8", "apply_phases_fp8",
+    "gather_kv_fp8", "decode_fp8",
 ]
 
 
@@ -338,3 +340,145 @@ def decode_multi(query, key_cache, value_cache, block_tables, cu_seqlens_q,
                     q[a + j, h:h + 1].astype(np.float64), K[:p + 1, h // g],
                     V[:p + 1, h // g], float(scale))[0]
     return out
+
+
+# ----------------------------------------------------------------------------
+# fp8 (e4m3) KV cache
+# ----------------------------------------------------------------------------
+# [BOOK] §4.8 lists a lower-precision KV cache among the ways to fit more
+# tokens in a KV budget; [CSDN] 三.2 (the KVBlock field table) stores block K/V
+# as FP16 or FP8.  The pages fix no FP8 format or scaling; the reading taken
+# is the OCP 8-bit floating point format E4M3 ("e4m3fn": sign, 4 exponent
+# bits with bias 7, 3 mantissa bits, no infinities, exponent and mantissa
+# all ones = NaN, largest finite value 448) with one scale per tensor:
+# stored value = decode(code) * scale, code = encode(x / scale).
+
+def fp8_e4m3_value(code: int) -> float:
+    """Value of one E4M3 code from the format's definition (NaN for the two
+    NaN codes)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:                                  # subnormal: m/8 * 2^(1-7)
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Elementwise fp8_e4m3_value of a uint8 array, float64."""
+    table = np.array([fp8_e4m3_value(c) for c in range(256)], np.float64)
+    return table[np.asarray(codes, np.uint8)]
+
+
+def fp8_e4m3_encode(x) -> np.ndarray:
+    """Code of the E4M3 value nearest to each float in x, ties to the code
+    with an even mantissa (round to nearest even); magnitudes are first
+    clamped to 448, NaN gives the NaN code of its sign.  Comparisons are
+    against exact midpoints, so no rounding happens inside."""
+    a = np.asarray(x, np.float64)
+    mags = np.array([fp8_e4m3_value(c) for c in range(0x7F)])   # 0 .. 448
+    neg = np.signbit(a)
+    nan = np.isnan(a)
+    m = np.minimum(np.abs(np.where(nan, 0.0, a)), 448.0)
+    hi = np.searchsorted(mags, m, side="left")                  # first mag >= m
+    exact = mags[np.minimum(hi, len(mags) - 1)] == m
+    lo = np.maximum(hi - 1, 0)
+    mid = (mags[lo] + mags[np.minimum(hi, len(mags) - 1)]) / 2.0
+    tie_pick = np.where(lo % 2 == 0, lo, hi)                    # even mantissa
+    c = np.where(exact, hi, np.where(m < mid, lo, np.where(m > mid, hi, tie_pick)))
+    c = np.where(nan, 0x7F, c).astype(np.uint8)
+    return (c | np.where(neg, 0x80, 0).astype(np.uint8)).astype(np.uint8)
+
+
+def fp8_quantize_rows(rows, scale: float) -> np.ndarray:
+    """fp16 rows -> codes: x times the fp32 reciprocal of the scale, the
+    product rounded to fp32 (the precision the quantised code is decided
+    in), then encoded.  The code depends only on x's 16 bits, so it is
+    computed once for each of the 65536 fp16 values and looked up."""
+    inv = np.float32(1.0) / np.float32(scale)
+    every = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    with np.errstate(over="ignore", invalid="ignore"):
+        prod = every.astype(np.float32) * inv
+    table = fp8_e4m3_encode(prod.astype(np.float64))
+    return table[np.asarray(rows).view(np.uint16)]
+
+
+def cache_write_fp8(key_cache: np.ndarray, value_cache: np.ndarray,
+                    key: np.ndarray, value: np.ndarray, slots,
+                    k_scale: float, v_scale: float) -> None:
+    """As cache_write, into an fp8 pool (uint8 [nb, B, H_kv, D]): the rows
+    are quantised with their tensor's scale first."""
+    nb, B, Hkv, D = key_cache.shape
+    kc = key_cache.reshape(nb * B, Hkv, D)
+    vc = value_cache.reshape(nb * B, Hkv, D)
+    kq = fp8_quantize_rows(key, k_scale)
+    vq = fp8_quantize_rows(value, v_scale)
+    for j in range(len(slots)):
+        s = int(slots[j])
+        if s < 0:
+            continue
+        kc[s] = kq[j]
+        vc[s] = vq[j]
+
+
+def apply_phases_fp8(key_cache: np.ndarray, value_cache: np.ndarray, phases,
+                     block_size: int, k_scale: float, v_scale: float) -> None:
+    """apply_phases for an fp8 pool: writes quantise, block copies move the
+    one-byte codes."""
+    for ph in phases:
+        if ph is None:
+            continue
+        if hasattr(ph, "src"):
+            for a, b in zip(ph.src, ph.dst):
+                key_cache[int(b)] = key_cache[int(a)]
+                value_cache[int(b)] = value_cache[int(a)]
+        else:
+            s = slot_mapping(ph.table, ph.seq, ph.pos, block_size)
+            cache_write_fp8(key_cache, value_cache, ph.key, ph.value, s,
+                            k_scale, v_scale)
+
+
+def gather_kv_fp8(key_cache, value_cache, table_row, n: int, k_scale: float,
+                  v_scale: float):
+    """gather_kv over an fp8 pool: the first n token rows in logical order,
+    dequantised (code value times scale), float64 [n, H_kv, D]."""
+    kc = np.asarray(key_cache, np.uint8)
+    vc = np.asarray(value_cache, np.uint8)
+    B = kc.shape[1]
+    ids = [int(table_row[lb]) for lb in range(blocks_needed(n, B))]
+    for b in ids:
+        assert 0 <= b < kc.shape[0], "block id out of range"
+    K = np.concatenate([kc[b] for b in ids], axis=0)[:n]
+    V = np.concatenate([vc[b] for b in ids], axis=0)[:n]
+    return (fp8_e4m3_decode(K) * float(k_scale),
+            fp8_e4m3_decode(V) * float(v_scale))
+
+
+def decode_fp8(query, key_cache, value_cache, block_tables, context_lens,
+               scale: float, k_scale: float, v_scale: float,
+               pairs=None) -> np.ndarray:
+    """decode over an fp8 pool: attention over the dequantised K and V.
+    With ``pairs`` (a list of (sequence, query head)), only those outputs,
+    [len(pairs), D]; else every one, [S, H, D]."""
+    q = np.asarray(query).view(np.float16)
+    S, H, D = q.shape
+    Hkv = np.asarray(key_cache).shape[2]
+    g = H // Hkv
+    todo = pairs if pairs is not None else [(i, h) for i in range(S) for h in range(H)]
+    out = np.empty((len(todo), D), np.float64)
+    cur, K, V = None, None, None
+    for k, (i, h) in enumerate(todo):
+        i, h = int(i), int(h)
+        if i != cur:
+            n = int(context_lens[i])
+            assert n >= 1, "context_len must be >= 1"
+            K, V = gather_kv_fp8(key_cache, value_cache, block_tables[i], n,
+                                 k_scale, v_scale)
+            cur = i
+        out[k] = _two_pass_softmax_attention(
+            q[i, h:h + 1].astype(np.float64), K[:, h // g], V[:, h // g],
+            float(scale))[0]
+    return out if pairs is not None else out.reshape(S, H, D)

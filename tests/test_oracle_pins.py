@@ -585,3 +585,114 @@ def test_multi_rows_ignore_later_keys():
         assert (a[cu[i]:cu[i + 1] - 1] == b2[cu[i]:cu[i + 1] - 1]).all()
         changed |= not (a[cu[i + 1] - 1] == b2[cu[i + 1] - 1]).all()
     assert changed
+
+
+# ----------------------------------------------------------------------------
+# fp8 (e4m3) KV cache: the format's definition, a library codec, closed forms
+# ----------------------------------------------------------------------------
+
+def _finite_fp16():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    return h[np.isfinite(h)]
+
+
+def test_fp8_value_table_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.fp8_e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert (np.isnan(ours) == nan).all() and nan.sum() == 2      # 0x7f and 0xff
+    assert (ours[~nan] == ref[~nan]).all()
+    assert (np.signbit(ours[~nan]) == np.signbit(ref[~nan])).all()
+
+
+def test_fp8_value_closed_forms():
+    v = oracle.fp8_e4m3_value
+    assert v(0x7E) == 448.0 and v(0xFE) == -448.0            # 1.75 * 2^8
+    assert v(0x01) == 2.0 ** -9                               # smallest subnormal
+    assert v(0x07) == 7 / 8 * 2.0 ** -6                       # largest subnormal
+    assert v(0x08) == 2.0 ** -6                               # smallest normal
+    assert v(0x38) == 1.0 and v(0x40) == 2.0 and v(0x3C) == 1.5
+    assert v(0x00) == 0.0 and math.copysign(1.0, v(0x80)) == -1.0
+    assert math.isnan(v(0x7F)) and math.isnan(v(0xFF))
+    mags = [v(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(mags, mags[1:]))          # code order = value order
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.0123, 2.7, 1 / 448])
+def test_fp8_encode_matches_torch_on_every_finite_fp16(scale):
+    x = _finite_fp16().astype(np.float32)
+    inv = np.float32(1.0) / np.float32(scale)
+    with np.errstate(over="ignore"):
+        y = (x * inv).astype(np.float32)
+    ours = oracle.fp8_quantize_rows(_finite_fp16(), scale)
+    # torch's conversion rounds to nearest even but gives NaN far above the
+    # largest finite value, so it is handed the clamped product
+    ref = torch.from_numpy(np.clip(y, -448, 448)).to(torch.float8_e4m3fn)
+    assert (ours == ref.view(torch.uint8).numpy()).all()
+
+
+def test_fp8_encode_ties_clamp_and_specials():
+    e = lambda xs: [int(c) for c in oracle.fp8_e4m3_encode(np.array(xs, np.float64))]
+    assert e([2.0 ** -10, 3 * 2.0 ** -10]) == [0x00, 0x02]     # ties to even
+    assert e([1.0625, 1.1875, 1.3125]) == [0x38, 0x3A, 0x3A]   # midpoints: even wins
+    assert e([1.0626, 1.0624]) == [0x39, 0x38]
+    assert e([448.0, 449.0, 1e9, np.inf, -np.inf]) == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE]
+    assert e([-0.0, -1e-5, 1e-5]) == [0x80, 0x80, 0x00]         # sign kept on underflow
+    assert e([np.nan]) == [0x7F]
+
+
+def test_fp8_encode_inverts_value():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert (oracle.fp8_e4m3_encode(oracle.fp8_e4m3_decode(codes)) == codes).all()
+
+
+def test_fp8_quantisation_error_bound():
+    # round to nearest with 3 mantissa bits: error <= 2^-4 relative in the
+    # normal range, <= 2^-10 (half the subnormal step) below it
+    rng = np.random.default_rng(5)
+    y = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 0.1, 3.0, 100.0)])
+    y = y[np.abs(y) <= 448]
+    err = np.abs(oracle.fp8_e4m3_decode(oracle.fp8_e4m3_encode(y)) - y)
+    assert (err <= np.maximum(2.0 ** -4 * np.abs(y), 2.0 ** -10)).all()
+
+
+def test_fp8_cache_write_places_quantised_rows():
+    rng = np.random.default_rng(6)
+    nb, B, Hkv, D = 3, 4, 2, 8
+    kc = np.full((nb, B, Hkv, D), 0xAA, np.uint8)
+    vc = kc.copy()
+    key = (rng.standard_normal((3, Hkv, D)) * 4).astype(np.float16)
+    val = (rng.standard_normal((3, Hkv, D)) * 4).astype(np.float16)
+    oracle.cache_write_fp8(kc, vc, key, val, [5, -1, 11], 0.05, 0.02)
+    tk = lambda x, s: torch.from_numpy(np.clip(
+        x.astype(np.float32) * (np.float32(1) / np.float32(s)), -448, 448)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (kc.reshape(nb * B, Hkv, D)[5] == tk(key[0], 0.05)).all()
+    assert (vc.reshape(nb * B, Hkv, D)[11] == tk(val[2], 0.02)).all()
+    untouched = np.ones(nb * B, bool)
+    untouched[[5, 11]] = False
+    assert (kc.reshape(nb * B, Hkv, D)[untouched] == 0xAA).all()
+
+
+def test_fp8_decode_equals_fp16_decode_of_the_dequantised_pool():
+    # power-of-two scales make every dequantised value an fp16 number, so an
+    # fp16 pool holding them must give the same attention
+    rng = np.random.default_rng(7)
+    nb, B, Hkv, D, H, S = 9, 16, 2, 64, 8, 3
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    kc = rng.choice(finite[np.abs(oracle.fp8_e4m3_decode(finite)) < 8], (nb, B, Hkv, D))
+    vc = rng.choice(finite, (nb, B, Hkv, D))
+    ks, vs = 0.125, 2.0 ** -7
+    k16 = (oracle.fp8_e4m3_decode(kc) * ks).astype(np.float16)
+    v16 = (oracle.fp8_e4m3_decode(vc) * vs).astype(np.float16)
+    assert (k16.astype(np.float64) == oracle.fp8_e4m3_decode(kc) * ks).all()
+    q = rng.standard_normal((S, H, D)).astype(np.float16)
+    bt = np.array([[4, 1, 7], [0, 8, 2], [3, 5, 6]], np.int32)
+    cl = np.array([33, 1, 48], np.int32)
+    ref = oracle.decode(q, k16, v16, bt, cl, 0.125)
+    got = oracle.decode_fp8(q, kc, vc, bt, cl, 0.125, ks, vs)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-14)
+    pairs = [(2, 7), (0, 0), (1, 3)]
+    sub = oracle.decode_fp8(q, kc, vc, bt, cl, 0.125, ks, vs, pairs=pairs)
+    assert np.allclose(sub, np.stack([ref[i, h] for i, h in pairs]), rtol=1e-12, atol=1e-14)
