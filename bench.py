@@ -380,6 +380,108 @@ def multi_bench(args, w, dev) -> int:
     return 0
 
 
+def fp8_scales(w):
+    """Per-tensor scales mapping the largest |K| and |V| the workload writes
+    to 448, the largest finite e4m3 magnitude."""
+    rows = [p for p in w.history if hasattr(p, "seq")] + [w.step_write]
+    ka = max(float(np.abs(p.key.astype(np.float32)).max(initial=0)) for p in rows)
+    va = max(float(np.abs(p.value.astype(np.float32)).max(initial=0)) for p in rows)
+    return ka / 448.0, va / 448.0
+
+
+def fp8_bench(args, w, dev) -> int:
+    """Decode over an fp8 (e4m3) pool: COW copies, slot mapping,
+    pa_cache_write_fp8 of the new tokens, then pa_decode_balanced_fp8."""
+    import torch
+    from paged_kv_cache_120_amd import runner
+    ks, vs = fp8_scales(w)
+    base = runner.upload_fp8(w, ks, vs, dev)
+    runner.apply_history_fp8(w, base)
+    steps = [base]
+    for _ in range(1, max(1, args.rotate)):
+        st = runner.upload_fp8(w, ks, vs, dev)
+        st.pool = base.pool.clone()
+        steps.append(st)
+    torch.cuda.synchronize()
+    R = len(steps)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(steps[i % R])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            fn(steps[i % R])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_step = timed(runner.fp8_step)
+    kms = timed(runner.fp8_decode)
+    runner.fp8_step(steps[(args.steps - 1) % R])
+    torch.cuda.synchronize()
+    kvb = kv_bytes(w) // 2                         # one byte per element
+    S, H, D = w.query.shape
+    kb = balanced_kernel_bytes(w, steps[0].grid, False) - kv_bytes(w) // 2
+    achieved = kb / (kms * 1e-3) / 1e9
+    value = kvb / (ms_step * 1e-3) / 1e9
+    rec = {
+        "metric": "paged decode over an fp8 (e4m3) KV cache: KV GB/s + seqs/s",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16 math on fp8 (e4m3) KV",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "name": args.config,
+                   "num_seqs": w.num_seqs, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_size": w.head_size,
+                   "block_size": w.block_size, "num_blocks": w.num_blocks,
+                   "total_context_tokens": int(w.context_lens.sum()),
+                   "k_scale": ks, "v_scale": vs, "rotated_pool_copies": R,
+                   "seed": w.seed, "balanced_grid": steps[0].grid},
+        "accumulate": "f32", "kv_bytes_per_step": kvb,
+        "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "balanced_kernel (fp8 KV)",
+                     "kernel_ms": round(kms, 5), "algorithmic_bytes": kb},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        gpu = steps[(args.steps - 1) % R].out.cpu().numpy().astype(np.float64)
+        kc = (w.pool_init[0] & 0xFF).astype(np.uint8)
+        vc = (w.pool_init[1] & 0xFF).astype(np.uint8)
+        oracle.apply_phases_fp8(kc, vc, list(w.history), w.block_size, ks, vs)
+        try:
+            from threadpoolctl import threadpool_limits
+            ctx = threadpool_limits(1)
+        except Exception:                               # pragma: no cover
+            ctx = None
+        t0 = time.perf_counter()
+        done, ok = 0, True
+        while time.perf_counter() - t0 < 10.0 and done < w.num_seqs:
+            oracle.apply_phases_fp8(kc, vc, [w.step_copies, w.step_write], w.block_size,
+                                    ks, vs)
+            i = done
+            o = oracle.decode_fp8(w.query[i:i + 1], kc, vc, w.block_tables[i:i + 1],
+                                  w.context_lens[i:i + 1], w.scale, ks, vs)[0]
+            err = np.abs(gpu[i] - o)
+            ok &= bool(((err <= 2e-3) | (err <= 1e-2 * np.abs(o))).all())
+            done += 1
+        el = time.perf_counter() - t0
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+        rec["parity"] = {"seqs_checked": done, "within_tolerance": ok}
+        rec["cpu_baseline"] = {"value": round(done / el, 3), "unit": "seqs/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{done} sequence decodes over the fp8 pool (cache "
+                                         f"write of the step's tokens each), float64 "
+                                         f"NumPy, 1 BLAS thread"}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -387,12 +489,15 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="fused",
-                    choices=["fused", "balanced", "splitk", "single", "swap", "multi"],
+                    choices=["fused", "balanced", "splitk", "single", "swap", "multi",
+                             "fp8"],
                     help="fused: pa_decode_step (append + balanced decode, one kernel); "
                          "balanced/splitk/single: slot mapping + cache write + that decode; "
                          "swap: pa_swap_blocks of the batch's blocks to pinned host memory "
                          "and back (its own JSON line); multi: cache write of each "
-                         "sequence's query chunk + pa_decode_multi (the *_spec4 configs)")
+                         "sequence's query chunk + pa_decode_multi (the *_spec4 configs); "
+                         "fp8: the balanced decode over an e4m3 pool (fp8 cache write + "
+                         "pa_decode_balanced_fp8, its own JSON line)")
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--partition", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -417,6 +522,8 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     if args.mode == "swap":
         return swap_bench(args, w, dev)
+    if args.mode == "fp8":
+        return fp8_bench(args, w, dev)
     if args.mode == "multi" or "cu_seqlens_q" in w.info:
         if args.mode != "multi" or "cu_seqlens_q" not in w.info:
             print("--mode multi goes with a multi-token config (c2_spec4, c3_spec4)",

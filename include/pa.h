@@ -6,6 +6,7 @@
  *   [GUST] "PagedAttention：KV Cache的虚拟内存" (thegustafson.com "Paged
  *          Attention", bittide translation)
  *   [P5]   "PagedAttention原理（下）" (5688vip, vLLM推理框架全解析 04)
+ *   [CSDN] CSDN PageAttention tutorial (nanhubrain.csdn.net)
  *
  * Conventions shared by every entry point
  *   - Every pointer is a device pointer unless stated otherwise.  The caller
@@ -257,6 +258,50 @@ pa_status pa_decode_balanced(void* out, const void* query,
                              int32_t num_blocks, float scale, int32_t grid,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/*
+ * FP8 KV cache: a pool that stores one byte per element instead of two
+ * ([BOOK] §4.8 names a lower-precision KV cache as a way to fit more
+ * concurrent tokens in the same memory; [CSDN] part 3 (2), the KVBlock
+ * field table, lists FP16/FP8 block storage).  Layout as the fp16 pool
+ * with 1-byte elements: each half is [num_blocks, block_size, num_kv_heads,
+ * head_size] uint8, 16-byte aligned.  Each byte is an OCP FP8 E4M3 code
+ * (e4m3fn: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, 0x7f / 0xff NaN, largest finite 448).  The stored value of a
+ * code c is decode(c) * k_scale for K and decode(c) * v_scale for V, with
+ * one scale per tensor (per layer) chosen by the caller.  pa_copy_blocks and
+ * pa_swap_blocks move bytes, so they serve an fp8 pool given as an fp16 one
+ * with head_size / 2 (head_size / 2 must be a multiple of 8).
+ *
+ * pa_cache_write_fp8: as pa_cache_write, into an fp8 pool.  Element x
+ *   becomes the code nearest (ties to even) to clamp(float(x) * (1 / s),
+ *   -448, 448) where s = k_scale or v_scale and 1 / s is rounded to fp32
+ *   once on the host; NaN inputs give a NaN code.  Scales must be finite
+ *   and > 0 (else PA_ERR_SHAPE).
+ * pa_balanced_grid_fp8 / pa_decode_balanced_fp8: as pa_balanced_grid /
+ *   pa_decode_balanced over an fp8 pool (same workspace size and rules,
+ *   query and output fp16).  The result is attention over the dequantised
+ *   K and V (codes times their scales), within the fp16 path's tolerance
+ *   of that.  Scales as above.
+ */
+pa_status pa_cache_write_fp8(const void* key, const void* value,
+                             void* key_cache, void* value_cache,
+                             const int32_t* slot_mapping, int32_t num_tokens,
+                             int32_t num_blocks, int32_t block_size,
+                             int32_t num_kv_heads, int32_t head_size,
+                             float k_scale, float v_scale, hipStream_t stream);
+int32_t pa_balanced_grid_fp8(int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_size, int32_t block_size);
+pa_status pa_decode_balanced_fp8(void* out, const void* query,
+                                 const void* key_cache, const void* value_cache,
+                                 const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_size, int32_t block_size,
+                                 int32_t num_blocks, float scale, float k_scale,
+                                 float v_scale, int32_t grid, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
  * pa_decode_step -- one whole decode step in one kernel: for every

@@ -19,7 +19,8 @@ __all__ = [
     "pa_slot_mapping", "pa_cache_write", "pa_copy_blocks", "pa_swap_blocks", "pa_decode",
     "pa_splitk_workspace_size", "pa_decode_splitk", "pa_decode_reduce",
     "pa_balanced_grid", "pa_balanced_workspace_size", "pa_decode_balanced",
-    "pa_decode_step", "pa_multi_workspace_size", "pa_decode_multi", "STATUS",
+    "pa_decode_step", "pa_multi_workspace_size", "pa_decode_multi",
+    "pa_cache_write_fp8", "pa_balanced_grid_fp8", "pa_decode_balanced_fp8", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -69,6 +70,12 @@ def _load() -> ctypes.CDLL:
                                               i32, i32, i32, f32, i32, vp, sz, vp]),
         "pa_decode_step": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32,
                                           i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]),
+        "pa_cache_write_fp8": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                              f32, f32, vp]),
+        "pa_balanced_grid_fp8": (i32, [i32, i32, i32, i32]),
+        "pa_decode_balanced_fp8": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32,
+                                                  i32, i32, i32, i32, f32, f32, f32, i32,
+                                                  vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -117,6 +124,13 @@ def pa_balanced_grid(num_heads: int, num_kv_heads: int, head_size: int,
     """Workgroups of the balanced decode the current device holds at once
     (0 if unknown).  Initialises the HIP runtime on the current device."""
     return int(_lib().pa_balanced_grid(num_heads, num_kv_heads, head_size, block_size))
+
+
+def pa_balanced_grid_fp8(num_heads: int, num_kv_heads: int, head_size: int,
+                         block_size: int) -> int:
+    """As pa_balanced_grid, for the decode over an fp8 pool."""
+    return int(_lib().pa_balanced_grid_fp8(num_heads, num_kv_heads, head_size,
+                                           block_size))
 
 
 def pa_balanced_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int,
@@ -173,6 +187,14 @@ def _mapped(t, dtype, name: str, ndim: Optional[int] = None) -> int:
     return _dev(t, dtype, name, ndim)
 
 
+def _dev_fp8(t, name: str, ndim: int) -> int:
+    """An fp8 pool half: uint8 codes or torch.float8_e4m3fn (same bytes)."""
+    torch = _torch()
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        return _dev(t, torch.float8_e4m3fn, name, ndim)
+    return _dev(t, torch.uint8, name, ndim)
+
+
 def _check(func: str, status: int) -> None:
     if status != 0:
         raise PaError(func, status)
@@ -208,6 +230,23 @@ def pa_cache_write(key, value, key_cache, value_cache, slot_mapping,
         _dev(value_cache, torch.float16, "value_cache", 4),
         _dev(slot_mapping, torch.int32, "slot_mapping", 1),
         key.shape[0], nb, B, Hkv, D, _stream(stream)))
+
+
+def pa_cache_write_fp8(key, value, key_cache, value_cache, slot_mapping,
+                       k_scale: float, v_scale: float, stream=None) -> None:
+    """key/value fp16 [N, H_kv, D] -> e4m3 codes of x / scale (clamped to
+    +-448) in key_cache/value_cache (uint8 or float8_e4m3fn [nb, B, H_kv, D])
+    at slot_mapping (int32 [N])."""
+    torch = _torch()
+    nb, B, Hkv, D = key_cache.shape
+    if tuple(value_cache.shape) != (nb, B, Hkv, D) or key.shape[1:] != (Hkv, D) \
+            or value.shape != key.shape:
+        raise ValueError("pa_cache_write_fp8: inconsistent shapes")
+    _check("pa_cache_write_fp8", _lib().pa_cache_write_fp8(
+        _dev(key, torch.float16, "key", 3), _dev(value, torch.float16, "value", 3),
+        _dev_fp8(key_cache, "key_cache", 4), _dev_fp8(value_cache, "value_cache", 4),
+        _dev(slot_mapping, torch.int32, "slot_mapping", 1),
+        key.shape[0], nb, B, Hkv, D, float(k_scale), float(v_scale), _stream(stream)))
 
 
 def pa_copy_blocks(key_cache, value_cache, src, dst, stream=None) -> None:
@@ -350,6 +389,31 @@ def pa_decode_balanced(out, query, key_cache, value_cache, block_tables,
     _check("pa_decode_balanced", _lib().pa_decode_balanced(
         _dev(out, torch.float16, "out", 3), q, kc, vc, bt, M, cl, S, H, Hkv, D, B, nb,
         float(scale), int(grid), ws, nbytes, _stream(stream)))
+
+
+def pa_decode_balanced_fp8(out, query, key_cache, value_cache, block_tables,
+                           context_lens, scale: float, k_scale: float, v_scale: float,
+                           grid: int, workspace, stream=None) -> None:
+    """Balanced split-KV decode over an fp8 pool (uint8 or float8_e4m3fn
+    [nb, B, H_kv, D] halves; stored value = code * k_scale / v_scale)."""
+    torch = _torch()
+    S, H, D = query.shape
+    nb, B, Hkv, D2 = key_cache.shape
+    if D2 != D or tuple(value_cache.shape) != (nb, B, Hkv, D):
+        raise ValueError("decode: inconsistent head_size / cache shapes")
+    if block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("decode: block_tables / context_lens do not match query")
+    if tuple(out.shape) != (S, H, D):
+        raise ValueError("pa_decode_balanced_fp8: out shape")
+    ws = _dev(workspace, workspace.dtype, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("pa_decode_balanced_fp8", _lib().pa_decode_balanced_fp8(
+        _dev(out, torch.float16, "out", 3), _dev(query, torch.float16, "query", 3),
+        _dev_fp8(key_cache, "key_cache", 4), _dev_fp8(value_cache, "value_cache", 4),
+        _dev(block_tables, torch.int32, "block_tables", 2), block_tables.shape[1],
+        _dev(context_lens, torch.int32, "context_lens", 1), S, H, Hkv, D, B, nb,
+        float(scale), float(k_scale), float(v_scale), int(grid), ws, nbytes,
+        _stream(stream)))
 
 
 def pa_decode_step(out, query, key, value, key_cache, value_cache, block_tables,

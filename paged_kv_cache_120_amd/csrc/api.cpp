@@ -124,6 +124,31 @@ pa_status pa_cache_write(const void* key, const void* value, void* key_cache,
       (int64_t)num_blocks * block_size, (int)cpr, stream));
 }
 
+pa_status pa_cache_write_fp8(const void* key, const void* value,
+                             void* key_cache, void* value_cache,
+                             const int32_t* slot_mapping, int32_t num_tokens,
+                             int32_t num_blocks, int32_t block_size,
+                             int32_t num_kv_heads, int32_t head_size,
+                             float k_scale, float v_scale, hipStream_t stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || block_size <= 0 ||
+      num_kv_heads <= 0 || head_size <= 0 || head_size % 8 != 0 ||
+      !(isfinite(k_scale) && k_scale > 0.f) ||
+      !(isfinite(v_scale) && v_scale > 0.f))
+    return PA_ERR_SHAPE;
+  const int64_t cpr = (int64_t)num_kv_heads * head_size / 8;  // 8-element chunks
+  if (cpr >= (1ll << 31)) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return PA_ERR_NULL;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(slot_mapping, 4))
+    return PA_ERR_ALIGN;
+  return hip_status(pa::launch_cache_write_fp8(
+      key, value, key_cache, value_cache, slot_mapping, num_tokens,
+      (int64_t)num_blocks * block_size, (int)cpr, 1.f / k_scale, 1.f / v_scale,
+      stream));
+}
+
 pa_status pa_copy_blocks(void* key_cache, void* value_cache,
                          const int32_t* src, const int32_t* dst,
                          int32_t num_pairs, int32_t num_blocks,
@@ -383,6 +408,15 @@ int32_t pa_balanced_grid(int32_t num_heads, int32_t num_kv_heads,
   return pa::balanced_grid(head_size, block_size, num_heads / num_kv_heads);
 }
 
+int32_t pa_balanced_grid_fp8(int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_size, int32_t block_size) {
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+      !supported_head(head_size) || !supported_block(block_size) ||
+      !supported_group(num_heads / num_kv_heads))
+    return 0;
+  return pa::balanced_grid(head_size, block_size, num_heads / num_kv_heads, 1);
+}
+
 // [counters int32 x S*H_kv] padded to 16 bytes, then max, sum (fp32 [rows])
 // and out (fp32 [rows, D]) with rows = (grid + S*H_kv) * g.
 static size_t balanced_header_bytes(int32_t num_seqs, int32_t num_kv_heads) {
@@ -410,7 +444,9 @@ static pa_status balanced_impl(void* out, const void* query, void* key_cache,
                                int32_t num_blocks, float scale, int32_t grid,
                                void* workspace, size_t workspace_bytes,
                                const void* key, const void* value,
-                               int32_t* slot_mapping, hipStream_t stream) {
+                               int32_t* slot_mapping, hipStream_t stream,
+                               int elem_bytes = 2, float k_scale = 1.f,
+                               float v_scale = 1.f) {
   pa_status st = check_decode(query, key_cache, value_cache, block_tables,
                               max_blocks_per_seq, context_lens, num_seqs,
                               num_heads, num_kv_heads, head_size, block_size,
@@ -452,7 +488,10 @@ static pa_status balanced_impl(void* out, const void* query, void* key_cache,
   a.slot_out = slot_mapping;
   a.split = 1;
   a.scale = scale;
-  return hip_status(pa::launch_balanced(a, head_size, block_size, g, grid, stream));
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return hip_status(pa::launch_balanced(a, head_size, block_size, g, grid,
+                                        stream, elem_bytes));
 }
 
 pa_status pa_decode_balanced(void* out, const void* query, const void* key_cache,
@@ -471,6 +510,27 @@ pa_status pa_decode_balanced(void* out, const void* query, const void* key_cache
                        num_kv_heads, head_size, block_size, num_blocks, scale,
                        grid, workspace, workspace_bytes, nullptr, nullptr,
                        nullptr, stream);
+}
+
+pa_status pa_decode_balanced_fp8(void* out, const void* query,
+                                 const void* key_cache, const void* value_cache,
+                                 const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_size, int32_t block_size,
+                                 int32_t num_blocks, float scale, float k_scale,
+                                 float v_scale, int32_t grid, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  if (!(isfinite(k_scale) && k_scale > 0.f) ||
+      !(isfinite(v_scale) && v_scale > 0.f))
+    return PA_ERR_SHAPE;
+  return balanced_impl(out, query, const_cast<void*>(key_cache),
+                       const_cast<void*>(value_cache), block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                       num_kv_heads, head_size, block_size, num_blocks, scale,
+                       grid, workspace, workspace_bytes, nullptr, nullptr,
+                       nullptr, stream, 1, k_scale, v_scale);
 }
 
 pa_status pa_decode_step(void* out, const void* query, const void* key,

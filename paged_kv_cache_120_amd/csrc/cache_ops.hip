@@ -5,7 +5,8 @@
 // §4.3.2 / §4.5 (1) (reshape_and_cache: write each new token's K/V rows to
 // its slot); "PagedAttention：KV Cache的虚拟内存" copy-on-write paragraph and
 // "PagedAttention原理（下）" §4.3 (copy the shared block, then repoint) and
-// §4.4 (move the blocks of a paused request out to CPU memory and back).
+// §4.4 (move the blocks of a paused request out to CPU memory and back);
+// ch.4 §4.8 (a lower-precision KV cache: the fp8 cache write).
 //
 // All three move whole 16-byte chunks; consecutive lanes touch consecutive
 // chunks of a token row (cache write) or of a block (copy), so every wave
@@ -44,6 +45,56 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     for (int cc = blockIdx.x * 256 + threadIdx.x; cc < cpr; cc += gridDim.x * 256) {
       kc[dst + cc] = key[src + cc];
       vc[dst + cc] = value[src + cc];
+    }
+  }
+}
+
+// e4m3 code pair of x*inv and y*inv: the conversion rounds to nearest even
+// and gives NaN above the largest finite code, so values are clamped to
+// +-448 first (NaN inputs stay NaN).  Result in the low or high 16 bits of
+// `old` as `hi` says.
+__device__ __forceinline__ int fp8_pair(float x, float y, float inv, int old,
+                                        bool hi) {
+  float u = x * inv, v = y * inv;
+  u = u > 448.f ? 448.f : (u < -448.f ? -448.f : u);
+  v = v > 448.f ? 448.f : (v < -448.f ? -448.f : v);
+  return hi ? __builtin_amdgcn_cvt_pk_fp8_f32(u, v, old, true)
+            : __builtin_amdgcn_cvt_pk_fp8_f32(u, v, old, false);
+}
+
+__device__ __forceinline__ u32x2 f16x8_to_fp8x8(u32x4 h, float inv) {
+  const unsigned w[4] = {h.x, h.y, h.z, h.w};
+  float f[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f[2 * k] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[k] & 0xffffu));
+    f[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[k] >> 16));
+  }
+  int lo = fp8_pair(f[0], f[1], inv, 0, false);
+  lo = fp8_pair(f[2], f[3], inv, lo, true);
+  int hi = fp8_pair(f[4], f[5], inv, 0, false);
+  hi = fp8_pair(f[6], f[7], inv, hi, true);
+  u32x2 r;
+  r.x = (unsigned)lo;
+  r.y = (unsigned)hi;
+  return r;
+}
+
+// As cache_write_kernel, into an fp8 pool: each lane turns one 16-byte
+// chunk of 8 fp16 values into 8 one-byte codes.
+__global__ __launch_bounds__(256) void cache_write_fp8_kernel(
+    const u32x4* __restrict__ key, const u32x4* __restrict__ value,
+    u32x2* __restrict__ kc, u32x2* __restrict__ vc,
+    const int* __restrict__ slots, int n, long long num_slots, int cpr,
+    float inv_k, float inv_v) {
+  for (int j = blockIdx.y; j < n; j += gridDim.y) {
+    const int s = slots[j];
+    if (s < 0 || (long long)s >= num_slots) continue;
+    const size_t src = (size_t)j * cpr;
+    const size_t dst = (size_t)s * cpr;
+    for (int cc = blockIdx.x * 256 + threadIdx.x; cc < cpr; cc += gridDim.x * 256) {
+      kc[dst + cc] = f16x8_to_fp8x8(key[src + cc], inv_k);
+      vc[dst + cc] = f16x8_to_fp8x8(value[src + cc], inv_v);
     }
   }
 }
@@ -110,6 +161,18 @@ hipError_t launch_cache_write(const void* key, const void* value, void* kc,
   hipLaunchKernelGGL(cache_write_kernel, grid, dim3(256), 0, stream,
                      (const u32x4*)key, (const u32x4*)value, (u32x4*)kc,
                      (u32x4*)vc, slots, n, (long long)num_slots, cpr);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_write_fp8(const void* key, const void* value, void* kc,
+                                  void* vc, const int* slots, int n,
+                                  int64_t num_slots, int cpr, float inv_k,
+                                  float inv_v, hipStream_t stream) {
+  dim3 grid(clamp_grid((cpr + 255) / 256, 64), clamp_grid(n, 65535));
+  hipLaunchKernelGGL(cache_write_fp8_kernel, grid, dim3(256), 0, stream,
+                     (const u32x4*)key, (const u32x4*)value, (u32x2*)kc,
+                     (u32x2*)vc, slots, n, (long long)num_slots, cpr, inv_k,
+                     inv_v);
   return hipGetLastError();
 }
 

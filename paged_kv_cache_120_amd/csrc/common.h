@@ -8,6 +8,8 @@
 namespace pa {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -36,6 +38,27 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r,
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, PA_LOAD_AUX);
 }
 
+
+__device__ __forceinline__ u32x2 load8(__amdgpu_buffer_rsrc_t r,
+                                       uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, PA_LOAD_AUX);
+}
+
+// Eight OCP fp8 e4m3 codes (bytes in order) to eight fp16 values, exactly:
+// every e4m3 value (|x| <= 448, subnormals 2^-9 .. 7*2^-9) is an fp16
+// value.  (On gfx950 the fp8 conversions use the OCP formats.)
+__device__ __forceinline__ u32x4 fp8x8_to_f16x8(u32x2 w) {
+  // gfx950's scaled conversion turns two e4m3 codes (one 16-bit half of the
+  // word) into two fp16 values; with scale 1 it is exact, since every e4m3
+  // value is an fp16 number
+  const unsigned w0 = w.x, w1 = w.y;
+  u32x4 r;
+  r.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, false));
+  r.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, true));
+  r.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, false));
+  r.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, true));
+  return r;
+}
 
 // Cross-lane moves inside a 16-lane DPP row (all lanes must be active).
 template <int CTRL>

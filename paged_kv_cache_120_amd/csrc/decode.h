@@ -36,6 +36,9 @@ struct DecodeArgs {
   const int* cu_seqlens_q;
   int q_tiles;
   int num_q_tokens;
+  // fp8 pools: dequantisation scales (value = code * scale)
+  float k_scale;
+  float v_scale;
 };
 
 
@@ -61,11 +64,13 @@ hipError_t launch_multi(const DecodeArgs& a, int head_size, int block_size,
                         int group, dim3 grid, hipStream_t stream);
 hipError_t launch_multi_reduce(const ReduceArgs& a, int head_size,
                                int num_q_tokens, hipStream_t stream);
+// elem_bytes: 2 for an fp16 pool, 1 for an fp8 (e4m3) pool
 hipError_t launch_balanced(const DecodeArgs& a, int head_size, int block_size,
-                           int group, int grid, hipStream_t stream);
+                           int group, int grid, hipStream_t stream,
+                           int elem_bytes = 2);
 // workgroups of the balanced kernel resident at once on the current device
 // (0 if it cannot be determined)
-int balanced_grid(int head_size, int block_size, int group);
+int balanced_grid(int head_size, int block_size, int group, int elem_bytes = 2);
 
 // cache operations
 hipError_t launch_slot_mapping(int* out, const int* block_tables, int M,
@@ -75,6 +80,12 @@ hipError_t launch_cache_write(const void* key, const void* value, void* kc,
                               void* vc, const int* slots, int n,
                               int64_t num_slots, int chunks_per_row,
                               hipStream_t stream);
+// fp16 rows -> e4m3 codes of x / scale (clamped to the finite range)
+hipError_t launch_cache_write_fp8(const void* key, const void* value, void* kc,
+                                  void* vc, const int* slots, int n,
+                                  int64_t num_slots, int chunks_per_row,
+                                  float inv_k_scale, float inv_v_scale,
+                                  hipStream_t stream);
 hipError_t launch_copy_blocks(void* kc, void* vc, const int* src,
                               const int* dst, int pairs, int num_blocks,
                               int64_t chunks_per_block, hipStream_t stream);

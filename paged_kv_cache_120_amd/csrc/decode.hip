@@ -131,6 +131,25 @@ __device__ __forceinline__ void merge_waves(Smem& sm, Sink& sink) {
   __syncthreads();    // LDS free for the next range
 }
 
+// One load of 8 cached elements: 16 bytes of fp16 (EB = 2) or 8 bytes of
+// e4m3 codes (EB = 1), kept in that form until used, then widened to fp16.
+template <int EB>
+struct KvLoad {
+  using type = u32x4;
+  __device__ static type load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return load16(r, off);
+  }
+};
+template <>
+struct KvLoad<1> {
+  using type = u32x2;
+  __device__ static type load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return load8(r, off);
+  }
+};
+__device__ __forceinline__ u32x4 widen(u32x4 v) { return v; }
+__device__ __forceinline__ u32x4 widen(u32x2 v) { return fp8x8_to_f16x8(v); }
+
 // ---------------------------------------------------------------------------
 // Vector-ALU range body
 // ---------------------------------------------------------------------------
@@ -143,7 +162,7 @@ __device__ __forceinline__ void merge_waves(Smem& sm, Sink& sink) {
 // product is reduced across the row with four DPP adds (bitwise identical in
 // every lane) and everything else is lane-local until the end, where row
 // groups merge with cross-lane shuffles and waves through LDS.
-template <int D, int B, int G, int NJ>
+template <int D, int B, int G, int NJ, int EB = 2>
 struct ValuPath {
   static constexpr int LPR = D / 8;       // lanes per token row
   static constexpr int RPI = 64 / LPR;    // token rows per wave load
@@ -170,7 +189,9 @@ struct ValuPath {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane / LPR;
     const int c = lane % LPR;
-    if (last >= 0) append_token<D, B>(a, kvh, seq, last);
+    if constexpr (EB == 2) {
+      if (last >= 0) append_token<D, B>(a, kvh, seq, last);
+    }
 
     u32x4 qv[G];
 #pragma unroll
@@ -181,11 +202,12 @@ struct ValuPath {
     BlockWindow bw;
     bw.init(a.block_tables + (size_t)seq * a.max_blocks_per_seq, t0 / B,
             (t1 + B - 1) / B, lane);
-    const uint32_t row_stride = (uint32_t)a.num_kv_heads * D * 2;
+    const uint32_t row_stride = (uint32_t)a.num_kv_heads * D * EB;
     const uint64_t blk_bytes = (uint64_t)B * row_stride;
-    const char* kbase = a.key_cache + (size_t)kvh * D * 2;
-    const char* vbase = a.value_cache + (size_t)kvh * D * 2;
-    const float sl2 = a.scale * kLog2e;
+    const char* kbase = a.key_cache + (size_t)kvh * D * EB;
+    const char* vbase = a.value_cache + (size_t)kvh * D * EB;
+    // fp8 pools: K's scale folds into the score scale, V's into the output
+    const float sl2 = a.scale * kLog2e * (EB == 1 ? a.k_scale : 1.f);
 
     // m: the reference the state is kept relative to; mt: the true max
     float m[G], mt[G], l[G], acc[G][8];
@@ -199,39 +221,44 @@ struct ValuPath {
     }
 
     // loads of one batch into (kk, vv), including the appended token's row
-    auto issue = [&](int base, u32x4 (&kk)[NJ], u32x4 (&vv)[NJ]) {
+    using Raw = typename KvLoad<EB>::type;
+    auto issue = [&](int base, Raw (&kk)[NJ], Raw (&vv)[NJ]) {
       bw.cover(base / B, (base + TB - 1) / B, lane);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int tok0 = base + j * RPI;   // wave-uniform
         const int lb = tok0 / B;
         const int blk = bw.block(lb);
-        const uint32_t off = (uint32_t)(tok0 % B + r) * row_stride + c * 16;
-        kk[j] = load16(block_rsrc<B>(kbase, blk, lb, t1, row_stride, blk_bytes,
-                                     a.num_blocks), off);
-        vv[j] = load16(block_rsrc<B>(vbase, blk, lb, t1, row_stride, blk_bytes,
-                                     a.num_blocks), off);
+        const uint32_t off = (uint32_t)(tok0 % B + r) * row_stride + c * 8 * EB;
+        const __amdgpu_buffer_rsrc_t rk = block_rsrc<B>(
+            kbase, blk, lb, t1, row_stride, blk_bytes, a.num_blocks);
+        const __amdgpu_buffer_rsrc_t rv = block_rsrc<B>(
+            vbase, blk, lb, t1, row_stride, blk_bytes, a.num_blocks);
+        kk[j] = KvLoad<EB>::load(rk, off);
+        vv[j] = KvLoad<EB>::load(rv, off);
       }
-      if (last >= 0 && base + TB > last) {     // the appended token's row
-        const size_t src = ((size_t)seq * a.num_kv_heads + kvh) * D + c * 8;
+      if constexpr (EB == 2) {
+        if (last >= 0 && base + TB > last) {   // the appended row
+          const size_t src = ((size_t)seq * a.num_kv_heads + kvh) * D + c * 8;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          if (base + j * RPI + r == last) {
-            kk[j] = *reinterpret_cast<const u32x4*>(a.new_key + src);
-            vv[j] = *reinterpret_cast<const u32x4*>(a.new_value + src);
+          for (int j = 0; j < NJ; ++j) {
+            if (base + j * RPI + r == last) {
+              kk[j] = *reinterpret_cast<const u32x4*>(a.new_key + src);
+              vv[j] = *reinterpret_cast<const u32x4*>(a.new_value + src);
+            }
           }
         }
       }
     };
     // scores, softmax state and P.V of one loaded batch
-    auto consume = [&](int base, const u32x4 (&kk)[NJ], const u32x4 (&vv)[NJ]) {
+    auto consume = [&](int base, const Raw (&kk)[NJ], const Raw (&vv)[NJ]) {
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
         float s[NJ];
         float bm = -INFINITY;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          const float d = group_sum<LPR>(dot8(qv[gi], kk[j]));
+          const float d = group_sum<LPR>(dot8(qv[gi], widen(kk[j])));
           const int tok = base + j * RPI + r;
           s[j] = tok < t1 ? d * sl2 : -INFINITY;
           bm = fmaxf(bm, s[j]);
@@ -260,23 +287,25 @@ struct ValuPath {
           float x = acc[gi][e];
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
-            x = __builtin_fmaf(s[j], half_at(vv[j], e), x);
+            x = __builtin_fmaf(s[j], half_at(widen(vv[j]), e), x);
           acc[gi][e] = x;
         }
       }
     };
     for (int base = t0 + wave * TB; base < t1; base += kWaves * TB) {
-      u32x4 kk[NJ], vv[NJ];
+      Raw kk[NJ], vv[NJ];
       issue(base, kk, vv);
       consume(base, kk, vv);
     }
-    // state relative to the true running max from here on
+    // state relative to the true running max from here on (and in V's
+    // units for an fp8 pool)
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
       const float f = mt[gi] == -INFINITY ? 1.f : fast_exp2(m[gi] - mt[gi]);
       l[gi] *= f;
+      const float fv = EB == 1 ? f * a.v_scale : f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[gi][e] *= f;
+      for (int e = 0; e < 8; ++e) acc[gi][e] *= fv;
       m[gi] = mt[gi];
     }
 
@@ -338,7 +367,7 @@ struct ValuPath {
 // Every per-head quantity (running max, sum, rescale factor) lives in the
 // lanes owning that head's column, and O^T's rows are channels, so the
 // rescale is lane-local.
-template <int D, int B, int G>
+template <int D, int B, int G, int EB = 2>
 struct MfmaPath {
   static constexpr int MT = D == 128 ? 1 : 2;   // 16-token tiles per batch
   static constexpr int TB = 16 * MT;
@@ -378,7 +407,9 @@ struct MfmaPath {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;                  // token row (A) / column (B, D)
     const int grp = lane >> 4;                  // lane group 0..3
-    if (last >= 0) append_token<D, B>(a, kvh, seq, last);
+    if constexpr (EB == 2) {
+      if (last >= 0) append_token<D, B>(a, kvh, seq, last);
+    }
 
     f16x8 qb[KK];
 #pragma unroll
@@ -392,11 +423,11 @@ struct MfmaPath {
     BlockWindow bw;
     bw.init(a.block_tables + (size_t)seq * a.max_blocks_per_seq, t0 / B,
             (t1 + B - 1) / B, lane);
-    const uint32_t row_stride = (uint32_t)a.num_kv_heads * D * 2;
+    const uint32_t row_stride = (uint32_t)a.num_kv_heads * D * EB;
     const uint64_t blk_bytes = (uint64_t)B * row_stride;
-    const char* kbase = a.key_cache + (size_t)kvh * D * 2;
-    const char* vbase = a.value_cache + (size_t)kvh * D * 2;
-    const float sl2 = a.scale * kLog2e;
+    const char* kbase = a.key_cache + (size_t)kvh * D * EB;
+    const char* vbase = a.value_cache + (size_t)kvh * D * EB;
+    const float sl2 = a.scale * kLog2e * (EB == 1 ? a.k_scale : 1.f);
 
     float m = -INFINITY;                        // reference of head `col`
     float mt = -INFINITY;                       // its true running max
@@ -408,7 +439,7 @@ struct MfmaPath {
 
     for (int base = t0 + wave * TB; base < t1; base += kWaves * TB) {
       bw.cover(base / B, (base + TB - 1) / B, lane);
-      u32x4 kr[MT][KK], vr[MT][KK];
+      typename KvLoad<EB>::type kr[MT][KK], vr[MT][KK];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int tile0 = base + mt * 16;       // wave-uniform
@@ -418,23 +449,26 @@ struct MfmaPath {
             kbase, blk, lb, t1, row_stride, blk_bytes, a.num_blocks);
         const __amdgpu_buffer_rsrc_t rv = block_rsrc<B>(
             vbase, blk, lb, t1, row_stride, blk_bytes, a.num_blocks);
-        const uint32_t off = (uint32_t)(tile0 % B + col) * row_stride + grp * 16;
+        const uint32_t off =
+            (uint32_t)(tile0 % B + col) * row_stride + grp * 8 * EB;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          kr[mt][kk] = load16(rk, off + kk * 64);
-          vr[mt][kk] = load16(rv, off + kk * 64);
+          kr[mt][kk] = KvLoad<EB>::load(rk, off + kk * 32 * EB);
+          vr[mt][kk] = KvLoad<EB>::load(rv, off + kk * 32 * EB);
         }
       }
-      if (last >= 0 && base + TB > last) {     // the appended token's row
+      if constexpr (EB == 2) {
+        if (last >= 0 && base + TB > last) {   // the appended row
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          if (base + mt * 16 + col == last) {
-            const size_t src =
-                ((size_t)seq * a.num_kv_heads + kvh) * D + grp * 8;
+          for (int mt = 0; mt < MT; ++mt) {
+            if (base + mt * 16 + col == last) {
+              const size_t src =
+                  ((size_t)seq * a.num_kv_heads + kvh) * D + grp * 8;
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-              kr[mt][kk] = *reinterpret_cast<const u32x4*>(a.new_key + src + kk * 32);
-              vr[mt][kk] = *reinterpret_cast<const u32x4*>(a.new_value + src + kk * 32);
+              for (int kk = 0; kk < KK; ++kk) {
+                kr[mt][kk] = *reinterpret_cast<const u32x4*>(a.new_key + src + kk * 32);
+                vr[mt][kk] = *reinterpret_cast<const u32x4*>(a.new_value + src + kk * 32);
+              }
             }
           }
         }
@@ -448,7 +482,7 @@ struct MfmaPath {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              __builtin_bit_cast(f16x8, kr[mt][kk]), qb[kk], acc, 0, 0, 0);
+              __builtin_bit_cast(f16x8, widen(kr[mt][kk])), qb[kk], acc, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = base + mt * 16 + grp * 4 + i;
@@ -462,7 +496,7 @@ struct MfmaPath {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           _Float16* dst = vw + (mt * 16 + col) * VS + kk * 32 + grp * 8;
-          const u32x4 v = vr[mt][kk];
+          const u32x4 v = widen(vr[mt][kk]);
           reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
           reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
         }
@@ -517,8 +551,9 @@ struct MfmaPath {
     {
       const float f = mt == -INFINITY ? 1.f : fast_exp2(m - mt);
       l *= f;
+      const float fv = EB == 1 ? f * a.v_scale : f;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= f;
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= fv;
       m = mt;
     }
     l += __shfl_xor(l, 16);
@@ -943,72 +978,97 @@ __attribute__((amdgpu_waves_per_eu(Path::kMinWaves))) void balanced_kernel(
 // Dispatch
 // ---------------------------------------------------------------------------
 
-// Loads in flight per wave batch (16-byte K and V loads per lane) for the
-// vector-ALU body; measured on MI355X: 8 is best for groups of 1-2, 2 for a
-// group of 4 (fewer registers, four waves per SIMD).  A group of 8 runs on
-// the matrix cores; for a group of 4 the matrix-core body measured slower
-// than the vector one (3.7-3.9 vs 4.0-4.3 TB/s on the GQA-4 workload).
-template <int D, int B, int G>
+// Loads in flight per wave batch for the vector-ALU body (NJ); measured on
+// MI355X.  fp16 pools: 8 is best for groups of 1-2, 2 for a group of 4 (fewer
+// registers, four waves per SIMD).  fp8 pools move half the bytes per load,
+// so groups of 1 and 4 keep twice the loads in flight (16 and 4; a group of
+// 4 runs 10% faster); a group of 2 stays at 8 (16 would halve its waves).
+// A group of 8 runs on the matrix cores; for a group of 4 the matrix-core
+// body measured slower than the vector one (fp16: 3.7-3.9 vs 4.0-4.3 TB/s
+// on the GQA-4 workload; fp8: 82 vs 65 us).
+template <int G, int EB>
+constexpr int valu_loads() {
+  return EB == 2 ? (G >= 4 ? 2 : 8) : (G == 4 ? 4 : G == 2 ? 8 : 16);
+}
+template <int D, int B, int G, int EB = 2>
 struct PathFor {
-  using type = ValuPath<D, B, G, (G >= 4 ? 2 : 8)>;
+  using type = ValuPath<D, B, G, valu_loads<G, EB>(), EB>;
 };
-template <int D, int B>
-struct PathFor<D, B, 8> {
-  using type = MfmaPath<D, B, 8>;
+template <int D, int B, int EB>
+struct PathFor<D, B, 8, EB> {
+  using type = MfmaPath<D, B, 8, EB>;
 };
 
 enum class Op { kPartition, kBalanced, kOccupancy, kMulti };
 
-template <int D, int B, int G>
+// EB: bytes per cached element (2: fp16 pool, 1: fp8 e4m3 pool).  The fp8
+// pool has the balanced kernel only.
+template <int D, int B, int G, int EB>
 static hipError_t run_op(Op op, const DecodeArgs* a, dim3 grid,
                          hipStream_t st, int* occ) {
-  using P = typename PathFor<D, B, G>::type;
+  using P = typename PathFor<D, B, G, EB>::type;
   switch (op) {
-    case Op::kPartition:
-      hipLaunchKernelGGL((partition_kernel<P, D, B, G>), grid, dim3(kThreads), 0, st, *a);
-      return hipGetLastError();
     case Op::kBalanced:
       hipLaunchKernelGGL((balanced_kernel<P, D, B, G>), grid, dim3(kThreads), 0, st, *a);
       return hipGetLastError();
     case Op::kOccupancy:
       return hipOccupancyMaxActiveBlocksPerMultiprocessor(
           occ, reinterpret_cast<const void*>(&balanced_kernel<P, D, B, G>), kThreads, 0);
-    case Op::kMulti:
-      hipLaunchKernelGGL((multi_kernel<D, B, G>), grid, dim3(kThreads), 0, st, *a);
-      return hipGetLastError();
+    default:
+      break;
+  }
+  if constexpr (EB == 2) {
+    switch (op) {
+      case Op::kPartition:
+        hipLaunchKernelGGL((partition_kernel<P, D, B, G>), grid, dim3(kThreads), 0, st, *a);
+        return hipGetLastError();
+      case Op::kMulti:
+        hipLaunchKernelGGL((multi_kernel<D, B, G>), grid, dim3(kThreads), 0, st, *a);
+        return hipGetLastError();
+      default:
+        break;
+    }
   }
   return hipErrorInvalidValue;
 }
 
-template <int D, int B>
+template <int D, int B, int EB>
 static hipError_t dispatch_db(Op op, int G, const DecodeArgs* a, dim3 grid,
                               hipStream_t st, int* occ) {
   switch (G) {
-    case 1: return run_op<D, B, 1>(op, a, grid, st, occ);
-    case 2: return run_op<D, B, 2>(op, a, grid, st, occ);
-    case 4: return run_op<D, B, 4>(op, a, grid, st, occ);
-    case 8: return run_op<D, B, 8>(op, a, grid, st, occ);
+    case 1: return run_op<D, B, 1, EB>(op, a, grid, st, occ);
+    case 2: return run_op<D, B, 2, EB>(op, a, grid, st, occ);
+    case 4: return run_op<D, B, 4, EB>(op, a, grid, st, occ);
+    case 8: return run_op<D, B, 8, EB>(op, a, grid, st, occ);
   }
   return hipErrorInvalidValue;
 }
 
-template <int D>
+template <int D, int EB>
 static hipError_t dispatch_d(Op op, int B, int G, const DecodeArgs* a, dim3 grid,
                              hipStream_t st, int* occ) {
   switch (B) {
-    case 16: return dispatch_db<D, 16>(op, G, a, grid, st, occ);
-    case 32: return dispatch_db<D, 32>(op, G, a, grid, st, occ);
-    case 64: return dispatch_db<D, 64>(op, G, a, grid, st, occ);
+    case 16: return dispatch_db<D, 16, EB>(op, G, a, grid, st, occ);
+    case 32: return dispatch_db<D, 32, EB>(op, G, a, grid, st, occ);
+    case 64: return dispatch_db<D, 64, EB>(op, G, a, grid, st, occ);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int EB>
+static hipError_t dispatch_eb(Op op, int D, int B, int G, const DecodeArgs* a,
+                              dim3 grid, hipStream_t st, int* occ) {
+  switch (D) {
+    case 64: return dispatch_d<64, EB>(op, B, G, a, grid, st, occ);
+    case 128: return dispatch_d<128, EB>(op, B, G, a, grid, st, occ);
   }
   return hipErrorInvalidValue;
 }
 
 static hipError_t dispatch(Op op, int D, int B, int G, const DecodeArgs* a,
-                           dim3 grid, hipStream_t st, int* occ) {
-  switch (D) {
-    case 64: return dispatch_d<64>(op, B, G, a, grid, st, occ);
-    case 128: return dispatch_d<128>(op, B, G, a, grid, st, occ);
-  }
+                           dim3 grid, hipStream_t st, int* occ, int eb = 2) {
+  if (eb == 1) return dispatch_eb<1>(op, D, B, G, a, grid, st, occ);
+  if (eb == 2) return dispatch_eb<2>(op, D, B, G, a, grid, st, occ);
   return hipErrorInvalidValue;
 }
 
@@ -1019,12 +1079,12 @@ hipError_t launch_decode(const DecodeArgs& a, int head_size, int block_size,
 }
 
 hipError_t launch_balanced(const DecodeArgs& a, int head_size, int block_size,
-                           int group, int grid, hipStream_t stream) {
+                           int group, int grid, hipStream_t stream, int elem_bytes) {
   return dispatch(Op::kBalanced, head_size, block_size, group, &a,
-                  dim3(grid), stream, nullptr);
+                  dim3(grid), stream, nullptr, elem_bytes);
 }
 
-int balanced_grid(int head_size, int block_size, int group) {
+int balanced_grid(int head_size, int block_size, int group, int elem_bytes) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   int cus = 0;
@@ -1033,7 +1093,7 @@ int balanced_grid(int head_size, int block_size, int group) {
     return 0;
   int per_cu = 0;
   if (dispatch(Op::kOccupancy, head_size, block_size, group, nullptr, dim3(1),
-               nullptr, &per_cu) != hipSuccess)
+               nullptr, &per_cu, elem_bytes) != hipSuccess)
     return 0;
   return per_cu > 0 ? per_cu * cus : 0;
 }

@@ -6,7 +6,9 @@ tokens, the cache write, then decode -- single-pass (``pa_decode``), split
 (``pa_decode_balanced``); or, mode "fused", copies then ``pa_decode_step``
 (slot mapping, cache write and balanced decode in one kernel).  With several
 query tokens per sequence (``upload_multi``), ``multi_step`` runs
-``pa_decode_multi`` after the same writes.  Inputs are plain arrays (a
+``pa_decode_multi`` after the same writes.  With an fp8 pool
+(``upload_fp8``), ``fp8_step`` runs the copies, ``pa_cache_write_fp8`` and
+``pa_decode_balanced_fp8``.  Inputs are plain arrays (a
 workload object with the attributes used below); this module only uploads
 them and calls the binding, so every step runs in the library's kernels.
 """
@@ -18,8 +20,9 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-from . import (pa_balanced_grid, pa_balanced_workspace_size, pa_cache_write,
-               pa_copy_blocks, pa_decode, pa_decode_balanced, pa_decode_multi,
+from . import (pa_balanced_grid, pa_balanced_grid_fp8, pa_balanced_workspace_size,
+               pa_cache_write, pa_cache_write_fp8, pa_copy_blocks, pa_decode,
+               pa_decode_balanced, pa_decode_balanced_fp8, pa_decode_multi,
                pa_decode_reduce, pa_decode_splitk, pa_decode_step,
                pa_multi_workspace_size, pa_slot_mapping, pa_splitk_workspace_size)
 
@@ -206,3 +209,69 @@ def split_views(step: DeviceStep, S: int, H: int, D: int, M: int, B: int, P: int
 __all__: List[str] = ["DeviceStep", "upload", "apply_history", "write_step",
                       "decode_step", "fused_step", "full_step", "run_phase",
                       "split_views"]
+
+
+# ---------------------------------------------------------------------------
+# fp8 (e4m3) pool
+# ---------------------------------------------------------------------------
+
+def _byte_view(half: torch.Tensor) -> torch.Tensor:
+    """An fp8 pool half [nb, B, H_kv, D] uint8 seen as fp16 [nb, B, H_kv, D/2]:
+    block copies move bytes, so the fp16 copy kernel serves both pools."""
+    return half.view(torch.float16)
+
+
+def run_phase_fp8(ph, pool, block_size: int, k_scale: float, v_scale: float,
+                  stream=None) -> None:
+    if ph is None:
+        return
+    if isinstance(ph, DevCopy):
+        pa_copy_blocks(_byte_view(pool[0]), _byte_view(pool[1]), ph.src, ph.dst,
+                       stream=stream)
+        return
+    pa_slot_mapping(ph.slots, ph.table, ph.seq, ph.pos, block_size, stream=stream)
+    pa_cache_write_fp8(ph.key, ph.value, pool[0], pool[1], ph.slots, k_scale, v_scale,
+                       stream=stream)
+
+
+def upload_fp8(w, k_scale: float, v_scale: float, device: str = "cuda") -> DeviceStep:
+    """As upload, with a uint8 pool of e4m3 codes whose initial garbage is
+    the low byte of the fp16 garbage; the balanced grid and workspace are
+    the fp8 decode's."""
+    dev = torch.device(device)
+    pool = _t((w.pool_init & 0xFF).astype(np.uint8), dev)
+    st = upload(w, device, pool=torch.empty(0, dtype=torch.float16, device=dev))
+    st.pool = pool
+    S, H, D = w.query.shape
+    with torch.cuda.device(dev):
+        st.grid = pa_balanced_grid_fp8(H, w.num_kv_heads, D, w.block_size)
+    if st.grid <= 0:
+        raise RuntimeError("pa_balanced_grid_fp8 failed")
+    bws = pa_balanced_workspace_size(S, H, w.num_kv_heads, D, st.grid)
+    st.bal_workspace = torch.zeros(max(bws, 16), dtype=torch.uint8, device=dev)
+    st.k_scale, st.v_scale = float(k_scale), float(v_scale)
+    return st
+
+
+def apply_history_fp8(w, step: DeviceStep, stream=None) -> None:
+    for ph in w.history:
+        d = _dev_phase(ph, step.pool.device)
+        run_phase_fp8(d, step.pool, w.block_size, step.k_scale, step.v_scale,
+                      stream=stream)
+        del d
+
+
+def fp8_decode(step: DeviceStep, stream=None) -> None:
+    pa_decode_balanced_fp8(step.out, step.query, step.key_cache, step.value_cache,
+                           step.block_tables, step.context_lens, step.scale,
+                           step.k_scale, step.v_scale, step.grid, step.bal_workspace,
+                           stream=stream)
+
+
+def fp8_step(step: DeviceStep, stream=None) -> None:
+    """COW copies, slot mapping, fp8 cache write, then the fp8 decode."""
+    run_phase_fp8(step.copies, step.pool, step.block_size, step.k_scale, step.v_scale,
+                  stream=stream)
+    run_phase_fp8(step.write, step.pool, step.block_size, step.k_scale, step.v_scale,
+                  stream=stream)
+    fp8_decode(step, stream=stream)

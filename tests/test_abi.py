@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
     syms = header_symbols()
     for name in ["pa_cache_write", "pa_decode", "pa_decode_splitk", "pa_decode_reduce",
                  "pa_splitk_workspace_size", "pa_status_str", "pa_kv_cache_shape",
-                 "pa_slot_mapping", "pa_copy_blocks", "pa_swap_blocks"]:
+                 "pa_slot_mapping", "pa_copy_blocks", "pa_swap_blocks",
+                 "pa_cache_write_fp8", "pa_balanced_grid_fp8", "pa_decode_balanced_fp8"]:
         assert name in syms
 
 
@@ -126,6 +127,33 @@ def test_cache_op_validation(pa):
     assert sw(FAKE, FAKE, 10, FAKE, FAKE, 20, FAKE, FAKE, -1, 16, 2, 128, None) == 2
     assert sw(FAKE, FAKE, 10, FAKE, FAKE, 20, FAKE, FAKE, 3, 16, 2, 100, None) == 2
     assert sw(FAKE, FAKE, 10, FAKE + 8, FAKE, 20, FAKE, FAKE, 3, 16, 2, 128, None) == 4
+
+
+def test_fp8_validation(pa):
+    L = pa.lib
+    cw = L.pa_cache_write_fp8
+    assert cw(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 10, 16, 2, 128, 0.1, 0.1, None) == 0
+    assert cw(FAKE, None, FAKE, FAKE, FAKE, 3, 10, 16, 2, 128, 0.1, 0.1, None) == 1
+    assert cw(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 10, 16, 2, 128, 0.0, 0.1, None) == 2
+    assert cw(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 10, 16, 2, 128, 0.1, float("inf"), None) == 2
+    assert cw(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 10, 16, 2, 128, float("nan"), 0.1, None) == 2
+    assert cw(FAKE, FAKE, FAKE + 8, FAKE, FAKE, 3, 10, 16, 2, 128, 0.1, 0.1, None) == 4
+    assert L.pa_balanced_grid_fp8(8, 2, 96, 16) == 0
+    assert L.pa_balanced_grid_fp8(24, 2, 128, 16) == 0
+    need = pa.pa_balanced_workspace_size(2, 8, 2, 128, 64)
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 8, 2, 128, 16, 10, 0.1]
+    d = L.pa_decode_balanced_fp8
+    assert d(*a, -1.0, 0.5, 64, FAKE, need, None) == 2
+    assert d(*a, 0.5, 0.0, 64, FAKE, need, None) == 2
+    assert d(*a, 0.5, 0.5, 0, FAKE, need, None) == 2
+    assert d(*a, 0.5, 0.5, 64, FAKE, need - 1, None) == 5
+    assert d(*a, 0.5, 0.5, 64, None, need, None) == 1
+    b = list(a)
+    b[10] = 96
+    assert d(*b, 0.5, 0.5, 64, FAKE, need, None) == 3
+    b = list(a)
+    b[7] = 0
+    assert d(*b, 0.5, 0.5, 64, FAKE, need, None) == 0                # empty batch
 
 
 def test_binding_rejects_host_tensors(pa):
