@@ -26,22 +26,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
                                            (int)bytes, kBufferRsrcWord3);
 }
 
-// K/V rows are read exactly once per decode step, so they are fetched with
-// the non-temporal policy (aux bit 1 -> `nt`): on MI355X this lifts a paged
-// 256-byte-segment read stream from ~6.0 to ~6.8 TB/s.
-#ifndef PA_LOAD_AUX
-#define PA_LOAD_AUX 2
-#endif
+// Cache policy of K/V loads (the buffer instruction's aux bits).  Rows are
+// read once per decode step, so a load that fetches whole 128-byte lines uses
+// the non-temporal policy (kLoadNt, aux bit 1 -> `nt`): on MI355X this lifts
+// a paged 256-byte-segment read stream from ~6.0 to ~6.8 TB/s.  A load that
+// fetches half lines (the matrix-core operand layout: 64 bytes of each of 16
+// rows) uses the default policy (kLoadCached), so the second half of each
+// line, loaded by the next instruction, hits in the vector L1 (c5: +5%).
+constexpr int kLoadNt = 2;
+constexpr int kLoadCached = 0;
 
+template <int AUX = kLoadNt>
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r,
                                         uint32_t voff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, PA_LOAD_AUX);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, AUX);
 }
 
-
+template <int AUX = kLoadNt>
 __device__ __forceinline__ u32x2 load8(__amdgpu_buffer_rsrc_t r,
                                        uint32_t voff) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, PA_LOAD_AUX);
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, AUX);
 }
 
 // Eight OCP fp8 e4m3 codes (bytes in order) to eight fp16 values, exactly:
@@ -72,6 +76,7 @@ constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;
 constexpr int kRowMirror = 0x140;
+constexpr int kRowRor8 = 0x128;      // row_ror:8 = lane ^ 8 within a row of 16
 
 // Sum over aligned groups of LANES (8 or 16) lanes; every lane of a group
 // ends with the bitwise-identical total (each step adds two equal-order

@@ -28,6 +28,8 @@
 // byte is used once per step.  Block ids for a 64-block window come from one
 // vector load per wave and are broadcast with v_readlane.  Scores are kept in
 // base-2 units (x log2 e) so every exponential is one v_exp_f32.
+#include <type_traits>
+
 #include "common.h"
 #include "decode.h"
 
@@ -133,18 +135,18 @@ __device__ __forceinline__ void merge_waves(Smem& sm, Sink& sink) {
 
 // One load of 8 cached elements: 16 bytes of fp16 (EB = 2) or 8 bytes of
 // e4m3 codes (EB = 1), kept in that form until used, then widened to fp16.
-template <int EB>
+template <int EB, int AUX = kLoadNt>
 struct KvLoad {
   using type = u32x4;
   __device__ static type load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return load16(r, off);
+    return load16<AUX>(r, off);
   }
 };
-template <>
-struct KvLoad<1> {
+template <int AUX>
+struct KvLoad<1, AUX> {
   using type = u32x2;
   __device__ static type load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return load8(r, off);
+    return load8<AUX>(r, off);
   }
 };
 __device__ __forceinline__ u32x4 widen(u32x4 v) { return v; }
@@ -347,10 +349,11 @@ struct ValuPath {
 };
 
 // ---------------------------------------------------------------------------
-// Matrix-core range body (g = 8)
+// Matrix-core range bodies
 // ---------------------------------------------------------------------------
 //
-// Per wave, a batch is MT tiles of 16 tokens (one at D = 128, which keeps
+// MfmaPath: 16 MFMA columns given by the caller (the multi-token kernel's
+// (query token, head) pairs).  Per wave, a batch is MT tiles of 16 tokens (one at D = 128, which keeps
 // the kernel within 128 VGPRs: four waves per SIMD).  Two MFMA shapes:
 //   S^T (16 tokens x 16 heads) = K x Q^T with the 16x16x32 fp16 MFMA (lane l
 //        holds A[l%16][8(l/16)+i], B[8(l/16)+i][l%16], D[4(l/16)+i][l%16]):
@@ -367,7 +370,7 @@ struct ValuPath {
 // Every per-head quantity (running max, sum, rescale factor) lives in the
 // lanes owning that head's column, and O^T's rows are channels, so the
 // rescale is lane-local.
-template <int D, int B, int G, int EB = 2>
+template <int D, int B, int G>
 struct MfmaPath {
   static constexpr int MT = D == 128 ? 1 : 2;   // 16-token tiles per batch
   static constexpr int TB = 16 * MT;
@@ -407,9 +410,7 @@ struct MfmaPath {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;                  // token row (A) / column (B, D)
     const int grp = lane >> 4;                  // lane group 0..3
-    if constexpr (EB == 2) {
-      if (last >= 0) append_token<D, B>(a, kvh, seq, last);
-    }
+    if (last >= 0) append_token<D, B>(a, kvh, seq, last);
 
     f16x8 qb[KK];
 #pragma unroll
@@ -423,11 +424,11 @@ struct MfmaPath {
     BlockWindow bw;
     bw.init(a.block_tables + (size_t)seq * a.max_blocks_per_seq, t0 / B,
             (t1 + B - 1) / B, lane);
-    const uint32_t row_stride = (uint32_t)a.num_kv_heads * D * EB;
+    const uint32_t row_stride = (uint32_t)a.num_kv_heads * D * 2;
     const uint64_t blk_bytes = (uint64_t)B * row_stride;
-    const char* kbase = a.key_cache + (size_t)kvh * D * EB;
-    const char* vbase = a.value_cache + (size_t)kvh * D * EB;
-    const float sl2 = a.scale * kLog2e * (EB == 1 ? a.k_scale : 1.f);
+    const char* kbase = a.key_cache + (size_t)kvh * D * 2;
+    const char* vbase = a.value_cache + (size_t)kvh * D * 2;
+    const float sl2 = a.scale * kLog2e;
 
     float m = -INFINITY;                        // reference of head `col`
     float mt = -INFINITY;                       // its true running max
@@ -439,7 +440,7 @@ struct MfmaPath {
 
     for (int base = t0 + wave * TB; base < t1; base += kWaves * TB) {
       bw.cover(base / B, (base + TB - 1) / B, lane);
-      typename KvLoad<EB>::type kr[MT][KK], vr[MT][KK];
+      u32x4 kr[MT][KK], vr[MT][KK];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int tile0 = base + mt * 16;       // wave-uniform
@@ -450,14 +451,14 @@ struct MfmaPath {
         const __amdgpu_buffer_rsrc_t rv = block_rsrc<B>(
             vbase, blk, lb, t1, row_stride, blk_bytes, a.num_blocks);
         const uint32_t off =
-            (uint32_t)(tile0 % B + col) * row_stride + grp * 8 * EB;
+            (uint32_t)(tile0 % B + col) * row_stride + grp * 16;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          kr[mt][kk] = KvLoad<EB>::load(rk, off + kk * 32 * EB);
-          vr[mt][kk] = KvLoad<EB>::load(rv, off + kk * 32 * EB);
+          kr[mt][kk] = load16<kLoadCached>(rk, off + kk * 64);   // half lines
+          vr[mt][kk] = load16<kLoadCached>(rv, off + kk * 64);
         }
       }
-      if constexpr (EB == 2) {
+      {
         if (last >= 0 && base + TB > last) {   // the appended row
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
@@ -482,7 +483,7 @@ struct MfmaPath {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              __builtin_bit_cast(f16x8, widen(kr[mt][kk])), qb[kk], acc, 0, 0, 0);
+              __builtin_bit_cast(f16x8, kr[mt][kk]), qb[kk], acc, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = base + mt * 16 + grp * 4 + i;
@@ -496,7 +497,7 @@ struct MfmaPath {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           _Float16* dst = vw + (mt * 16 + col) * VS + kk * 32 + grp * 8;
-          const u32x4 v = widen(vr[mt][kk]);
+          const u32x4 v = vr[mt][kk];
           reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
           reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
         }
@@ -548,6 +549,262 @@ struct MfmaPath {
 
     // state relative to the true max; the sum over the 4 lane groups; then
     // merge the waves through LDS
+    {
+      const float f = mt == -INFINITY ? 1.f : fast_exp2(m - mt);
+      l *= f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= f;
+      m = mt;
+    }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (col < G) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sm.acc[wave][col][dt * 16 + grp * 4 + i] = o[dt][i];
+      if (grp == 0) {
+        sm.m[wave][col] = m;
+        sm.l[wave][col] = l;
+      }
+    }
+    merge_waves<D, G>(sm, sink);
+  }
+};
+
+// Mfma8Path: the decode body for a group of 8, with whole-line K/V loads.
+// MfmaPath's operand layout loads 64 bytes of each of 16 rows per
+// instruction (half lines).  Here a 16-token tile is two halves of 8 tokens,
+// and in a half, MFMA row i is token i/2 with channel half i%2 of each line
+// chunk, so one instruction fetches 8 tokens x 128 contiguous bytes.  For
+// the product to stay a matrix product, the channel half also indexes the
+// columns: the 16 B columns are (head n%8, channel half n/8).  Column (g, h)
+// multiplies every row by head g's channels of half h; only the rows of half
+// h are kept, and lanes n and n^8 add their two halves into the full score
+// (both get the same bits).  Columns 8..15 then duplicate columns 0..7
+// through softmax and P.V, and only 0..7 are stored.  A lane's four score
+// slots are tokens T = {2q, 2q+1, 8+2q, 9+2q} of the tile (q = lane/16);
+// the P.V k-order follows T, which only changes which LDS rows V^T reads.
+// CPL channels per lane per load: 8 (fp16, 16 bytes), 16 (fp8 at D = 128,
+// 16 bytes, two MFMA k-steps) or 8 (fp8 at D = 64, 8 bytes).
+template <int D, int B, int EB>
+struct Mfma8Path {
+  static constexpr int G = 8;
+  static constexpr int MT = D == 128 ? 1 : 2;   // 16-token tiles per batch
+  static constexpr int TB = 16 * MT;
+  static constexpr int CPL = (EB == 1 && D >= 128) ? 16 : 8;
+  static constexpr int KL = D / (8 * CPL);      // loads per row pair
+  static constexpr int KS = CPL / 8;            // MFMA k-steps per load
+  static constexpr int DT = D / 16;
+  static constexpr int VS = D + 4;              // padded LDS row (halves)
+  static constexpr int kMinWaves = 4;           // 128 VGPRs: 4 waves per SIMD
+  static_assert(B % 16 == 0, "a tile must not straddle two blocks");
+  static_assert(KL * 8 * CPL == D, "line chunks cover the row");
+  using Raw = std::conditional_t<CPL * EB == 16, u32x4, u32x2>;
+
+  struct Smem {
+    _Float16 vs[kWaves][TB][VS];
+    float acc[kWaves][G][D];
+    float m[kWaves][G];
+    float l[kWaves][G];
+  };
+
+  __device__ static Raw load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (CPL * EB == 16) return load16(r, off);
+    else return load8(r, off);
+  }
+  // fp16 channels s*8 .. s*8+7 of a loaded chunk
+  __device__ static u32x4 part(const Raw& w, int s) {
+    if constexpr (EB == 2) {
+      return w;
+    } else if constexpr (CPL == 8) {
+      return fp8x8_to_f16x8(w);
+    } else {
+      const unsigned x = w.x, y = w.y, z = w.z, v = w.w;
+      return s == 0 ? fp8x8_to_f16x8((u32x2){x, y}) : fp8x8_to_f16x8((u32x2){z, v});
+    }
+  }
+
+  // t0 must be a multiple of 16; `last` as for ValuPath::run (fp16 only).
+  template <class Sink>
+  __device__ static void run(const DecodeArgs& a, Smem& sm, int kvh, int seq,
+                             int t0, int t1, int last, Sink& sink) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+    const int g = col & 7;                      // B column: head
+    const int h = col >> 3;                     // B column: channel half
+    if constexpr (EB == 2) {
+      if (last >= 0) append_token<D, B>(a, kvh, seq, last);
+    }
+
+    // B operand of load kl, k-step s: head g, channels
+    // kl*8*CPL + h*4*CPL + grp*CPL + s*8 .. +7
+    f16x8 qb[KL][KS];
+    const _Float16* qrow =
+        a.query + ((size_t)seq * a.num_heads + (size_t)kvh * G + g) * D;
+#pragma unroll
+    for (int kl = 0; kl < KL; ++kl)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        qb[kl][s] = __builtin_bit_cast(
+            f16x8, *reinterpret_cast<const u32x4*>(
+                       qrow + kl * 8 * CPL + h * 4 * CPL + grp * CPL + s * 8));
+
+    BlockWindow bw;
+    bw.init(a.block_tables + (size_t)seq * a.max_blocks_per_seq, t0 / B,
+            (t1 + B - 1) / B, lane);
+    const uint32_t row_stride = (uint32_t)a.num_kv_heads * D * EB;
+    const uint64_t blk_bytes = (uint64_t)B * row_stride;
+    const char* kbase = a.key_cache + (size_t)kvh * D * EB;
+    const char* vbase = a.value_cache + (size_t)kvh * D * EB;
+    const float sl2 = a.scale * kLog2e * (EB == 1 ? a.k_scale : 1.f);
+    // A operand row of a half tile: token col/2, channels (load kl)
+    // kl*8*CPL + (col%2)*4*CPL + grp*CPL ..
+    const int rtok = col >> 1;
+    const int rch = (col & 1) * 4 * CPL + grp * CPL;
+
+    float m = -INFINITY;                        // reference of head g
+    float mt = -INFINITY;                       // its true running max
+    float l = 0.f;                              // this lane's share of the sum
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    _Float16* vw = &sm.vs[wave][0][0];
+
+    for (int base = t0 + wave * TB; base < t1; base += kWaves * TB) {
+      bw.cover(base / B, (base + TB - 1) / B, lane);
+      Raw kr[MT][2][KL], vr[MT][2][KL];
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+        const int tile0 = base + mi * 16;       // wave-uniform
+        const int lb = tile0 / B;
+        const int blk = bw.block(lb);
+        const __amdgpu_buffer_rsrc_t rk = block_rsrc<B>(
+            kbase, blk, lb, t1, row_stride, blk_bytes, a.num_blocks);
+        const __amdgpu_buffer_rsrc_t rv = block_rsrc<B>(
+            vbase, blk, lb, t1, row_stride, blk_bytes, a.num_blocks);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const uint32_t off =
+              (uint32_t)(tile0 % B + hf * 8 + rtok) * row_stride + rch * EB;
+#pragma unroll
+          for (int kl = 0; kl < KL; ++kl) {
+            kr[mi][hf][kl] = load(rk, off + kl * 8 * CPL * EB);
+            vr[mi][hf][kl] = load(rv, off + kl * 8 * CPL * EB);
+          }
+        }
+      }
+      if constexpr (EB == 2) {
+        if (last >= 0 && base + TB > last) {   // the appended row
+          const size_t src = ((size_t)seq * a.num_kv_heads + kvh) * D + rch;
+#pragma unroll
+          for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+              if (base + mi * 16 + hf * 8 + rtok == last) {
+#pragma unroll
+                for (int kl = 0; kl < KL; ++kl) {
+                  kr[mi][hf][kl] =
+                      *reinterpret_cast<const u32x4*>(a.new_key + src + kl * 8 * CPL);
+                  vr[mi][hf][kl] =
+                      *reinterpret_cast<const u32x4*>(a.new_value + src + kl * 8 * CPL);
+                }
+              }
+        }
+      }
+
+      // scores of head g: slot j = token tile0 + T(j)
+      float sc[MT][4];
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kl = 0; kl < KL; ++kl)
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  __builtin_bit_cast(f16x8, part(kr[mi][hf][kl], s)), qb[kl][s], acc,
+                  0, 0, 0);
+          // rows 4q + j: token 2q + j/2, channel half j%2; keep half h
+          const float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
+          const float p0 = h ? a1 : a0;
+          const float p1 = h ? a3 : a2;
+          const float f0 = p0 + dpp<kRowRor8>(p0);
+          const float f1 = p1 + dpp<kRowRor8>(p1);
+          const int tok = base + mi * 16 + hf * 8 + 2 * grp;
+          sc[mi][2 * hf] = tok < t1 ? f0 * sl2 : -INFINITY;
+          sc[mi][2 * hf + 1] = tok + 1 < t1 ? f1 * sl2 : -INFINITY;
+        }
+      }
+
+      // V tile to LDS in token-major rows (8-byte stores)
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int kl = 0; kl < KL; ++kl)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+              _Float16* dst =
+                  vw + (mi * 16 + hf * 8 + rtok) * VS + kl * 8 * CPL + rch + s * 8;
+              const u32x4 v = part(vr[mi][hf][kl], s);
+              reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
+              reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
+            }
+
+      // online softmax for head g (max over the batch and the 4 groups)
+      float bm = -INFINITY;
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[mi][i]);
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      mt = fmaxf(mt, bm);
+      if (__builtin_amdgcn_ballot_w64(bm > m + kSlack)) {
+        const float mn = fmaxf(m, mt);
+        const float al = fast_exp2(m - (mn == -INFINITY ? 0.f : mn));
+        l *= al;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
+        m = mn;
+      }
+      const float sh = m == -INFINITY ? 0.f : m;
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[mi][i] = fast_exp2(sc[mi][i] - sh);
+          l += sc[mi][i];
+        }
+
+      // O^T += V^T P^T, the tile's 16 tokens in the slot order T
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+        f16x4 pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pb[i] = (_Float16)sc[mi][i];
+        const _Float16* v0 = vw + (mi * 16 + 2 * grp) * VS + col;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          f16x4 va;
+          va[0] = v0[dt * 16];
+          va[1] = v0[VS + dt * 16];
+          va[2] = v0[8 * VS + dt * 16];
+          va[3] = v0[9 * VS + dt * 16];
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, o[dt], 0, 0, 0);
+        }
+      }
+    }
+
+    // state relative to the true max (and in V's units for an fp8 pool);
+    // the sum over the 4 lane groups; then merge the waves through LDS
     {
       const float f = mt == -INFINITY ? 1.f : fast_exp2(m - mt);
       l *= f;
@@ -996,7 +1253,7 @@ struct PathFor {
 };
 template <int D, int B, int EB>
 struct PathFor<D, B, 8, EB> {
-  using type = MfmaPath<D, B, 8, EB>;
+  using type = Mfma8Path<D, B, EB>;
 };
 
 enum class Op { kPartition, kBalanced, kOccupancy, kMulti };
