@@ -77,6 +77,7 @@ constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;
 constexpr int kRowMirror = 0x140;
 constexpr int kRowRor8 = 0x128;      // row_ror:8 = lane ^ 8 within a row of 16
+constexpr int kRowRor4 = 0x124;      // row_ror:4
 
 // Sum over aligned groups of LANES (8 or 16) lanes; every lane of a group
 // ends with the bitwise-identical total (each step adds two equal-order

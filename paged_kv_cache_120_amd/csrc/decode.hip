@@ -573,34 +573,37 @@ struct MfmaPath {
   }
 };
 
-// Mfma8Path: the decode body for a group of 8, with whole-line K/V loads.
-// MfmaPath's operand layout loads 64 bytes of each of 16 rows per
-// instruction (half lines).  Here a 16-token tile is two halves of 8 tokens,
-// and in a half, MFMA row i is token i/2 with channel half i%2 of each line
-// chunk, so one instruction fetches 8 tokens x 128 contiguous bytes.  For
-// the product to stay a matrix product, the channel half also indexes the
-// columns: the 16 B columns are (head n%8, channel half n/8).  Column (g, h)
-// multiplies every row by head g's channels of half h; only the rows of half
-// h are kept, and lanes n and n^8 add their two halves into the full score
-// (both get the same bits).  Columns 8..15 then duplicate columns 0..7
-// through softmax and P.V, and only 0..7 are stored.  A lane's four score
-// slots are tokens T = {2q, 2q+1, 8+2q, 9+2q} of the tile (q = lane/16);
-// the P.V k-order follows T, which only changes which LDS rows V^T reads.
-// CPL channels per lane per load: 8 (fp16, 16 bytes), 16 (fp8 at D = 128,
-// 16 bytes, two MFMA k-steps) or 8 (fp8 at D = 64, 8 bytes).
-template <int D, int B, int EB>
-struct Mfma8Path {
-  static constexpr int G = 8;
+// MfmaSplitPath: the decode body for a group of g = 8 or 4 on the matrix
+// cores, with whole-line K/V loads.  MfmaPath's operand layout loads 64
+// bytes of each of 16 rows per instruction (half lines).  Here MFMA row i is
+// token i/R and channel split i%R of each line chunk (R = 16/g), so one
+// instruction fetches g tokens x R*64 contiguous bytes.  For the product to
+// stay a matrix product, the split also indexes the columns: the 16 B
+// columns are (head n%g, split n/g).  Column (h, q) multiplies every row by
+// head h's channels of split q; only the rows of split q are kept, and the R
+// lanes n, n+g, .. of a head add their splits into the full score (all with
+// the same bits).  The extra columns then duplicate head h through softmax
+// and P.V, and only columns < g are stored.  A tile of 16 tokens takes R
+// MFMA row groups of g tokens; a lane's four score slots are tokens
+// T(j) = (j/U)*g + (lane/16)*U + j%U of the tile (U = 4/R), and the P.V
+// k-order follows T, which only changes which LDS rows V^T reads.
+// CPL channels per lane per load: min(16 bytes, D/(4R) channels), >= 8.
+template <int D, int B, int G, int EB>
+struct MfmaSplitPath {
+  static constexpr int R = 16 / G;              // channel splits = rows per token
+  static constexpr int U = 4 / R;               // useful D values per lane per MFMA
   static constexpr int MT = D == 128 ? 1 : 2;   // 16-token tiles per batch
   static constexpr int TB = 16 * MT;
-  static constexpr int CPL = (EB == 1 && D >= 128) ? 16 : 8;
-  static constexpr int KL = D / (8 * CPL);      // loads per row pair
+  static constexpr int CPL = (16 / EB) < D / (4 * R) ? (16 / EB) : D / (4 * R);
+  static constexpr int LC = R * 4 * CPL;        // channels of one line chunk
+  static constexpr int KL = D / LC;             // loads per row group
   static constexpr int KS = CPL / 8;            // MFMA k-steps per load
   static constexpr int DT = D / 16;
   static constexpr int VS = D + 4;              // padded LDS row (halves)
   static constexpr int kMinWaves = 4;           // 128 VGPRs: 4 waves per SIMD
+  static_assert(G == 8 || G == 4, "16 columns = g heads x R splits");
   static_assert(B % 16 == 0, "a tile must not straddle two blocks");
-  static_assert(KL * 8 * CPL == D, "line chunks cover the row");
+  static_assert(CPL >= 8 && CPL % 8 == 0 && KL * LC == D, "line chunks cover the row");
   using Raw = std::conditional_t<CPL * EB == 16, u32x4, u32x2>;
 
   struct Smem {
@@ -634,24 +637,24 @@ struct Mfma8Path {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;
     const int grp = lane >> 4;
-    const int g = col & 7;                      // B column: head
-    const int h = col >> 3;                     // B column: channel half
+    const int hd = col % G;                     // B column: head
+    const int q = col / G;                      // B column: split
     if constexpr (EB == 2) {
       if (last >= 0) append_token<D, B>(a, kvh, seq, last);
     }
 
-    // B operand of load kl, k-step s: head g, channels
-    // kl*8*CPL + h*4*CPL + grp*CPL + s*8 .. +7
+    // B operand of load kl, k-step s: head hd, channels
+    // kl*LC + q*4*CPL + grp*CPL + s*8 .. +7
     f16x8 qb[KL][KS];
     const _Float16* qrow =
-        a.query + ((size_t)seq * a.num_heads + (size_t)kvh * G + g) * D;
+        a.query + ((size_t)seq * a.num_heads + (size_t)kvh * G + hd) * D;
 #pragma unroll
     for (int kl = 0; kl < KL; ++kl)
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         qb[kl][s] = __builtin_bit_cast(
             f16x8, *reinterpret_cast<const u32x4*>(
-                       qrow + kl * 8 * CPL + h * 4 * CPL + grp * CPL + s * 8));
+                       qrow + kl * LC + q * 4 * CPL + grp * CPL + s * 8));
 
     BlockWindow bw;
     bw.init(a.block_tables + (size_t)seq * a.max_blocks_per_seq, t0 / B,
@@ -661,12 +664,12 @@ struct Mfma8Path {
     const char* kbase = a.key_cache + (size_t)kvh * D * EB;
     const char* vbase = a.value_cache + (size_t)kvh * D * EB;
     const float sl2 = a.scale * kLog2e * (EB == 1 ? a.k_scale : 1.f);
-    // A operand row of a half tile: token col/2, channels (load kl)
-    // kl*8*CPL + (col%2)*4*CPL + grp*CPL ..
-    const int rtok = col >> 1;
-    const int rch = (col & 1) * 4 * CPL + grp * CPL;
+    // A operand row of a row group: token col/R, channels (load kl)
+    // kl*LC + (col%R)*4*CPL + grp*CPL ..
+    const int rtok = col / R;
+    const int rch = (col % R) * 4 * CPL + grp * CPL;
 
-    float m = -INFINITY;                        // reference of head g
+    float m = -INFINITY;                        // reference of head hd
     float mt = -INFINITY;                       // its true running max
     float l = 0.f;                              // this lane's share of the sum
     f32x4 o[DT];
@@ -676,7 +679,7 @@ struct Mfma8Path {
 
     for (int base = t0 + wave * TB; base < t1; base += kWaves * TB) {
       bw.cover(base / B, (base + TB - 1) / B, lane);
-      Raw kr[MT][2][KL], vr[MT][2][KL];
+      Raw kr[MT][R][KL], vr[MT][R][KL];
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
         const int tile0 = base + mi * 16;       // wave-uniform
@@ -687,13 +690,13 @@ struct Mfma8Path {
         const __amdgpu_buffer_rsrc_t rv = block_rsrc<B>(
             vbase, blk, lb, t1, row_stride, blk_bytes, a.num_blocks);
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+        for (int rg = 0; rg < R; ++rg) {
           const uint32_t off =
-              (uint32_t)(tile0 % B + hf * 8 + rtok) * row_stride + rch * EB;
+              (uint32_t)(tile0 % B + rg * G + rtok) * row_stride + rch * EB;
 #pragma unroll
           for (int kl = 0; kl < KL; ++kl) {
-            kr[mi][hf][kl] = load(rk, off + kl * 8 * CPL * EB);
-            vr[mi][hf][kl] = load(rv, off + kl * 8 * CPL * EB);
+            kr[mi][rg][kl] = load(rk, off + kl * LC * EB);
+            vr[mi][rg][kl] = load(rv, off + kl * LC * EB);
           }
         }
       }
@@ -703,42 +706,46 @@ struct Mfma8Path {
 #pragma unroll
           for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-              if (base + mi * 16 + hf * 8 + rtok == last) {
+            for (int rg = 0; rg < R; ++rg)
+              if (base + mi * 16 + rg * G + rtok == last) {
 #pragma unroll
                 for (int kl = 0; kl < KL; ++kl) {
-                  kr[mi][hf][kl] =
-                      *reinterpret_cast<const u32x4*>(a.new_key + src + kl * 8 * CPL);
-                  vr[mi][hf][kl] =
-                      *reinterpret_cast<const u32x4*>(a.new_value + src + kl * 8 * CPL);
+                  kr[mi][rg][kl] =
+                      *reinterpret_cast<const u32x4*>(a.new_key + src + kl * LC);
+                  vr[mi][rg][kl] =
+                      *reinterpret_cast<const u32x4*>(a.new_value + src + kl * LC);
                 }
               }
         }
       }
 
-      // scores of head g: slot j = token tile0 + T(j)
+      // scores of head hd: slot j = token tile0 + T(j)
       float sc[MT][4];
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+        for (int rg = 0; rg < R; ++rg) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kl = 0; kl < KL; ++kl)
 #pragma unroll
             for (int s = 0; s < KS; ++s)
               acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                  __builtin_bit_cast(f16x8, part(kr[mi][hf][kl], s)), qb[kl][s], acc,
+                  __builtin_bit_cast(f16x8, part(kr[mi][rg][kl], s)), qb[kl][s], acc,
                   0, 0, 0);
-          // rows 4q + j: token 2q + j/2, channel half j%2; keep half h
-          const float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
-          const float p0 = h ? a1 : a0;
-          const float p1 = h ? a3 : a2;
-          const float f0 = p0 + dpp<kRowRor8>(p0);
-          const float f1 = p1 + dpp<kRowRor8>(p1);
-          const int tok = base + mi * 16 + hf * 8 + 2 * grp;
-          sc[mi][2 * hf] = tok < t1 ? f0 * sl2 : -INFINITY;
-          sc[mi][2 * hf + 1] = tok + 1 < t1 ? f1 * sl2 : -INFINITY;
+          // rows 4grp + j: token (4grp + j)/R, split j%R; keep split q
+          const float av[4] = {acc[0], acc[1], acc[2], acc[3]};
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            float p = av[R * u];
+#pragma unroll
+            for (int k = 1; k < R; ++k) p = q == k ? av[k + R * u] : p;
+            // sum over the R lanes of head hd (bitwise equal in each)
+            if constexpr (R >= 2) p += dpp<kRowRor8>(p);
+            if constexpr (R >= 4) p += dpp<kRowRor4>(p);
+            const int tok = base + mi * 16 + rg * G + grp * U + u;
+            sc[mi][rg * U + u] = tok < t1 ? p * sl2 : -INFINITY;
+          }
         }
       }
 
@@ -746,19 +753,19 @@ struct Mfma8Path {
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
+        for (int rg = 0; rg < R; ++rg)
 #pragma unroll
           for (int kl = 0; kl < KL; ++kl)
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
               _Float16* dst =
-                  vw + (mi * 16 + hf * 8 + rtok) * VS + kl * 8 * CPL + rch + s * 8;
-              const u32x4 v = part(vr[mi][hf][kl], s);
+                  vw + (mi * 16 + rg * G + rtok) * VS + kl * LC + rch + s * 8;
+              const u32x4 v = part(vr[mi][rg][kl], s);
               reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
               reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
             }
 
-      // online softmax for head g (max over the batch and the 4 groups)
+      // online softmax for head hd (max over the batch and the 4 groups)
       float bm = -INFINITY;
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi)
@@ -790,14 +797,13 @@ struct Mfma8Path {
         f16x4 pb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) pb[i] = (_Float16)sc[mi][i];
-        const _Float16* v0 = vw + (mi * 16 + 2 * grp) * VS + col;
+        const _Float16* v0 = vw + (mi * 16 + grp * U) * VS + col;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           f16x4 va;
-          va[0] = v0[dt * 16];
-          va[1] = v0[VS + dt * 16];
-          va[2] = v0[8 * VS + dt * 16];
-          va[3] = v0[9 * VS + dt * 16];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            va[j] = v0[((j / U) * G + j % U) * VS + dt * 16];
           o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, o[dt], 0, 0, 0);
         }
       }
@@ -1235,14 +1241,15 @@ __attribute__((amdgpu_waves_per_eu(Path::kMinWaves))) void balanced_kernel(
 // Dispatch
 // ---------------------------------------------------------------------------
 
-// Loads in flight per wave batch for the vector-ALU body (NJ); measured on
-// MI355X.  fp16 pools: 8 is best for groups of 1-2, 2 for a group of 4 (fewer
-// registers, four waves per SIMD).  fp8 pools move half the bytes per load,
-// so groups of 1 and 4 keep twice the loads in flight (16 and 4; a group of
-// 4 runs 10% faster); a group of 2 stays at 8 (16 would halve its waves).
-// A group of 8 runs on the matrix cores; for a group of 4 the matrix-core
-// body measured slower than the vector one (fp16: 3.7-3.9 vs 4.0-4.3 TB/s
-// on the GQA-4 workload; fp8: 82 vs 65 us).
+// Bodies per group size, measured on MI355X.  Groups of 8, and of 4 at head
+// size 128, run on the matrix cores with whole-line loads (g = 4 on c3: 4.4
+// vs 3.9-4.0 TB/s for the vector body, fp8 48-50 vs 71-72 us; the earlier
+// half-line matrix-core body had lost to the vector one).  The rest run the
+// vector-ALU body with NJ loads in flight per wave batch: fp16 pools 8 for
+// groups of 1-2, 2 for a group of 4 (fewer registers, four waves per SIMD);
+// fp8 pools move half the bytes per load, so a group of 1 keeps 16 loads and
+// a group of 4 keeps 4 in flight (+10% for g = 4); a group of 2 stays at 8
+// (16 would halve its waves).
 template <int G, int EB>
 constexpr int valu_loads() {
   return EB == 2 ? (G >= 4 ? 2 : 8) : (G == 4 ? 4 : G == 2 ? 8 : 16);
@@ -1253,7 +1260,11 @@ struct PathFor {
 };
 template <int D, int B, int EB>
 struct PathFor<D, B, 8, EB> {
-  using type = Mfma8Path<D, B, EB>;
+  using type = MfmaSplitPath<D, B, 8, EB>;
+};
+template <int B, int EB>
+struct PathFor<128, B, 4, EB> {
+  using type = MfmaSplitPath<128, B, 4, EB>;
 };
 
 enum class Op { kPartition, kBalanced, kOccupancy, kMulti };
