@@ -482,6 +482,90 @@ def fp8_bench(args, w, dev) -> int:
     return 0
 
 
+def prefix_kernel_bytes(w, groups) -> int:
+    """Algorithmic bytes of one pa_decode_shared_prefix: K/V of each group's
+    shared partitions once, the rest of every sequence's context once, the
+    query and output, and the per-(sequence, head, partition) states written
+    and read back by the reduce."""
+    S, H, D = w.query.shape
+    P = w.partition_size
+    n = w.context_lens.astype(np.int64)
+    off, mem, blk = groups
+    shared = np.zeros(S, np.int64)
+    row = 2 * w.num_kv_heads * D * 2
+    kv = 0
+    for j in range(len(blk)):
+        t = int(blk[j]) * w.block_size // P * P
+        ms = mem[off[j]:off[j + 1]]
+        kv += min(t, int(n[ms].max())) * row
+        for m in ms:
+            shared[m] = min(t, int(n[m]))
+    kv += int((n - shared).sum()) * row
+    parts = int(((n + P - 1) // P).sum())
+    return kv + 2 * S * H * D * 2 + 2 * parts * H * (D + 2) * 4
+
+
+def prefix_bench(args, w, dev) -> int:
+    """Decode with shared prefixes read once per group: COW copies + slot
+    mapping + cache write, then pa_decode_shared_prefix."""
+    import torch
+    from paged_kv_cache_120_amd import runner
+    base = runner.upload_prefix(w, dev)
+    runner.apply_history(w, base)
+    steps = [base] + [runner.upload_prefix(w, dev, pool=base.pool.clone())
+                      for _ in range(1, max(1, args.rotate))]
+    torch.cuda.synchronize()
+    R = len(steps)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(steps[i % R])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            fn(steps[i % R])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_step = timed(runner.prefix_step)
+    kms = timed(runner.prefix_decode)
+    runner.prefix_step(steps[(args.steps - 1) % R])
+    torch.cuda.synchronize()
+    groups = runner.prefix_groups(w.block_tables, w.context_lens, w.block_size)
+    kvb = kv_bytes(w)
+    kb = prefix_kernel_bytes(w, groups)
+    achieved = kb / (kms * 1e-3) / 1e9
+    rec = {
+        "metric": "paged decode with shared prefixes: logical KV GB/s + seqs/s",
+        "value": round(kvb / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "name": args.config,
+                   "num_seqs": w.num_seqs, "groups": int(len(groups[2])),
+                   "shared_blocks": [int(x) for x in groups[2][:4]],
+                   "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_size": w.head_size, "block_size": w.block_size,
+                   "partition_size": w.partition_size,
+                   "total_context_tokens": int(w.context_lens.sum()),
+                   "rotated_pool_copies": R, "seed": w.seed},
+        "accumulate": "f32", "kv_bytes_per_step_logical": kvb,
+        "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel": "prefix_kernel + partition_kernel + reduce_kernel",
+                     "kernel_ms": round(kms, 5), "algorithmic_bytes": kb},
+    }
+    if not args.no_cpu_baseline:
+        parity, cpu = cpu_baseline(w, steps[(args.steps - 1) % R].out.cpu().numpy())
+        rec["parity"], rec["cpu_baseline"] = parity, cpu
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -490,14 +574,15 @@ def main(argv=None) -> int:
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="fused",
                     choices=["fused", "balanced", "splitk", "single", "swap", "multi",
-                             "fp8"],
+                             "fp8", "prefix"],
                     help="fused: pa_decode_step (append + balanced decode, one kernel); "
                          "balanced/splitk/single: slot mapping + cache write + that decode; "
                          "swap: pa_swap_blocks of the batch's blocks to pinned host memory "
                          "and back (its own JSON line); multi: cache write of each "
                          "sequence's query chunk + pa_decode_multi (the *_spec4 configs); "
                          "fp8: the balanced decode over an e4m3 pool (fp8 cache write + "
-                         "pa_decode_balanced_fp8, its own JSON line)")
+                         "pa_decode_balanced_fp8, its own JSON line); prefix: writes + "
+                         "pa_decode_shared_prefix (c4; its own JSON line)")
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--partition", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -524,6 +609,8 @@ def main(argv=None) -> int:
         return swap_bench(args, w, dev)
     if args.mode == "fp8":
         return fp8_bench(args, w, dev)
+    if args.mode == "prefix":
+        return prefix_bench(args, w, dev)
     if args.mode == "multi" or "cu_seqlens_q" in w.info:
         if args.mode != "multi" or "cu_seqlens_q" not in w.info:
             print("--mode multi goes with a multi-token config (c2_spec4, c3_spec4)",

@@ -260,6 +260,49 @@ pa_status pa_decode_balanced(void* out, const void* query,
                              hipStream_t stream);
 
 /*
+ * Shared-prefix decode: the same result as pa_decode_splitk +
+ * pa_decode_reduce (same partitions, same reduce; within pa_decode's
+ * tolerance of the exact attention), but a partition that lies inside the
+ * full blocks a group of sequences shares is read once for the whole group.
+ * [GUST] copy-on-write paragraph: many requests start with the same system
+ * prompt or sampled continuations of one prompt, so their tables point at
+ * the same physical blocks until one of them writes; [BOOK] §4.7.1 (the
+ * samples of one prompt reference its blocks) and §4.7.2-4.7.3 (prefix caching
+ * reuses full blocks only).
+ *   group_offsets  int32 [num_groups + 1]: members of group j are
+ *                  group_members[group_offsets[j] .. group_offsets[j+1]-1]
+ *   group_members  int32: sequence indices (each sequence in at most one
+ *                  group; indices outside [0, num_seqs) are ignored)
+ *   group_blocks   int32 [num_groups]: leading logical blocks that every
+ *                  member's block_tables row holds with the same physical
+ *                  ids (precondition; the first member's row is read)
+ *   max_group_size >= every group's member count, and max_group_blocks >=
+ *                  every group_blocks entry (host values sizing the launch;
+ *                  members or blocks beyond them are simply not shared)
+ *   The shared partitions of group j are the first
+ *   min(group_blocks[j], max_group_blocks) * block_size / partition_size
+ *   (whole partitions only); every other partition is computed per
+ *   sequence.  A member whose context ends inside a shared partition gets
+ *   its own key limit.  Other arguments as pa_decode_splitk; out as
+ *   pa_decode_reduce.  num_groups == 0 is plain split-K decode.
+ * pa_prefix_workspace_size: bytes of workspace (16-byte aligned): the
+ *   split-K workspace followed by int32 [num_seqs].  No zero-fill needed.
+ */
+size_t pa_prefix_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                int32_t head_size, int32_t max_blocks_per_seq,
+                                int32_t block_size, int32_t partition_size);
+pa_status pa_decode_shared_prefix(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+    int32_t num_blocks, float scale, int32_t partition_size,
+    const int32_t* group_offsets, const int32_t* group_members,
+    const int32_t* group_blocks, int32_t num_groups, int32_t max_group_size,
+    int32_t max_group_blocks, void* workspace, size_t workspace_bytes,
+    hipStream_t stream);
+
+/*
  * FP8 KV cache: a pool that stores one byte per element instead of two
  * ([BOOK] §4.8 names a lower-precision KV cache as a way to fit more
  * concurrent tokens in the same memory; [CSDN] part 3 (2), the KVBlock

@@ -20,7 +20,8 @@ __all__ = [
     "pa_splitk_workspace_size", "pa_decode_splitk", "pa_decode_reduce",
     "pa_balanced_grid", "pa_balanced_workspace_size", "pa_decode_balanced",
     "pa_decode_step", "pa_multi_workspace_size", "pa_decode_multi",
-    "pa_cache_write_fp8", "pa_balanced_grid_fp8", "pa_decode_balanced_fp8", "STATUS",
+    "pa_cache_write_fp8", "pa_balanced_grid_fp8", "pa_decode_balanced_fp8",
+    "pa_prefix_workspace_size", "pa_decode_shared_prefix", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +74,10 @@ def _load() -> ctypes.CDLL:
         "pa_cache_write_fp8": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                               f32, f32, vp]),
         "pa_balanced_grid_fp8": (i32, [i32, i32, i32, i32]),
+        "pa_prefix_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
+        "pa_decode_shared_prefix": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32,
+                                                   i32, i32, i32, i32, f32, i32, vp, vp,
+                                                   vp, i32, i32, i32, vp, sz, vp]),
         "pa_decode_balanced_fp8": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32,
                                                   i32, i32, i32, i32, f32, f32, f32, i32,
                                                   vp, sz, vp]),
@@ -131,6 +136,14 @@ def pa_balanced_grid_fp8(num_heads: int, num_kv_heads: int, head_size: int,
     """As pa_balanced_grid, for the decode over an fp8 pool."""
     return int(_lib().pa_balanced_grid_fp8(num_heads, num_kv_heads, head_size,
                                            block_size))
+
+
+def pa_prefix_workspace_size(num_seqs: int, num_heads: int, head_size: int,
+                             max_blocks_per_seq: int, block_size: int,
+                             partition_size: int) -> int:
+    return int(_lib().pa_prefix_workspace_size(num_seqs, num_heads, head_size,
+                                               max_blocks_per_seq, block_size,
+                                               partition_size))
 
 
 def pa_balanced_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int,
@@ -414,6 +427,33 @@ def pa_decode_balanced_fp8(out, query, key_cache, value_cache, block_tables,
         _dev(context_lens, torch.int32, "context_lens", 1), S, H, Hkv, D, B, nb,
         float(scale), float(k_scale), float(v_scale), int(grid), ws, nbytes,
         _stream(stream)))
+
+
+def pa_decode_shared_prefix(out, query, key_cache, value_cache, block_tables,
+                            context_lens, scale: float, partition_size: int,
+                            group_offsets, group_members, group_blocks,
+                            max_group_size: int, max_group_blocks: int, workspace,
+                            stream=None) -> None:
+    """Split-K decode where each group's shared full blocks are read once for
+    all its members (group_* int32 device tensors: CSR member lists and the
+    shared leading block count per group)."""
+    torch = _torch()
+    (q, kc, vc, bt, cl), (S, H, Hkv, D, B, nb, M) = _decode_common(
+        query, key_cache, value_cache, block_tables, context_lens)
+    if tuple(out.shape) != (S, H, D):
+        raise ValueError("pa_decode_shared_prefix: out shape")
+    G = int(group_blocks.numel())
+    if tuple(group_offsets.shape) != (G + 1,):
+        raise ValueError("pa_decode_shared_prefix: group_offsets must have num_groups + 1 entries")
+    ws = _dev(workspace, workspace.dtype, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("pa_decode_shared_prefix", _lib().pa_decode_shared_prefix(
+        _dev(out, torch.float16, "out", 3), q, kc, vc, bt, M, cl, S, H, Hkv, D, B, nb,
+        float(scale), int(partition_size),
+        _dev(group_offsets, torch.int32, "group_offsets", 1),
+        _dev(group_members, torch.int32, "group_members", 1),
+        _dev(group_blocks, torch.int32, "group_blocks", 1), G, int(max_group_size),
+        int(max_group_blocks), ws, nbytes, _stream(stream)))
 
 
 def pa_decode_step(out, query, key, value, key_cache, value_cache, block_tables,

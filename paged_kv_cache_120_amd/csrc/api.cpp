@@ -285,6 +285,104 @@ pa_status pa_decode_splitk(const void* query, const void* key_cache,
                                       num_heads / num_kv_heads, grid, stream));
 }
 
+size_t pa_prefix_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                int32_t head_size, int32_t max_blocks_per_seq,
+                                int32_t block_size, int32_t partition_size) {
+  const size_t split = pa_splitk_workspace_size(num_seqs, num_heads, head_size,
+                                                max_blocks_per_seq, block_size,
+                                                partition_size);
+  if (split == 0 && num_seqs != 0) return 0;
+  return split + (((size_t)(num_seqs > 0 ? num_seqs : 0) * 4 + 15) & ~(size_t)15);
+}
+
+pa_status pa_decode_shared_prefix(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+    int32_t num_blocks, float scale, int32_t partition_size,
+    const int32_t* group_offsets, const int32_t* group_members,
+    const int32_t* group_blocks, int32_t num_groups, int32_t max_group_size,
+    int32_t max_group_blocks, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  pa_status st = check_decode(query, key_cache, value_cache, block_tables,
+                              max_blocks_per_seq, context_lens, num_seqs,
+                              num_heads, num_kv_heads, head_size, block_size,
+                              num_blocks, scale);
+  if (st != PA_OK) return st;
+  if (partition_size <= 0 || partition_size % block_size != 0 ||
+      num_groups < 0 || max_group_size < 0 || max_group_blocks < 0)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  const int64_t pm = max_partitions(max_blocks_per_seq, block_size, partition_size);
+  if (pm > 65535) return PA_ERR_SHAPE;        // grid.z
+  const int32_t g = num_heads / num_kv_heads;
+  const int64_t per_tile = 16 / g;            // members per prefix tile
+  const int64_t tiles = (max_group_size + per_tile - 1) / per_tile;
+  if ((int64_t)num_groups * (tiles > 0 ? tiles : 1) > 65535) return PA_ERR_SHAPE;
+  if (!out || !workspace) return PA_ERR_NULL;
+  if (num_groups > 0 && (!group_offsets || !group_members || !group_blocks))
+    return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(workspace, 16) ||
+      (num_groups > 0 && (!aligned(group_offsets, 4) ||
+                          !aligned(group_members, 4) || !aligned(group_blocks, 4))))
+    return PA_ERR_ALIGN;
+  if (workspace_bytes < pa_prefix_workspace_size(num_seqs, num_heads, head_size,
+                                                 max_blocks_per_seq, block_size,
+                                                 partition_size))
+    return PA_ERR_WORKSPACE;
+  const size_t rows = (size_t)num_seqs * num_heads * pm;
+  pa::DecodeArgs a = {};
+  a.ws_max = static_cast<float*>(workspace);
+  a.ws_sum = a.ws_max + rows;
+  a.ws_out = a.ws_sum + rows;
+  int* part_start = reinterpret_cast<int*>(a.ws_out + rows * head_size);
+  a.query = static_cast<const _Float16*>(query);
+  a.key_cache = static_cast<const char*>(key_cache);
+  a.value_cache = static_cast<const char*>(value_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.partition_size = partition_size;
+  a.max_partitions = (int)pm;
+  a.split = 1;
+  a.scale = scale;
+  a.grp_offsets = group_offsets;
+  a.grp_members = group_members;
+  a.grp_blocks = group_blocks;
+  a.num_groups = num_groups;
+  int64_t gp = (int64_t)max_group_blocks * block_size / partition_size;
+  a.grp_max_parts = (int)(gp < pm ? gp : pm);
+  a.grp_max_members = (int)(tiles * per_tile);
+  a.q_tiles = (int)(tiles > 0 ? tiles : 1);
+  st = hip_status(pa::launch_prefix_marks(a, block_size, part_start, stream));
+  if (st != PA_OK) return st;
+  if (num_groups > 0 && tiles > 0 && a.grp_max_parts > 0) {
+    dim3 pg(num_kv_heads, (unsigned)(num_groups * tiles), (unsigned)a.grp_max_parts);
+    st = hip_status(pa::launch_prefix(a, head_size, block_size, g, pg, stream));
+    if (st != PA_OK) return st;
+  }
+  a.part_start = part_start;
+  dim3 grid(num_kv_heads, num_seqs, (unsigned)pm);
+  st = hip_status(pa::launch_decode(a, head_size, block_size, g, grid, stream));
+  if (st != PA_OK) return st;
+  pa::ReduceArgs r = {};
+  r.out = static_cast<_Float16*>(out);
+  r.ws_max = a.ws_max;
+  r.ws_sum = a.ws_sum;
+  r.ws_out = a.ws_out;
+  r.context_lens = context_lens;
+  r.num_heads = num_heads;
+  r.max_partitions = (int)pm;
+  r.partition_size = partition_size;
+  r.max_tokens = max_blocks_per_seq * block_size;
+  return hip_status(pa::launch_reduce(r, head_size, num_seqs, stream));
+}
+
 size_t pa_multi_workspace_size(int32_t num_q_tokens, int32_t num_heads,
                                int32_t head_size, int32_t max_blocks_per_seq,
                                int32_t block_size, int32_t partition_size) {

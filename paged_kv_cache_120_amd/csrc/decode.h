@@ -39,6 +39,16 @@ struct DecodeArgs {
   // fp8 pools: dequantisation scales (value = code * scale)
   float k_scale;
   float v_scale;
+  // shared-prefix decode: per-sequence first partition left to the
+  // partition kernel (earlier ones come from the prefix kernel), and the
+  // groups (member lists in CSR form, shared full blocks per group)
+  const int* part_start;
+  const int* grp_offsets;
+  const int* grp_members;
+  const int* grp_blocks;
+  int num_groups;
+  int grp_max_parts;     // shared partitions per group at most (grid.z)
+  int grp_max_members;   // members per group the prefix kernel covers
 };
 
 
@@ -64,6 +74,13 @@ hipError_t launch_multi(const DecodeArgs& a, int head_size, int block_size,
                         int group, dim3 grid, hipStream_t stream);
 hipError_t launch_multi_reduce(const ReduceArgs& a, int head_size,
                                int num_q_tokens, hipStream_t stream);
+// shared-prefix decode: part_start from the groups, then the prefix
+// partitions of every group (grid (H_kv, groups x member tiles, shared
+// partitions)); the rest is launch_decode (split mode) + launch_reduce
+hipError_t launch_prefix_marks(const DecodeArgs& a, int block_size,
+                               int* part_start, hipStream_t stream);
+hipError_t launch_prefix(const DecodeArgs& a, int head_size, int block_size,
+                         int group, dim3 grid, hipStream_t stream);
 // elem_bytes: 2 for an fp16 pool, 1 for an fp8 (e4m3) pool
 hipError_t launch_balanced(const DecodeArgs& a, int head_size, int block_size,
                            int group, int grid, hipStream_t stream,

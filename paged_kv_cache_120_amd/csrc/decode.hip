@@ -855,6 +855,8 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(DecodeArgs a) {
   const int max_tok = a.max_blocks_per_seq * B;
   n = n < max_tok ? n : max_tok;
   const int t0 = p * a.partition_size;
+  // shared-prefix decode: partitions below part_start came from prefix_kernel
+  if (a.split && a.part_start && p < a.part_start[seq]) return;
   if (n <= 0 || t0 >= n) {
     if (!a.split && p == 0) {
       for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
@@ -965,6 +967,102 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(DecodeArgs a) {
     a.ws_out[pi * D + d] = O;
   };
   Path::run_cols(a, sm, kvh, seq, t0, t1, -1, sink, qoff, ok ? pos0 + qj : -1);
+}
+
+// ---------------------------------------------------------------------------
+// Shared-prefix decode
+// ---------------------------------------------------------------------------
+//
+// Sequences whose tables point at the same physical blocks for a prefix
+// (parallel samples or a shared system prompt whose full blocks are shared
+// by reference) form a group.  Each split-KV partition that lies inside the
+// group's shared full blocks is computed once for all members: the
+// matrix-core body runs with 16 columns = (member, head) pairs, 16/g members
+// x the g heads of one kv head, reading the shared K/V once; each column
+// keeps its member's context length as its key limit.  Every member's state
+// goes to that member's own partition slot of the split-K workspace, where
+// the partition kernel (which skips those partitions) and the reduce find
+// it exactly as if it had been computed per sequence.
+
+// Number of shared partitions a group gets (full partitions inside its
+// shared full blocks, which count at most max_blocks_per_seq, and at most
+// the launch's grid depth).
+__device__ __forceinline__ int prefix_parts(const DecodeArgs& a, int g,
+                                            int block_size) {
+  int64_t blocks = a.grp_blocks[g];
+  blocks = blocks < a.max_blocks_per_seq ? blocks : a.max_blocks_per_seq;
+  const int64_t tok = blocks * block_size;
+  int64_t parts = tok > 0 ? tok / a.partition_size : 0;
+  return (int)(parts < a.grp_max_parts ? parts : a.grp_max_parts);
+}
+
+// part_start[s] = 0 for every sequence (grid over sequences) ...
+__global__ __launch_bounds__(256) void prefix_clear_kernel(int* part_start,
+                                                           int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256)
+    part_start[i] = 0;
+}
+// ... then the shared partition count of each member's group (one workgroup
+// per group), for the members the prefix kernel's tiles cover.  A sequence
+// listed in several groups breaks a precondition (which group's partitions
+// it receives is then unspecified).
+__global__ __launch_bounds__(256) void prefix_mark_kernel(DecodeArgs a,
+                                                          int* part_start,
+                                                          int block_size) {
+  const int g = blockIdx.x;
+  const int m0 = a.grp_offsets[g];
+  int m1 = a.grp_offsets[g + 1];
+  m1 = m1 - m0 < a.grp_max_members ? m1 : m0 + a.grp_max_members;
+  const int parts = prefix_parts(a, g, block_size);
+  for (int i = m0 + (int)threadIdx.x; i < m1; i += 256) {
+    const int s = a.grp_members[i];
+    if (s >= 0 && s < a.num_seqs) part_start[s] = parts;
+  }
+}
+
+template <int D, int B, int G>
+__global__ __launch_bounds__(kThreads) void prefix_kernel(DecodeArgs a) {
+  using Path = MfmaPath<D, B, 16>;
+  constexpr int MPT = 16 / G;                  // members per tile
+  __shared__ typename Path::Smem sm;
+  const int kvh = blockIdx.x;
+  const int g = blockIdx.y / a.q_tiles;
+  const int tile = blockIdx.y % a.q_tiles;
+  const int p = blockIdx.z;
+  const int H = a.num_heads;
+  const int m0 = a.grp_offsets[g];
+  const int cnt = a.grp_offsets[g + 1] - m0;
+  const int j0 = tile * MPT;
+  if (cnt <= 0 || j0 >= cnt || p >= prefix_parts(a, g, B)) return;
+  const int nm = cnt - j0 < MPT ? cnt - j0 : MPT;
+  const int lead = a.grp_members[m0];          // its row holds the shared blocks
+  if (lead < 0 || lead >= a.num_seqs) return;
+  const int max_tok = a.max_blocks_per_seq * B;
+  const int t0 = p * a.partition_size;
+  const int t1 = t0 + a.partition_size;
+  const int col = threadIdx.x & 15;
+  const int mj = col / G;
+  const int ms = mj < nm ? a.grp_members[m0 + j0 + mj] : -1;
+  int n = (ms >= 0 && ms < a.num_seqs) ? a.context_lens[ms] : 0;
+  n = n < max_tok ? n : max_tok;
+  const bool ok = n > t0;                      // member has keys here
+  const int64_t qoff = ok ? ((int64_t)ms * H + (int64_t)kvh * G + col % G) * D : -1;
+  auto sink = [&](int c, int d, float mx, float L, float O) {
+    if (c / G >= nm) return;
+    const int s = a.grp_members[m0 + j0 + c / G];
+    if (s < 0 || s >= a.num_seqs) return;
+    int ns = a.context_lens[s];
+    ns = ns < max_tok ? ns : max_tok;
+    if (ns <= t0) return;                      // the reduce never reads it
+    const size_t pi =
+        ((size_t)s * H + (size_t)kvh * G + c % G) * a.max_partitions + p;
+    if (d == 0) {
+      a.ws_max[pi] = mx * kLn2;
+      a.ws_sum[pi] = L;
+    }
+    a.ws_out[pi * D + d] = O;
+  };
+  Path::run_cols(a, sm, kvh, lead, t0, t1, -1, sink, qoff, ok ? n - 1 : -1);
 }
 
 // One workgroup of D threads per (query head, query row): fold the
@@ -1267,7 +1365,7 @@ struct PathFor<128, B, 4, EB> {
   using type = MfmaSplitPath<128, B, 4, EB>;
 };
 
-enum class Op { kPartition, kBalanced, kOccupancy, kMulti };
+enum class Op { kPartition, kBalanced, kOccupancy, kMulti, kPrefix };
 
 // EB: bytes per cached element (2: fp16 pool, 1: fp8 e4m3 pool).  The fp8
 // pool has the balanced kernel only.
@@ -1292,6 +1390,9 @@ static hipError_t run_op(Op op, const DecodeArgs* a, dim3 grid,
         return hipGetLastError();
       case Op::kMulti:
         hipLaunchKernelGGL((multi_kernel<D, B, G>), grid, dim3(kThreads), 0, st, *a);
+        return hipGetLastError();
+      case Op::kPrefix:
+        hipLaunchKernelGGL((prefix_kernel<D, B, G>), grid, dim3(kThreads), 0, st, *a);
         return hipGetLastError();
       default:
         break;
@@ -1370,6 +1471,24 @@ hipError_t launch_multi(const DecodeArgs& a, int head_size, int block_size,
                         int group, dim3 grid, hipStream_t stream) {
   return dispatch(Op::kMulti, head_size, block_size, group, &a, grid, stream,
                   nullptr);
+}
+
+hipError_t launch_prefix(const DecodeArgs& a, int head_size, int block_size,
+                         int group, dim3 grid, hipStream_t stream) {
+  return dispatch(Op::kPrefix, head_size, block_size, group, &a, grid, stream,
+                  nullptr);
+}
+
+hipError_t launch_prefix_marks(const DecodeArgs& a, int block_size,
+                               int* part_start, hipStream_t stream) {
+  const int cg = a.num_seqs > 0 ? (a.num_seqs + 255) / 256 : 1;
+  hipLaunchKernelGGL(prefix_clear_kernel, dim3(cg < 1024 ? cg : 1024), dim3(256),
+                     0, stream, part_start, a.num_seqs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_groups <= 0) return e;
+  hipLaunchKernelGGL(prefix_mark_kernel, dim3(a.num_groups), dim3(256), 0,
+                     stream, a, part_start, block_size);
+  return hipGetLastError();
 }
 
 hipError_t launch_multi_reduce(const ReduceArgs& a, int head_size,

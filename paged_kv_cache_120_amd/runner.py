@@ -8,7 +8,9 @@ tokens, the cache write, then decode -- single-pass (``pa_decode``), split
 query tokens per sequence (``upload_multi``), ``multi_step`` runs
 ``pa_decode_multi`` after the same writes.  With an fp8 pool
 (``upload_fp8``), ``fp8_step`` runs the copies, ``pa_cache_write_fp8`` and
-``pa_decode_balanced_fp8``.  Inputs are plain arrays (a
+``pa_decode_balanced_fp8``.  ``upload_prefix`` + ``prefix_step`` run the
+writes, then ``pa_decode_shared_prefix`` with groups found by
+``prefix_groups``.  Inputs are plain arrays (a
 workload object with the attributes used below); this module only uploads
 them and calls the binding, so every step runs in the library's kernels.
 """
@@ -23,8 +25,9 @@ import torch
 from . import (pa_balanced_grid, pa_balanced_grid_fp8, pa_balanced_workspace_size,
                pa_cache_write, pa_cache_write_fp8, pa_copy_blocks, pa_decode,
                pa_decode_balanced, pa_decode_balanced_fp8, pa_decode_multi,
-               pa_decode_reduce, pa_decode_splitk, pa_decode_step,
-               pa_multi_workspace_size, pa_slot_mapping, pa_splitk_workspace_size)
+               pa_decode_reduce, pa_decode_shared_prefix, pa_decode_splitk,
+               pa_decode_step, pa_multi_workspace_size, pa_prefix_workspace_size,
+               pa_slot_mapping, pa_splitk_workspace_size)
 
 
 def _t(a, dev, dtype=None):
@@ -275,3 +278,72 @@ def fp8_step(step: DeviceStep, stream=None) -> None:
     run_phase_fp8(step.write, step.pool, step.block_size, step.k_scale, step.v_scale,
                   stream=stream)
     fp8_decode(step, stream=stream)
+
+
+# ---------------------------------------------------------------------------
+# shared-prefix decode
+# ---------------------------------------------------------------------------
+
+def prefix_groups(block_tables, context_lens, block_size: int):
+    """Groups of sequences whose table rows start with the same physical
+    blocks (what a scheduler knows from its reference counts): sequences are
+    grouped by their first block id; a group's shared block count is the
+    length of the members' common row prefix, at most min(n_i) // B full
+    blocks.  Returns (offsets, members, blocks) int32 arrays, groups of two
+    or more members only."""
+    bt = np.asarray(block_tables)
+    n = np.asarray(context_lens).astype(np.int64)
+    by_first = {}
+    for i in range(bt.shape[0]):
+        if n[i] >= block_size:
+            by_first.setdefault(int(bt[i, 0]), []).append(i)
+    offsets, members, blocks = [0], [], []
+    for first, mem in sorted(by_first.items()):
+        if len(mem) < 2:
+            continue
+        cap = int(min(n[m] for m in mem) // block_size)
+        rows = bt[mem, :cap]
+        same = (rows == rows[0]).all(axis=0)
+        k = int(np.argmin(same)) if not same.all() else cap
+        if k == 0:
+            continue
+        members += mem
+        offsets.append(len(members))
+        blocks.append(k)
+    return (np.asarray(offsets, np.int32), np.asarray(members, np.int32),
+            np.asarray(blocks, np.int32))
+
+
+def upload_prefix(w, device: str = "cuda", pool: Optional[torch.Tensor] = None,
+                  groups=None) -> DeviceStep:
+    """As upload, plus the shared-prefix groups of the step's tables (from
+    prefix_groups unless given) and the shared-prefix workspace."""
+    st = upload(w, device, pool)
+    dev = st.pool.device
+    if groups is None:
+        groups = prefix_groups(w.block_tables, w.context_lens, w.block_size)
+    off, mem, blk = groups
+    st.grp_offsets, st.grp_members, st.grp_blocks = (_t(off, dev), _t(mem, dev),
+                                                     _t(blk, dev))
+    st.grp_max_size = int(np.diff(off).max(initial=1)) if len(off) > 1 else 1
+    st.grp_max_blocks = int(blk.max(initial=0))
+    S, H, D = w.query.shape
+    nbytes = pa_prefix_workspace_size(S, H, D, w.max_blocks_per_seq, w.block_size,
+                                      w.partition_size)
+    st.prefix_workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    return st
+
+
+def prefix_decode(step: DeviceStep, stream=None) -> None:
+    pa_decode_shared_prefix(step.out, step.query, step.key_cache, step.value_cache,
+                            step.block_tables, step.context_lens, step.scale,
+                            step.partition_size, step.grp_offsets, step.grp_members,
+                            step.grp_blocks, step.grp_max_size, step.grp_max_blocks,
+                            step.prefix_workspace, stream=stream)
+
+
+def prefix_step(step: DeviceStep, stream=None) -> None:
+    """COW copies, slot mapping and cache write, then the shared-prefix
+    decode."""
+    write_step(step, stream=stream)
+    prefix_decode(step, stream=stream)

@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     for name in ["pa_cache_write", "pa_decode", "pa_decode_splitk", "pa_decode_reduce",
                  "pa_splitk_workspace_size", "pa_status_str", "pa_kv_cache_shape",
                  "pa_slot_mapping", "pa_copy_blocks", "pa_swap_blocks",
-                 "pa_cache_write_fp8", "pa_balanced_grid_fp8", "pa_decode_balanced_fp8"]:
+                 "pa_cache_write_fp8", "pa_balanced_grid_fp8", "pa_decode_balanced_fp8",
+                 "pa_prefix_workspace_size", "pa_decode_shared_prefix"]:
         assert name in syms
 
 
@@ -154,6 +155,26 @@ def test_fp8_validation(pa):
     b = list(a)
     b[7] = 0
     assert d(*b, 0.5, 0.5, 64, FAKE, need, None) == 0                # empty batch
+
+
+def test_shared_prefix_validation(pa):
+    L = pa.lib
+    need = pa.pa_prefix_workspace_size(2, 8, 128, 8, 16, 64)
+    assert need == pa.pa_splitk_workspace_size(2, 8, 128, 8, 16, 64) + 16
+    d = L.pa_decode_shared_prefix
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 8, 2, 128, 16, 10, 0.1, 64]
+    g = [FAKE, FAKE, FAKE, 3, 4, 8]
+    assert d(*a[:7], 0, *a[8:], *g, FAKE, need, None) == 0           # empty batch
+    assert d(*a[:14], 40, *g, FAKE, need, None) == 2                 # P % B
+    assert d(*a, FAKE, None, FAKE, 3, 4, 8, FAKE, need, None) == 1   # members NULL
+    assert d(*a, FAKE + 2, FAKE, FAKE, 3, 4, 8, FAKE, need, None) == 4
+    assert d(*a, *g, FAKE, need - 1, None) == 5
+    assert d(*a, *g, None, need, None) == 1
+    assert d(*a, FAKE, FAKE, FAKE, -1, 4, 8, FAKE, need, None) == 2
+    assert d(*a, FAKE, FAKE, FAKE, 70000, 4, 8, FAKE, need, None) == 2  # grid.y
+    b = list(a)
+    b[10] = 96
+    assert d(*b, *g, FAKE, need, None) == 3
 
 
 def test_binding_rejects_host_tensors(pa):
