@@ -317,8 +317,15 @@ pa_status pa_decode_shared_prefix(
   const int64_t pm = max_partitions(max_blocks_per_seq, block_size, partition_size);
   if (pm > 65535) return PA_ERR_SHAPE;        // grid.z
   const int32_t g = num_heads / num_kv_heads;
-  const int64_t per_tile = 16 / g;            // members per prefix tile
-  const int64_t tiles = (max_group_size + per_tile - 1) / per_tile;
+  // members per prefix tile: the whole-line body when it needs no more
+  // tiles than the 16-column body
+  const int64_t per16 = 16 / g;
+  const int64_t perw = pa::split_columns(head_size, g) / g;
+  const int64_t tiles16 = (max_group_size + per16 - 1) / per16;
+  const int64_t tilesw = perw > 0 ? (max_group_size + perw - 1) / perw : tiles16 + 1;
+  const bool whole_line = tilesw <= tiles16;
+  const int64_t per_tile = whole_line ? perw : per16;
+  const int64_t tiles = whole_line ? tilesw : tiles16;
   if ((int64_t)num_groups * (tiles > 0 ? tiles : 1) > 65535) return PA_ERR_SHAPE;
   if (!out || !workspace) return PA_ERR_NULL;
   if (num_groups > 0 && (!group_offsets || !group_members || !group_blocks))
@@ -363,7 +370,8 @@ pa_status pa_decode_shared_prefix(
   if (st != PA_OK) return st;
   if (num_groups > 0 && tiles > 0 && a.grp_max_parts > 0) {
     dim3 pg(num_kv_heads, (unsigned)(num_groups * tiles), (unsigned)a.grp_max_parts);
-    st = hip_status(pa::launch_prefix(a, head_size, block_size, g, pg, stream));
+    st = hip_status(pa::launch_prefix(a, head_size, block_size, g, pg,
+                                      whole_line, stream));
     if (st != PA_OK) return st;
   }
   a.part_start = part_start;
@@ -411,7 +419,14 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache,
     return PA_ERR_SHAPE;
   if (num_seqs == 0 || num_q_tokens == 0) return PA_OK;
   const int32_t g = num_heads / num_kv_heads;
-  const int64_t tiles = (max_q_per_seq + 16 / g - 1) / (16 / g);
+  // the whole-line body (split_columns/g query tokens per tile) when it needs
+  // no more tiles, i.e. no more K/V passes, than the 16-column body
+  const int64_t per16 = 16 / g;
+  const int64_t perw = pa::split_columns(head_size, g) / g;
+  const int64_t tiles16 = (max_q_per_seq + per16 - 1) / per16;
+  const int64_t tilesw = perw > 0 ? (max_q_per_seq + perw - 1) / perw : tiles16 + 1;
+  const bool whole_line = tilesw <= tiles16;
+  const int64_t tiles = whole_line ? tilesw : tiles16;
   const int64_t pm = max_partitions(max_blocks_per_seq, block_size, partition_size);
   if (pm > 65535 || (int64_t)num_seqs * tiles > 65535 || num_q_tokens > 65535)
     return PA_ERR_SHAPE;                      // grid.z, grid.y
@@ -444,7 +459,8 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache,
   a.q_tiles = (int)tiles;
   a.num_q_tokens = num_q_tokens;
   dim3 grid(num_kv_heads, (unsigned)(num_seqs * tiles), (unsigned)pm);
-  st = hip_status(pa::launch_multi(a, head_size, block_size, g, grid, stream));
+  st = hip_status(pa::launch_multi(a, head_size, block_size, g, grid,
+                                   whole_line, stream));
   if (st != PA_OK) return st;
   pa::ReduceArgs r = {};
   r.out = static_cast<_Float16*>(out);

@@ -70,8 +70,13 @@ hipError_t launch_decode(const DecodeArgs& a, int head_size, int block_size,
                          int group, dim3 grid, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_size, int num_seqs,
                          hipStream_t stream);
+// whole_line: the whole-line body with split_columns() columns per tile
+// instead of the 16-column body
 hipError_t launch_multi(const DecodeArgs& a, int head_size, int block_size,
-                        int group, dim3 grid, hipStream_t stream);
+                        int group, dim3 grid, bool whole_line,
+                        hipStream_t stream);
+// distinct (row, head) columns of the whole-line body for this shape
+int split_columns(int head_size, int group);
 hipError_t launch_multi_reduce(const ReduceArgs& a, int head_size,
                                int num_q_tokens, hipStream_t stream);
 // shared-prefix decode: part_start from the groups, then the prefix
@@ -80,7 +85,8 @@ hipError_t launch_multi_reduce(const ReduceArgs& a, int head_size,
 hipError_t launch_prefix_marks(const DecodeArgs& a, int block_size,
                                int* part_start, hipStream_t stream);
 hipError_t launch_prefix(const DecodeArgs& a, int head_size, int block_size,
-                         int group, dim3 grid, hipStream_t stream);
+                         int group, dim3 grid, bool whole_line,
+                         hipStream_t stream);
 // elem_bytes: 2 for an fp16 pool, 1 for an fp8 (e4m3) pool
 hipError_t launch_balanced(const DecodeArgs& a, int head_size, int block_size,
                            int group, int grid, hipStream_t stream,

@@ -630,31 +630,52 @@ struct MfmaSplitPath {
   }
 
   // t0 must be a multiple of 16; `last` as for ValuPath::run (fp16 only).
+  // Column c (c < G) is query head kvh*G + c of sequence seq.
   template <class Sink>
   __device__ static void run(const DecodeArgs& a, Smem& sm, int kvh, int seq,
                              int t0, int t1, int last, Sink& sink) {
+    const int hd = (threadIdx.x & 15) % G;
+    const int64_t qoff =
+        ((int64_t)seq * a.num_heads + (int64_t)kvh * G + hd) * D;
+    body<false>(a, sm, kvh, seq, t0, t1, last, sink, qoff, 0x7fffffff);
+  }
+
+  // The same over G columns given by the caller (fp16 pools): the lanes of
+  // column c = (lane%16)%G pass the same query-row element offset qoff
+  // (-1: an unused column, zero query) and key limit lim (keys t <= lim).
+  template <class Sink>
+  __device__ static void run_cols(const DecodeArgs& a, Smem& sm, int kvh,
+                                  int seq, int t0, int t1, Sink& sink,
+                                  int64_t qoff, int lim) {
+    body<true>(a, sm, kvh, seq, t0, t1, -1, sink, qoff, lim);
+  }
+
+  template <bool kCols, class Sink>
+  __device__ static void body(const DecodeArgs& a, Smem& sm, int kvh, int seq,
+                              int t0, int t1, int last, Sink& sink,
+                              int64_t qoff, int lim) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;
     const int grp = lane >> 4;
-    const int hd = col % G;                     // B column: head
     const int q = col / G;                      // B column: split
     if constexpr (EB == 2) {
       if (last >= 0) append_token<D, B>(a, kvh, seq, last);
     }
 
-    // B operand of load kl, k-step s: head hd, channels
+    // B operand of load kl, k-step s: column hd's query row, channels
     // kl*LC + q*4*CPL + grp*CPL + s*8 .. +7
     f16x8 qb[KL][KS];
-    const _Float16* qrow =
-        a.query + ((size_t)seq * a.num_heads + (size_t)kvh * G + hd) * D;
 #pragma unroll
     for (int kl = 0; kl < KL; ++kl)
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        qb[kl][s] = __builtin_bit_cast(
-            f16x8, *reinterpret_cast<const u32x4*>(
-                       qrow + kl * LC + q * 4 * CPL + grp * CPL + s * 8));
+      for (int s = 0; s < KS; ++s) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (!kCols || qoff >= 0)
+          v = *reinterpret_cast<const u32x4*>(
+              a.query + qoff + kl * LC + q * 4 * CPL + grp * CPL + s * 8);
+        qb[kl][s] = __builtin_bit_cast(f16x8, v);
+      }
 
     BlockWindow bw;
     bw.init(a.block_tables + (size_t)seq * a.max_blocks_per_seq, t0 / B,
@@ -669,7 +690,7 @@ struct MfmaSplitPath {
     const int rtok = col / R;
     const int rch = (col % R) * 4 * CPL + grp * CPL;
 
-    float m = -INFINITY;                        // reference of head hd
+    float m = -INFINITY;                        // reference of column col % G
     float mt = -INFINITY;                       // its true running max
     float l = 0.f;                              // this lane's share of the sum
     f32x4 o[DT];
@@ -719,7 +740,7 @@ struct MfmaSplitPath {
         }
       }
 
-      // scores of head hd: slot j = token tile0 + T(j)
+      // scores of column col % G: slot j = token tile0 + T(j)
       float sc[MT][4];
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
@@ -740,11 +761,12 @@ struct MfmaSplitPath {
             float p = av[R * u];
 #pragma unroll
             for (int k = 1; k < R; ++k) p = q == k ? av[k + R * u] : p;
-            // sum over the R lanes of head hd (bitwise equal in each)
+            // sum over the R lanes of column col % G (bitwise equal in each)
             if constexpr (R >= 2) p += dpp<kRowRor8>(p);
             if constexpr (R >= 4) p += dpp<kRowRor4>(p);
             const int tok = base + mi * 16 + rg * G + grp * U + u;
-            sc[mi][rg * U + u] = tok < t1 ? p * sl2 : -INFINITY;
+            sc[mi][rg * U + u] =
+                (tok < t1 && (!kCols || tok <= lim)) ? p * sl2 : -INFINITY;
           }
         }
       }
@@ -765,7 +787,7 @@ struct MfmaSplitPath {
               reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
             }
 
-      // online softmax for head hd (max over the batch and the 4 groups)
+      // online softmax for column col % G (max over the batch and the 4 groups)
       float bm = -INFINITY;
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi)
@@ -908,6 +930,14 @@ __global__ __launch_bounds__(D) void reduce_kernel(ReduceArgs a) {
     O += a.ws_out[(base + p) * D + d] * f;
   }
   *o = (_Float16)(O / S);
+}
+
+// Columns of the whole-line body for query tokens or group members: VG =
+// 4 distinct (row, head) columns at head size 128 for g <= 4, else 8 (the
+// split body needs at least 8 channels per lane and load).
+template <int D, int G>
+constexpr int split_cols() {
+  return (D == 128 && G <= 4) ? 4 : 8;
 }
 
 // ---------------------------------------------------------------------------
@@ -1063,6 +1093,100 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(DecodeArgs a) {
     a.ws_out[pi * D + d] = O;
   };
   Path::run_cols(a, sm, kvh, lead, t0, t1, -1, sink, qoff, ok ? n - 1 : -1);
+}
+
+// prefix_kernel on the whole-line body: VG/g members per tile.
+template <int D, int B, int G>
+__global__ __launch_bounds__(kThreads) void prefix_split_kernel(DecodeArgs a) {
+  constexpr int VG = split_cols<D, G>();
+  using Path = MfmaSplitPath<D, B, VG, 2>;
+  constexpr int MPT = VG / G;                  // members per tile
+  __shared__ typename Path::Smem sm;
+  const int kvh = blockIdx.x;
+  const int g = blockIdx.y / a.q_tiles;
+  const int tile = blockIdx.y % a.q_tiles;
+  const int p = blockIdx.z;
+  const int H = a.num_heads;
+  const int m0 = a.grp_offsets[g];
+  const int cnt = a.grp_offsets[g + 1] - m0;
+  const int j0 = tile * MPT;
+  if (cnt <= 0 || j0 >= cnt || p >= prefix_parts(a, g, B)) return;
+  const int nm = cnt - j0 < MPT ? cnt - j0 : MPT;
+  const int lead = a.grp_members[m0];          // its row holds the shared blocks
+  if (lead < 0 || lead >= a.num_seqs) return;
+  const int max_tok = a.max_blocks_per_seq * B;
+  const int t0 = p * a.partition_size;
+  const int t1 = t0 + a.partition_size;
+  const int col = (threadIdx.x & 15) % VG;
+  const int mj = col / G;
+  const int ms = mj < nm ? a.grp_members[m0 + j0 + mj] : -1;
+  int n = (ms >= 0 && ms < a.num_seqs) ? a.context_lens[ms] : 0;
+  n = n < max_tok ? n : max_tok;
+  const bool ok = n > t0;                      // member has keys here
+  const int64_t qoff = ok ? ((int64_t)ms * H + (int64_t)kvh * G + col % G) * D : -1;
+  auto sink = [&](int c, int d, float mx, float L, float O) {
+    if (c / G >= nm) return;
+    const int s = a.grp_members[m0 + j0 + c / G];
+    if (s < 0 || s >= a.num_seqs) return;
+    int ns = a.context_lens[s];
+    ns = ns < max_tok ? ns : max_tok;
+    if (ns <= t0) return;                      // the reduce never reads it
+    const size_t pi =
+        ((size_t)s * H + (size_t)kvh * G + c % G) * a.max_partitions + p;
+    if (d == 0) {
+      a.ws_max[pi] = mx * kLn2;
+      a.ws_sum[pi] = L;
+    }
+    a.ws_out[pi * D + d] = O;
+  };
+  Path::run_cols(a, sm, kvh, lead, t0, t1, sink, qoff, ok ? n - 1 : -1);
+}
+
+// multi_kernel on the whole-line body: VG/g query tokens per tile (used
+// when that needs no more tiles than the 16-column body).
+template <int D, int B, int G>
+__global__ __launch_bounds__(kThreads) void multi_split_kernel(DecodeArgs a) {
+  constexpr int VG = split_cols<D, G>();
+  using Path = MfmaSplitPath<D, B, VG, 2>;
+  constexpr int QT = VG / G;                   // query tokens per tile
+  __shared__ typename Path::Smem sm;
+  const int kvh = blockIdx.x;
+  const int seq = blockIdx.y / a.q_tiles;
+  const int tile = blockIdx.y % a.q_tiles;
+  const int p = blockIdx.z;
+  const int H = a.num_heads;
+  const int q0 = a.cu_seqlens_q[seq];
+  const int T = a.cu_seqlens_q[seq + 1] - q0;
+  const int max_tok = a.max_blocks_per_seq * B;
+  int n = a.context_lens[seq];
+  n = n < max_tok ? n : max_tok;
+  const int j0 = tile * QT;
+  if (T <= 0 || j0 >= T || n <= 0 || q0 < 0) return;
+  int nq = T - j0 < QT ? T - j0 : QT;
+  if (q0 + j0 + nq > a.num_q_tokens) nq = a.num_q_tokens - q0 - j0;
+  if (nq <= 0) return;
+  const int pos0 = n - T + j0;
+  const int lim_max = pos0 + nq - 1;
+  const int t0 = p * a.partition_size;
+  if (lim_max < 0 || t0 > lim_max) return;
+  const int t1 = t0 + a.partition_size < lim_max + 1 ? t0 + a.partition_size
+                                                     : lim_max + 1;
+  const int cc = (threadIdx.x & 15) % VG;
+  const int qj = cc / G;
+  const bool ok = qj < nq && pos0 + qj >= 0;
+  const int64_t qoff =
+      ok ? (((int64_t)q0 + j0 + qj) * H + (int64_t)kvh * G + cc % G) * D : -1;
+  auto sink = [&](int c, int d, float mx, float L, float O) {
+    if (c / G >= nq) return;
+    const size_t r = (size_t)q0 + j0 + c / G;
+    const size_t pi = (r * H + (size_t)kvh * G + c % G) * a.max_partitions + p;
+    if (d == 0) {
+      a.ws_max[pi] = mx * kLn2;
+      a.ws_sum[pi] = L;
+    }
+    a.ws_out[pi * D + d] = O;
+  };
+  Path::run_cols(a, sm, kvh, seq, t0, t1, sink, qoff, ok ? pos0 + qj : -1);
 }
 
 // One workgroup of D threads per (query head, query row): fold the
@@ -1365,7 +1489,8 @@ struct PathFor<128, B, 4, EB> {
   using type = MfmaSplitPath<128, B, 4, EB>;
 };
 
-enum class Op { kPartition, kBalanced, kOccupancy, kMulti, kPrefix };
+enum class Op { kPartition, kBalanced, kOccupancy, kMulti, kPrefix, kMultiSplit,
+                kPrefixSplit };
 
 // EB: bytes per cached element (2: fp16 pool, 1: fp8 e4m3 pool).  The fp8
 // pool has the balanced kernel only.
@@ -1393,6 +1518,12 @@ static hipError_t run_op(Op op, const DecodeArgs* a, dim3 grid,
         return hipGetLastError();
       case Op::kPrefix:
         hipLaunchKernelGGL((prefix_kernel<D, B, G>), grid, dim3(kThreads), 0, st, *a);
+        return hipGetLastError();
+      case Op::kMultiSplit:
+        hipLaunchKernelGGL((multi_split_kernel<D, B, G>), grid, dim3(kThreads), 0, st, *a);
+        return hipGetLastError();
+      case Op::kPrefixSplit:
+        hipLaunchKernelGGL((prefix_split_kernel<D, B, G>), grid, dim3(kThreads), 0, st, *a);
         return hipGetLastError();
       default:
         break;
@@ -1468,15 +1599,21 @@ int balanced_grid(int head_size, int block_size, int group, int elem_bytes) {
 }
 
 hipError_t launch_multi(const DecodeArgs& a, int head_size, int block_size,
-                        int group, dim3 grid, hipStream_t stream) {
-  return dispatch(Op::kMulti, head_size, block_size, group, &a, grid, stream,
-                  nullptr);
+                        int group, dim3 grid, bool whole_line,
+                        hipStream_t stream) {
+  return dispatch(whole_line ? Op::kMultiSplit : Op::kMulti, head_size,
+                  block_size, group, &a, grid, stream, nullptr);
 }
 
 hipError_t launch_prefix(const DecodeArgs& a, int head_size, int block_size,
-                         int group, dim3 grid, hipStream_t stream) {
-  return dispatch(Op::kPrefix, head_size, block_size, group, &a, grid, stream,
-                  nullptr);
+                         int group, dim3 grid, bool whole_line,
+                         hipStream_t stream) {
+  return dispatch(whole_line ? Op::kPrefixSplit : Op::kPrefix, head_size,
+                  block_size, group, &a, grid, stream, nullptr);
+}
+
+int split_columns(int head_size, int group) {
+  return (head_size == 128 && group <= 4) ? 4 : 8;
 }
 
 hipError_t launch_prefix_marks(const DecodeArgs& a, int block_size,
