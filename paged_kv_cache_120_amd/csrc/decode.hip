@@ -1026,27 +1026,28 @@ __device__ __forceinline__ int prefix_parts(const DecodeArgs& a, int g,
   return (int)(parts < a.grp_max_parts ? parts : a.grp_max_parts);
 }
 
-// part_start[s] = 0 for every sequence (grid over sequences) ...
-__global__ __launch_bounds__(256) void prefix_clear_kernel(int* part_start,
-                                                           int n) {
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256)
-    part_start[i] = 0;
-}
-// ... then the shared partition count of each member's group (one workgroup
-// per group), for the members the prefix kernel's tiles cover.  A sequence
-// listed in several groups breaks a precondition (which group's partitions
-// it receives is then unspecified).
-__global__ __launch_bounds__(256) void prefix_mark_kernel(DecodeArgs a,
-                                                          int* part_start,
-                                                          int block_size) {
-  const int g = blockIdx.x;
-  const int m0 = a.grp_offsets[g];
-  int m1 = a.grp_offsets[g + 1];
-  m1 = m1 - m0 < a.grp_max_members ? m1 : m0 + a.grp_max_members;
-  const int parts = prefix_parts(a, g, block_size);
-  for (int i = m0 + (int)threadIdx.x; i < m1; i += 256) {
-    const int s = a.grp_members[i];
-    if (s >= 0 && s < a.num_seqs) part_start[s] = parts;
+// part_start[s]: the shared partition count of the group that lists s (for
+// the members the prefix kernel's tiles cover), else 0.  One workgroup:
+// clear, then each thread takes member entries and finds their group by
+// binary search over the offsets.  A sequence listed in several groups
+// breaks a precondition (which group's partitions it receives is then
+// unspecified).
+__global__ __launch_bounds__(256) void prefix_marks_kernel(DecodeArgs a,
+                                                           int* part_start,
+                                                           int block_size) {
+  for (int i = threadIdx.x; i < a.num_seqs; i += 256) part_start[i] = 0;
+  __syncthreads();
+  if (a.num_groups <= 0) return;
+  const int total = a.grp_offsets[a.num_groups];
+  for (int e = a.grp_offsets[0] + (int)threadIdx.x; e < total; e += 256) {
+    int lo = 0, hi = a.num_groups - 1;      // last group with offset <= e
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.grp_offsets[mid] <= e) lo = mid; else hi = mid - 1;
+    }
+    if (e - a.grp_offsets[lo] >= a.grp_max_members) continue;
+    const int s = a.grp_members[e];
+    if (s >= 0 && s < a.num_seqs) part_start[s] = prefix_parts(a, lo, block_size);
   }
 }
 
@@ -1618,13 +1619,8 @@ int split_columns(int head_size, int group) {
 
 hipError_t launch_prefix_marks(const DecodeArgs& a, int block_size,
                                int* part_start, hipStream_t stream) {
-  const int cg = a.num_seqs > 0 ? (a.num_seqs + 255) / 256 : 1;
-  hipLaunchKernelGGL(prefix_clear_kernel, dim3(cg < 1024 ? cg : 1024), dim3(256),
-                     0, stream, part_start, a.num_seqs);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.num_groups <= 0) return e;
-  hipLaunchKernelGGL(prefix_mark_kernel, dim3(a.num_groups), dim3(256), 0,
-                     stream, a, part_start, block_size);
+  hipLaunchKernelGGL(prefix_marks_kernel, dim3(1), dim3(256), 0, stream, a,
+                     part_start, block_size);
   return hipGetLastError();
 }
 
