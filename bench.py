@@ -391,7 +391,8 @@ def fp8_scales(w):
 
 def fp8_bench(args, w, dev) -> int:
     """Decode over an fp8 (e4m3) pool: COW copies, slot mapping,
-    pa_cache_write_fp8 of the new tokens, then pa_decode_balanced_fp8."""
+    pa_cache_write_fp8 of the new tokens, then pa_decode_balanced_fp8; the
+    one-kernel pa_decode_step_fp8 step is timed too (fused_step_ms)."""
     import torch
     from paged_kv_cache_120_amd import runner
     ks, vs = fp8_scales(w)
@@ -417,9 +418,12 @@ def fp8_bench(args, w, dev) -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    ms_step = timed(runner.fp8_step)
+    # the step as two launches (fp8 cache write, then the decode) is timed;
+    # the one-kernel step (pa_decode_step_fp8) is reported beside it
+    ms_step = timed(lambda st: runner.fp8_step(st, fused=False))
+    ms_fused = timed(runner.fp8_step)
     kms = timed(runner.fp8_decode)
-    runner.fp8_step(steps[(args.steps - 1) % R])
+    runner.fp8_step(steps[(args.steps - 1) % R], fused=False)
     torch.cuda.synchronize()
     kvb = kv_bytes(w) // 2                         # one byte per element
     S, H, D = w.query.shape
@@ -441,6 +445,7 @@ def fp8_bench(args, w, dev) -> int:
                    "seed": w.seed, "balanced_grid": steps[0].grid},
         "accumulate": "f32", "kv_bytes_per_step": kvb,
         "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "fused_step_ms": round(ms_fused, 5),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -580,8 +585,9 @@ def main(argv=None) -> int:
                          "swap: pa_swap_blocks of the batch's blocks to pinned host memory "
                          "and back (its own JSON line); multi: cache write of each "
                          "sequence's query chunk + pa_decode_multi (the *_spec4 configs); "
-                         "fp8: the balanced decode over an e4m3 pool (fp8 cache write + "
-                         "pa_decode_balanced_fp8, its own JSON line); prefix: writes + "
+                         "fp8: fp8 cache write + pa_decode_balanced_fp8 over an e4m3 "
+                         "pool, the one-kernel pa_decode_step_fp8 beside it (its own "
+                         "JSON line); prefix: writes + "
                          "pa_decode_shared_prefix (c4; its own JSON line)")
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--partition", type=int, default=512)

@@ -326,6 +326,11 @@ pa_status pa_decode_shared_prefix(
  *   query and output fp16).  The result is attention over the dequantised
  *   K and V (codes times their scales), within the fp16 path's tolerance
  *   of that.  Scales as above.
+ * pa_decode_step_fp8: pa_decode_step over an fp8 pool: each sequence's new
+ *   K/V row (fp16) is quantised exactly as pa_cache_write_fp8 does, stored
+ *   into its slot, and attended to in that quantised form, in one kernel;
+ *   the same as pa_slot_mapping + pa_cache_write_fp8 +
+ *   pa_decode_balanced_fp8.  Grid from pa_balanced_grid_fp8.
  */
 pa_status pa_cache_write_fp8(const void* key, const void* value,
                              void* key_cache, void* value_cache,
@@ -335,6 +340,17 @@ pa_status pa_cache_write_fp8(const void* key, const void* value,
                              float k_scale, float v_scale, hipStream_t stream);
 int32_t pa_balanced_grid_fp8(int32_t num_heads, int32_t num_kv_heads,
                              int32_t head_size, int32_t block_size);
+pa_status pa_decode_step_fp8(void* out, const void* query, const void* key,
+                             const void* value, void* key_cache,
+                             void* value_cache, int32_t* slot_mapping,
+                             const int32_t* block_tables,
+                             int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs,
+                             int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_size, int32_t block_size,
+                             int32_t num_blocks, float scale, float k_scale,
+                             float v_scale, int32_t grid, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 pa_status pa_decode_balanced_fp8(void* out, const void* query,
                                  const void* key_cache, const void* value_cache,
                                  const int32_t* block_tables,

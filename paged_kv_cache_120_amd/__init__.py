@@ -21,6 +21,7 @@ __all__ = [
     "pa_balanced_grid", "pa_balanced_workspace_size", "pa_decode_balanced",
     "pa_decode_step", "pa_multi_workspace_size", "pa_decode_multi",
     "pa_cache_write_fp8", "pa_balanced_grid_fp8", "pa_decode_balanced_fp8",
+    "pa_decode_step_fp8",
     "pa_prefix_workspace_size", "pa_decode_shared_prefix", "STATUS",
 ]
 
@@ -74,6 +75,9 @@ def _load() -> ctypes.CDLL:
         "pa_cache_write_fp8": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                               f32, f32, vp]),
         "pa_balanced_grid_fp8": (i32, [i32, i32, i32, i32]),
+        "pa_decode_step_fp8": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                              i32, i32, i32, i32, i32, i32, f32, f32, f32,
+                                              i32, vp, sz, vp]),
         "pa_prefix_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
         "pa_decode_shared_prefix": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32,
                                                    i32, i32, i32, i32, f32, i32, vp, vp,
@@ -454,6 +458,35 @@ def pa_decode_shared_prefix(out, query, key_cache, value_cache, block_tables,
         _dev(group_members, torch.int32, "group_members", 1),
         _dev(group_blocks, torch.int32, "group_blocks", 1), G, int(max_group_size),
         int(max_group_blocks), ws, nbytes, _stream(stream)))
+
+
+def pa_decode_step_fp8(out, query, key, value, key_cache, value_cache, block_tables,
+                       context_lens, scale: float, k_scale: float, v_scale: float,
+                       grid: int, workspace, slot_mapping=None, stream=None) -> None:
+    """pa_decode_step over an fp8 pool: key/value ([S, H_kv, D] fp16) are
+    quantised into their slots and attended to in that form."""
+    torch = _torch()
+    S, H, D = query.shape
+    nb, B, Hkv, D2 = key_cache.shape
+    if D2 != D or tuple(value_cache.shape) != (nb, B, Hkv, D):
+        raise ValueError("decode: inconsistent head_size / cache shapes")
+    if block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("decode: block_tables / context_lens do not match query")
+    if tuple(out.shape) != (S, H, D) or tuple(key.shape) != (S, Hkv, D) \
+            or tuple(value.shape) != (S, Hkv, D):
+        raise ValueError("pa_decode_step_fp8: shapes")
+    sm = None if slot_mapping is None else _dev(slot_mapping, torch.int32,
+                                                "slot_mapping", 1)
+    ws = _dev(workspace, workspace.dtype, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("pa_decode_step_fp8", _lib().pa_decode_step_fp8(
+        _dev(out, torch.float16, "out", 3), _dev(query, torch.float16, "query", 3),
+        _dev(key, torch.float16, "key", 3), _dev(value, torch.float16, "value", 3),
+        _dev_fp8(key_cache, "key_cache", 4), _dev_fp8(value_cache, "value_cache", 4), sm,
+        _dev(block_tables, torch.int32, "block_tables", 2), block_tables.shape[1],
+        _dev(context_lens, torch.int32, "context_lens", 1), S, H, Hkv, D, B, nb,
+        float(scale), float(k_scale), float(v_scale), int(grid), ws, nbytes,
+        _stream(stream)))
 
 
 def pa_decode_step(out, query, key, value, key_cache, value_cache, block_tables,

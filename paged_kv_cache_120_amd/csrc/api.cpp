@@ -604,6 +604,8 @@ static pa_status balanced_impl(void* out, const void* query, void* key_cache,
   a.scale = scale;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.inv_k_scale = 1.f / k_scale;
+  a.inv_v_scale = 1.f / v_scale;
   return hip_status(pa::launch_balanced(a, head_size, block_size, g, grid,
                                         stream, elem_bytes));
 }
@@ -645,6 +647,28 @@ pa_status pa_decode_balanced_fp8(void* out, const void* query,
                        num_kv_heads, head_size, block_size, num_blocks, scale,
                        grid, workspace, workspace_bytes, nullptr, nullptr,
                        nullptr, stream, 1, k_scale, v_scale);
+}
+
+pa_status pa_decode_step_fp8(void* out, const void* query, const void* key,
+                             const void* value, void* key_cache,
+                             void* value_cache, int32_t* slot_mapping,
+                             const int32_t* block_tables,
+                             int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs,
+                             int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_size, int32_t block_size,
+                             int32_t num_blocks, float scale, float k_scale,
+                             float v_scale, int32_t grid, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (!(isfinite(k_scale) && k_scale > 0.f) ||
+      !(isfinite(v_scale) && v_scale > 0.f))
+    return PA_ERR_SHAPE;
+  if (num_seqs > 0 && (!key || !value)) return PA_ERR_NULL;
+  return balanced_impl(out, query, key_cache, value_cache, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                       num_kv_heads, head_size, block_size, num_blocks, scale,
+                       grid, workspace, workspace_bytes, key, value,
+                       slot_mapping, stream, 1, k_scale, v_scale);
 }
 
 pa_status pa_decode_step(void* out, const void* query, const void* key,

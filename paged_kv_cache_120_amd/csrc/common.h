@@ -64,6 +64,37 @@ __device__ __forceinline__ u32x4 fp8x8_to_f16x8(u32x2 w) {
   return r;
 }
 
+// e4m3 code pair of x*inv and y*inv: the conversion rounds to nearest even
+// and gives NaN above the largest finite code, so values are clamped to
+// +-448 first (NaN inputs stay NaN).  Result in the low or high 16 bits of
+// `old` as `hi` says.
+__device__ __forceinline__ int fp8_pair(float x, float y, float inv, int old,
+                                        bool hi) {
+  float u = x * inv, v = y * inv;
+  u = u > 448.f ? 448.f : (u < -448.f ? -448.f : u);
+  v = v > 448.f ? 448.f : (v < -448.f ? -448.f : v);
+  return hi ? __builtin_amdgcn_cvt_pk_fp8_f32(u, v, old, true)
+            : __builtin_amdgcn_cvt_pk_fp8_f32(u, v, old, false);
+}
+
+__device__ __forceinline__ u32x2 f16x8_to_fp8x8(u32x4 h, float inv) {
+  const unsigned w[4] = {h.x, h.y, h.z, h.w};
+  float f[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f[2 * k] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[k] & 0xffffu));
+    f[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[k] >> 16));
+  }
+  int lo = fp8_pair(f[0], f[1], inv, 0, false);
+  lo = fp8_pair(f[2], f[3], inv, lo, true);
+  int hi = fp8_pair(f[4], f[5], inv, 0, false);
+  hi = fp8_pair(f[6], f[7], inv, hi, true);
+  u32x2 r;
+  r.x = (unsigned)lo;
+  r.y = (unsigned)hi;
+  return r;
+}
+
 // Cross-lane moves inside a 16-lane DPP row (all lanes must be active).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {

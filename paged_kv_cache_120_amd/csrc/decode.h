@@ -39,6 +39,8 @@ struct DecodeArgs {
   // fp8 pools: dequantisation scales (value = code * scale)
   float k_scale;
   float v_scale;
+  float inv_k_scale;     // fused fp8 append: 1/scale rounded to fp32
+  float inv_v_scale;
   // shared-prefix decode: per-sequence first partition left to the
   // partition kernel (earlier ones come from the prefix kernel), and the
   // groups (member lists in CSR form, shared full blocks per group)

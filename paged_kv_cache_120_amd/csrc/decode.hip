@@ -86,10 +86,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(
 }
 
 // Fused append: store this step's K/V row of head kvh (token `last` of the
-// sequence) into its slot, bit for bit, and record the slot.  Called by the
-// one range that holds token `last`; lanes 0 .. D/8-1 of wave 0 each move 16
-// bytes.  A slot outside the pool is skipped, as in the cache write.
-template <int D, int B>
+// sequence) into its slot and record the slot.  Called by the one range
+// that holds token `last`; lanes 0 .. D/8-1 of wave 0 each move 8 elements:
+// 16 bytes bit for bit into an fp16 pool, or their 8 e4m3 codes (quantised
+// as pa_cache_write_fp8 does) into an fp8 pool.  A slot outside the pool is
+// skipped, as in the cache write.
+template <int D, int B, int EB>
 __device__ __forceinline__ void append_token(const DecodeArgs& a, int kvh,
                                              int seq, int last) {
   if (threadIdx.x >= D / 8) return;
@@ -100,12 +102,19 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, int kvh,
     a.slot_out[seq] = ok ? (int)slot : -1;
   if (!ok) return;
   const size_t src = ((size_t)seq * a.num_kv_heads + kvh) * D + threadIdx.x * 8;
-  const size_t dst = (size_t)slot * a.num_kv_heads * D + (size_t)kvh * D +
-                     threadIdx.x * 8;
-  _Float16* kc = const_cast<_Float16*>(reinterpret_cast<const _Float16*>(a.key_cache));
-  _Float16* vc = const_cast<_Float16*>(reinterpret_cast<const _Float16*>(a.value_cache));
-  *reinterpret_cast<u32x4*>(kc + dst) = *reinterpret_cast<const u32x4*>(a.new_key + src);
-  *reinterpret_cast<u32x4*>(vc + dst) = *reinterpret_cast<const u32x4*>(a.new_value + src);
+  const size_t dst = ((size_t)slot * a.num_kv_heads * D + (size_t)kvh * D +
+                      threadIdx.x * 8) * EB;
+  char* kc = const_cast<char*>(a.key_cache);
+  char* vc = const_cast<char*>(a.value_cache);
+  const u32x4 k = *reinterpret_cast<const u32x4*>(a.new_key + src);
+  const u32x4 v = *reinterpret_cast<const u32x4*>(a.new_value + src);
+  if constexpr (EB == 2) {
+    *reinterpret_cast<u32x4*>(kc + dst) = k;
+    *reinterpret_cast<u32x4*>(vc + dst) = v;
+  } else {
+    *reinterpret_cast<u32x2*>(kc + dst) = f16x8_to_fp8x8(k, a.inv_k_scale);
+    *reinterpret_cast<u32x2*>(vc + dst) = f16x8_to_fp8x8(v, a.inv_v_scale);
+  }
 }
 
 // Final cross-wave merge.  Each wave left (m, l) per head and acc[head][d] in
@@ -191,9 +200,7 @@ struct ValuPath {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane / LPR;
     const int c = lane % LPR;
-    if constexpr (EB == 2) {
-      if (last >= 0) append_token<D, B>(a, kvh, seq, last);
-    }
+    if (last >= 0) append_token<D, B, EB>(a, kvh, seq, last);
 
     u32x4 qv[G];
 #pragma unroll
@@ -239,14 +246,19 @@ struct ValuPath {
         kk[j] = KvLoad<EB>::load(rk, off);
         vv[j] = KvLoad<EB>::load(rv, off);
       }
-      if constexpr (EB == 2) {
-        if (last >= 0 && base + TB > last) {   // the appended row
-          const size_t src = ((size_t)seq * a.num_kv_heads + kvh) * D + c * 8;
+      if (last >= 0 && base + TB > last) {   // the appended row
+        const size_t src = ((size_t)seq * a.num_kv_heads + kvh) * D + c * 8;
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            if (base + j * RPI + r == last) {
-              kk[j] = *reinterpret_cast<const u32x4*>(a.new_key + src);
-              vv[j] = *reinterpret_cast<const u32x4*>(a.new_value + src);
+        for (int j = 0; j < NJ; ++j) {
+          if (base + j * RPI + r == last) {
+            const u32x4 nk = *reinterpret_cast<const u32x4*>(a.new_key + src);
+            const u32x4 nv = *reinterpret_cast<const u32x4*>(a.new_value + src);
+            if constexpr (EB == 2) {
+              kk[j] = nk;
+              vv[j] = nv;
+            } else {   // the codes the append stores
+              kk[j] = f16x8_to_fp8x8(nk, a.inv_k_scale);
+              vv[j] = f16x8_to_fp8x8(nv, a.inv_v_scale);
             }
           }
         }
@@ -388,29 +400,18 @@ struct MfmaPath {
     float l[kWaves][G];
   };
 
-  // t0 must be a multiple of 16; `last` as for ValuPath::run.  Column c
-  // (c < G) is query head kvh*G + c of sequence seq.
-  template <class Sink>
-  __device__ static void run(const DecodeArgs& a, Smem& sm, int kvh, int seq,
-                             int t0, int t1, int last, Sink& sink) {
-    const int col = threadIdx.x & 15;
-    const int64_t qoff =
-        col < G ? ((int64_t)seq * a.num_heads + (int64_t)kvh * G + col) * D : -1;
-    run_cols(a, sm, kvh, seq, t0, t1, last, sink, qoff, 0x7fffffff);
-  }
-
-  // The same over columns given by the caller: this lane's column reads the
-  // query row at element offset qoff (-1: an unused column, zero query) and
-  // attends to keys t <= lim only (the causal limit of a query token).
+  // Keys [t0, t1) of head kvh (t0 a multiple of 16) for 16 columns given
+  // by the caller: this lane's column reads the query row at element offset
+  // qoff (-1: an unused column, zero query) and attends to keys t <= lim
+  // only (the causal limit of a query token).
   template <class Sink>
   __device__ static void run_cols(const DecodeArgs& a, Smem& sm, int kvh,
-                                  int seq, int t0, int t1, int last, Sink& sink,
+                                  int seq, int t0, int t1, Sink& sink,
                                   int64_t qoff, int lim) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;                  // token row (A) / column (B, D)
     const int grp = lane >> 4;                  // lane group 0..3
-    if (last >= 0) append_token<D, B>(a, kvh, seq, last);
 
     f16x8 qb[KK];
 #pragma unroll
@@ -456,22 +457,6 @@ struct MfmaPath {
         for (int kk = 0; kk < KK; ++kk) {
           kr[mt][kk] = load16<kLoadCached>(rk, off + kk * 64);   // half lines
           vr[mt][kk] = load16<kLoadCached>(rv, off + kk * 64);
-        }
-      }
-      {
-        if (last >= 0 && base + TB > last) {   // the appended row
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            if (base + mt * 16 + col == last) {
-              const size_t src =
-                  ((size_t)seq * a.num_kv_heads + kvh) * D + grp * 8;
-#pragma unroll
-              for (int kk = 0; kk < KK; ++kk) {
-                kr[mt][kk] = *reinterpret_cast<const u32x4*>(a.new_key + src + kk * 32);
-                vr[mt][kk] = *reinterpret_cast<const u32x4*>(a.new_value + src + kk * 32);
-              }
-            }
-          }
         }
       }
 
@@ -629,7 +614,22 @@ struct MfmaSplitPath {
     }
   }
 
-  // t0 must be a multiple of 16; `last` as for ValuPath::run (fp16 only).
+  // this lane's chunk of the appended row (CPL channels from p) in the
+  // pool's form: fp16 bits, or the codes the append stores
+  __device__ static Raw appended(const _Float16* p, float inv) {
+    if constexpr (EB == 2) {
+      return *reinterpret_cast<const u32x4*>(p);
+    } else if constexpr (CPL == 8) {
+      return f16x8_to_fp8x8(*reinterpret_cast<const u32x4*>(p), inv);
+    } else {
+      const u32x2 lo = f16x8_to_fp8x8(*reinterpret_cast<const u32x4*>(p), inv);
+      const u32x2 hi = f16x8_to_fp8x8(*reinterpret_cast<const u32x4*>(p + 8), inv);
+      const unsigned a0 = lo.x, a1 = lo.y, b0 = hi.x, b1 = hi.y;
+      return (u32x4){a0, a1, b0, b1};
+    }
+  }
+
+  // t0 must be a multiple of 16; `last` as for ValuPath::run.
   // Column c (c < G) is query head kvh*G + c of sequence seq.
   template <class Sink>
   __device__ static void run(const DecodeArgs& a, Smem& sm, int kvh, int seq,
@@ -659,9 +659,7 @@ struct MfmaSplitPath {
     const int col = lane & 15;
     const int grp = lane >> 4;
     const int q = col / G;                      // B column: split
-    if constexpr (EB == 2) {
-      if (last >= 0) append_token<D, B>(a, kvh, seq, last);
-    }
+    if (last >= 0) append_token<D, B, EB>(a, kvh, seq, last);
 
     // B operand of load kl, k-step s: column hd's query row, channels
     // kl*LC + q*4*CPL + grp*CPL + s*8 .. +7
@@ -721,23 +719,19 @@ struct MfmaSplitPath {
           }
         }
       }
-      if constexpr (EB == 2) {
-        if (last >= 0 && base + TB > last) {   // the appended row
-          const size_t src = ((size_t)seq * a.num_kv_heads + kvh) * D + rch;
+      if (last >= 0 && base + TB > last) {   // the appended row
+        const size_t src = ((size_t)seq * a.num_kv_heads + kvh) * D + rch;
 #pragma unroll
-          for (int mi = 0; mi < MT; ++mi)
+        for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-            for (int rg = 0; rg < R; ++rg)
-              if (base + mi * 16 + rg * G + rtok == last) {
+          for (int rg = 0; rg < R; ++rg)
+            if (base + mi * 16 + rg * G + rtok == last) {
 #pragma unroll
-                for (int kl = 0; kl < KL; ++kl) {
-                  kr[mi][rg][kl] =
-                      *reinterpret_cast<const u32x4*>(a.new_key + src + kl * LC);
-                  vr[mi][rg][kl] =
-                      *reinterpret_cast<const u32x4*>(a.new_value + src + kl * LC);
-                }
+              for (int kl = 0; kl < KL; ++kl) {
+                kr[mi][rg][kl] = appended(a.new_key + src + kl * LC, a.inv_k_scale);
+                vr[mi][rg][kl] = appended(a.new_value + src + kl * LC, a.inv_v_scale);
               }
-        }
+            }
       }
 
       // scores of column col % G: slot j = token tile0 + T(j)
@@ -996,7 +990,7 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(DecodeArgs a) {
     }
     a.ws_out[pi * D + d] = O;
   };
-  Path::run_cols(a, sm, kvh, seq, t0, t1, -1, sink, qoff, ok ? pos0 + qj : -1);
+  Path::run_cols(a, sm, kvh, seq, t0, t1, sink, qoff, ok ? pos0 + qj : -1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1093,7 +1087,7 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(DecodeArgs a) {
     }
     a.ws_out[pi * D + d] = O;
   };
-  Path::run_cols(a, sm, kvh, lead, t0, t1, -1, sink, qoff, ok ? n - 1 : -1);
+  Path::run_cols(a, sm, kvh, lead, t0, t1, sink, qoff, ok ? n - 1 : -1);
 }
 
 // prefix_kernel on the whole-line body: VG/g members per tile.

@@ -25,6 +25,7 @@ import torch
 from . import (pa_balanced_grid, pa_balanced_grid_fp8, pa_balanced_workspace_size,
                pa_cache_write, pa_cache_write_fp8, pa_copy_blocks, pa_decode,
                pa_decode_balanced, pa_decode_balanced_fp8, pa_decode_multi,
+               pa_decode_step_fp8,
                pa_decode_reduce, pa_decode_shared_prefix, pa_decode_splitk,
                pa_decode_step, pa_multi_workspace_size, pa_prefix_workspace_size,
                pa_slot_mapping, pa_splitk_workspace_size)
@@ -271,10 +272,23 @@ def fp8_decode(step: DeviceStep, stream=None) -> None:
                            stream=stream)
 
 
-def fp8_step(step: DeviceStep, stream=None) -> None:
-    """COW copies, slot mapping, fp8 cache write, then the fp8 decode."""
+def fp8_fused(step: DeviceStep, stream=None) -> None:
+    """pa_decode_step_fp8: quantised append + decode in one kernel."""
+    wr = step.write
+    pa_decode_step_fp8(step.out, step.query, wr.key, wr.value, step.key_cache,
+                       step.value_cache, step.block_tables, step.context_lens,
+                       step.scale, step.k_scale, step.v_scale, step.grid,
+                       step.bal_workspace, slot_mapping=wr.slots, stream=stream)
+
+
+def fp8_step(step: DeviceStep, fused: bool = True, stream=None) -> None:
+    """COW copies, then either the fused fp8 step or slot mapping + fp8
+    cache write + the fp8 decode."""
     run_phase_fp8(step.copies, step.pool, step.block_size, step.k_scale, step.v_scale,
                   stream=stream)
+    if fused:
+        fp8_fused(step, stream=stream)
+        return
     run_phase_fp8(step.write, step.pool, step.block_size, step.k_scale, step.v_scale,
                   stream=stream)
     fp8_decode(step, stream=stream)

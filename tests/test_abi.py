@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
                  "pa_splitk_workspace_size", "pa_status_str", "pa_kv_cache_shape",
                  "pa_slot_mapping", "pa_copy_blocks", "pa_swap_blocks",
                  "pa_cache_write_fp8", "pa_balanced_grid_fp8", "pa_decode_balanced_fp8",
-                 "pa_prefix_workspace_size", "pa_decode_shared_prefix"]:
+                 "pa_decode_step_fp8", "pa_prefix_workspace_size",
+                 "pa_decode_shared_prefix"]:
         assert name in syms
 
 
@@ -155,6 +156,17 @@ def test_fp8_validation(pa):
     b = list(a)
     b[7] = 0
     assert d(*b, 0.5, 0.5, 64, FAKE, need, None) == 0                # empty batch
+    st = L.pa_decode_step_fp8
+    sa = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 8, FAKE, 2, 8, 2, 128, 16, 10, 0.1]
+    assert st(*sa, 0.0, 0.5, 64, FAKE, need, None) == 2                  # k_scale
+    assert st(*sa, 0.5, float("nan"), 64, FAKE, need, None) == 2         # v_scale
+    sb = list(sa)
+    sb[2] = None
+    assert st(*sb, 0.5, 0.5, 64, FAKE, need, None) == 1                  # key NULL
+    sb = list(sa)
+    sb[10] = 0
+    assert st(*sb, 0.5, 0.5, 64, FAKE, need, None) == 0                  # empty batch
+    assert st(*sa, 0.5, 0.5, 64, FAKE, need - 1, None) == 5
 
 
 def test_shared_prefix_validation(pa):

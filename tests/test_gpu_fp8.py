@@ -23,14 +23,17 @@ def _gpu():
     return runner
 
 
-def check_fp8(w, kind="calibrated", pairs=None):
+def check_fp8(w, kind="calibrated", pairs=None, fused=False):
     runner = _gpu()
     ks, vs = fp8_scales(w, kind)
     st = runner.upload_fp8(w, ks, vs)
     runner.apply_history_fp8(w, st)
-    runner.fp8_step(st)
+    runner.fp8_step(st, fused=fused)
     torch.cuda.synchronize()
     kc, vc = oracle_pool_fp8(w, oracle, ks, vs)
+    ref_slots = oracle.slot_mapping(w.step_write.table, w.step_write.seq,
+                                    w.step_write.pos, w.block_size)
+    assert (st.write.slots.cpu().numpy() == ref_slots).all()
     gpool = st.pool.cpu().numpy()
     assert (gpool[0] == kc).all(), f"fp8 key cache differs in {(gpool[0] != kc).sum()} bytes"
     assert (gpool[1] == vc).all(), f"fp8 value cache differs in {(gpool[1] != vc).sum()} bytes"
@@ -52,24 +55,34 @@ def test_fp8_parity_small(name, kind):
     check_fp8(workloads.make(name), kind)
 
 
+@pytest.mark.parametrize("name", SMALL)
+def test_fp8_fused_step_parity_small(name):
+    """pa_decode_step_fp8: the quantised append lands bit-exactly and the
+    attention uses it."""
+    print(f"[fp8-fused] {name}", flush=True)
+    check_fp8(workloads.make(name), "calibrated", fused=True)
+
+
 @pytest.mark.parametrize("D,B,H,Hkv", [(128, 16, 32, 8), (64, 64, 16, 2),
                                        (128, 32, 8, 8), (64, 16, 8, 4),
                                        (128, 64, 16, 8)])
-def test_fp8_edge_lengths(D, B, H, Hkv):
-    print(f"[fp8-edge] D{D} B{B} H{H}/{Hkv}", flush=True)
+@pytest.mark.parametrize("fused", [False, True])
+def test_fp8_edge_lengths(D, B, H, Hkv, fused):
+    print(f"[fp8-edge] D{D} B{B} H{H}/{Hkv} fused={fused}", flush=True)
     w = workloads.make("c1", D=D, B=B, H=H, Hkv=Hkv, lens=EDGE_LENS,
                        pool=("choice_scale", 1.3), max_context=2048, seed=D + B + H)
-    check_fp8(w)
+    check_fp8(w, fused=fused)
 
 
-@pytest.mark.parametrize("name", ["c2", "c3"])
-def test_fp8_parity_full(name):
-    print(f"[fp8-full] {name}", flush=True)
+@pytest.mark.parametrize("name,fused", [("c2", False), ("c3", False), ("c2", True),
+                                        ("c3", True)])
+def test_fp8_parity_full(name, fused):
+    print(f"[fp8-full] {name} fused={fused}", flush=True)
     w = workloads.make(name)
     rng = np.random.default_rng(11)
     pairs = [(i, int(h)) for i in range(w.num_seqs)
              for h in rng.choice(w.num_heads, 4, replace=False)]
-    check_fp8(w, pairs=sorted(pairs))
+    check_fp8(w, pairs=sorted(pairs), fused=fused)
 
 
 def test_fp8_zero_context_and_any_grid():

@@ -27,7 +27,12 @@ def test_tables_counts_and_refcounts(name):
     for i, n in enumerate(w.context_lens):
         k = oracle.blocks_needed(int(n), B)
         assert (w.ref_cnt[w.block_tables[i, k:]] == 0).all()
-    assert np.isfinite(w.pool_init.view(np.float16).astype(np.float32)).all()
+    # finite fp16 garbage: no all-ones exponent field (Inf / NaN); checked in
+    # chunks so no pool-sized temporary is allocated
+    flat = w.pool_init.reshape(-1)
+    for i in range(0, flat.size, 1 << 22):
+        c = flat[i:i + (1 << 22)]
+        assert ((c & np.uint16(0x7C00)) != np.uint16(0x7C00)).all()
 
 
 def test_worked_example_tables_used_verbatim():
