@@ -598,9 +598,9 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(decode shards by sequence or KV head with no exchange; see the design "
-              "notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(decode shards by sequence or by KV head with no exchange between "
+              "GPUs). Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
