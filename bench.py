@@ -64,26 +64,32 @@ def split_kernel_bytes(w) -> int:
     return kv_bytes(w) + S * H * D * 2 + table + parts
 
 
+PAIR_COST = 64      # flat units the balanced split charges per (sequence, kv head)
+
+
 def balanced_split_ranges(w, grid: int) -> int:
     """Ranges of the balanced decode that belong to (sequence, kv head)
     pairs cut across several workgroups: each stores one partial state per
-    query head, which the pair's last workgroup reads back to merge."""
+    query head, which the pair's last workgroup reads back to merge.  Same
+    slicing as the kernel: a pair spans PAIR_COST units, then its length
+    padded to 16; equal 16-aligned slices of that space."""
     M = w.max_blocks_per_seq * w.block_size
     n = np.minimum(w.context_lens.astype(np.int64), M)
     pad = np.where(n > 0, (n + 15) // 16 * 16, 0)
+    span = np.where(pad > 0, pad + PAIR_COST, 0)
     Hkv = w.num_kv_heads
-    total = int(pad.sum()) * Hkv
+    total = int(span.sum()) * Hkv
     if total == 0:
         return 0
     C = -(-total // grid)
     C = (C + 15) // 16 * 16
-    prefix = np.concatenate([[0], np.cumsum(pad)[:-1]])
+    prefix = np.concatenate([[0], np.cumsum(span)[:-1]])
     count = 0
     for i in range(w.num_seqs):
         if n[i] <= 0:
             continue
         for kvh in range(Hkv):
-            F = int(prefix[i]) * Hkv + kvh * int(pad[i])
+            F = int(prefix[i]) * Hkv + kvh * int(span[i]) + PAIR_COST
             k = (F + int(n[i]) - 1) // C - F // C + 1
             if k > 1:
                 count += k
