@@ -423,6 +423,45 @@ def test_multi_token_parity(name):
     assert_attention_close(st.out.cpu().numpy(), ref, f"{name}/multi")
 
 
+@pytest.mark.parametrize("D,B,H,Hkv,T", [(128, 16, 16, 8, 2), (64, 32, 8, 8, 8),
+                                         (128, 16, 8, 8, 3), (64, 16, 16, 2, 1),
+                                         (128, 64, 64, 8, 1), (128, 32, 32, 8, 5)])
+def test_multi_token_shapes(D, B, H, Hkv, T):
+    """Shapes that run the whole-line body (g*T within its 4 or 8 columns,
+    partial tiles) and the 16-column body (g = 4, T = 5)."""
+    print(f"[multi-shape] D{D} B{B} H{H}/{Hkv} T{T}", flush=True)
+    w = workloads.make("c2_small_spec4", D=D, B=B, H=H, Hkv=Hkv, q_len=T,
+                       seed=D + B + H + T)
+    st = run_multi(w)
+    kc, vc = oracle_pool(w, oracle)
+    ref = oracle.decode_multi(w.query, kc, vc, w.block_tables, w.info["cu_seqlens_q"],
+                              w.context_lens, w.scale)
+    assert_attention_close(st.out.cpu().numpy(), ref, f"multi D{D} g{H // Hkv} T{T}")
+
+
+def test_multi_and_prefix_repeat_calls_bitwise():
+    """The multi-token and shared-prefix decodes give the same bits on
+    repeated calls (no atomics in their reductions)."""
+    pa, runner = _gpu()
+    w = workloads.make("c2_small_spec4")
+    st = run_multi(w)
+    first = st.out.clone()
+    for _ in range(3):
+        runner.multi_step(st)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), st.out.view(torch.int16))
+    w = workloads.make("c4_small")
+    st = runner.upload_prefix(w)
+    runner.apply_history(w, st)
+    runner.prefix_step(st)
+    torch.cuda.synchronize()
+    first = st.out.clone()
+    for _ in range(3):
+        runner.prefix_decode(st)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), st.out.view(torch.int16))
+
+
 def test_multi_token_zero_length_sequence_and_partition_sizes():
     """A sequence with no query rows contributes none and leaves its
     neighbours' rows exact; results agree across partition sizes."""

@@ -110,3 +110,15 @@ def test_zero_context_member_and_out_of_range_ids():
     kc, vc = oracle_pool(w, oracle)
     ref = oracle.decode(w.query[keep], kc, vc, w.block_tables[keep], ctx[keep], w.scale)
     assert_attention_close(out[keep], ref, "zero-context member")
+
+
+@pytest.mark.parametrize("D,H,Hkv", [(64, 16, 8), (128, 32, 8), (64, 8, 8), (128, 16, 8)])
+def test_shared_prefix_shapes(D, H, Hkv):
+    """Head sizes 64/128 and groups 1-4: the whole-line prefix body where its
+    tile holds a group's members, the 16-column body where it does not."""
+    print(f"[prefix-shape] D{D} H{H}/{Hkv}", flush=True)
+    w = workloads.make("c4_small", D=D, H=H, Hkv=Hkv)
+    st = run_prefix(w)
+    kc, vc = oracle_pool(w, oracle)
+    ref = oracle.decode(w.query, kc, vc, w.block_tables, w.context_lens, w.scale)
+    assert_attention_close(st.out.cpu().numpy(), ref, f"prefix D{D} g{H // Hkv}")
