@@ -294,7 +294,9 @@ def multi_kernel_bytes(w) -> int:
 
 def multi_bench(args, w, dev) -> int:
     """Steps of several query tokens per sequence: slot mapping + cache write
-    of every sequence's chunk, then pa_decode_multi (partitions + reduce)."""
+    of every sequence's chunk, then pa_decode_multi_balanced (one kernel)
+    when each sequence's rows x heads fit 16 columns, else pa_decode_multi
+    (partitions + reduce); the partition path's step is reported beside."""
     import torch
     import paged_kv_cache_120_amd as pa
     from paged_kv_cache_120_amd import runner
@@ -323,11 +325,26 @@ def multi_bench(args, w, dev) -> int:
 
     ms_step = timed(full)
     kms = timed(runner.multi_step)
+    balanced = steps[0].multi_grid > 0
+    ms_part = timed(lambda st: (runner.write_step(st), runner.multi_step(st, balanced=False)))
     full(steps[(args.steps - 1) % R])
     torch.cuda.synchronize()
     Q = int(w.query.shape[0])
     kvb = kv_bytes(w)
-    kb = multi_kernel_bytes(w)
+    if balanced:
+        # the balanced kernel: K/V once, query rows in, outputs out, table,
+        # and the states of cut pairs (written, read back) for the rows x
+        # heads in use
+        n = w.context_lens.astype(np.int64)
+        table = int(((n + w.block_size - 1) // w.block_size).sum()) * 4
+        cols = Q / w.num_seqs * w.group
+        kb = int(kvb + 2 * Q * w.num_heads * w.head_size * 2 + table
+                 + 2 * balanced_split_ranges(w, steps[0].multi_grid) * cols
+                 * (w.head_size + 2) * 4)
+        kname = "balanced_kernel (multi-token rows)"
+    else:
+        kb = multi_kernel_bytes(w)
+        kname = "multi_kernel + multi_reduce_kernel"
     achieved = kb / (kms * 1e-3) / 1e9
     rec = {
         "metric": "paged multi-token (speculative verify) KV GB/s + query tokens/s",
@@ -343,10 +360,11 @@ def multi_bench(args, w, dev) -> int:
                    "rotated_pool_copies": R, "seed": w.seed},
         "accumulate": "f32", "kv_bytes_per_step": kvb,
         "query_tokens_per_s": round(Q / (ms_step * 1e-3), 1),
+        "partition_path_step_ms": round(ms_part, 5),
         "pct_hbm_peak": round(100 * kvb / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "multi_kernel + multi_reduce_kernel",
+                     "traffic": None, "kernel": kname,
                      "kernel_ms": round(kms, 5), "algorithmic_bytes": kb},
     }
     if not args.no_cpu_baseline:

@@ -260,6 +260,41 @@ pa_status pa_decode_balanced(void* out, const void* query,
                              hipStream_t stream);
 
 /*
+ * Multi-token queries on the balanced split: pa_decode_multi's result
+ * (same rows, causal limits and tolerance) in ONE kernel, with the work of
+ * every (sequence, kv head) pair cut into equal slices as for
+ * pa_decode_balanced and cut pairs merged in-kernel.  A sequence's T query
+ * rows x g heads share one pass over its keys, so T * g <= 16 is required
+ * (max_q_per_seq * g > 16: PA_ERR_UNSUPPORTED; use pa_decode_multi).
+ * Rows of a sequence with context_lens <= 0, and rows placed before the
+ * first key (T > n), get zeros.
+ * pa_multi_balanced_grid: resident workgroups of this kernel for this
+ *   max_q_per_seq (0 if unsupported or unknown); pass the same
+ *   max_q_per_seq to pa_decode_multi_balanced, which picks the whole-line
+ *   matrix-core body when max_q_per_seq * g fits its 4 or 8 columns and
+ *   the 16-column body otherwise.
+ * pa_multi_balanced_workspace_size: int32 counters [num_seqs *
+ *   num_kv_heads] padded to 16 bytes, then fp32 max/sum [rows] and out
+ *   [rows, head_size], rows = (grid + num_seqs * num_kv_heads) * 16.  Zero-
+ *   fill once before the first call; each completed call leaves the
+ *   counters zero; calls sharing a workspace must not overlap.
+ * Other arguments as pa_decode_multi ([BOOK] §4.5 (2)).
+ */
+int32_t pa_multi_balanced_grid(int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_size, int32_t block_size,
+                               int32_t max_q_per_seq);
+size_t pa_multi_balanced_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
+                                        int32_t head_size, int32_t grid);
+pa_status pa_decode_multi_balanced(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* cu_seqlens_q, int32_t num_q_tokens, int32_t max_q_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+    int32_t num_blocks, float scale, int32_t grid, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Shared-prefix decode: the same result as pa_decode_splitk +
  * pa_decode_reduce (same partitions, same reduce; within pa_decode's
  * tolerance of the exact attention), but a partition that lies inside the

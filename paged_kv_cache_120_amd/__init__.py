@@ -21,7 +21,8 @@ __all__ = [
     "pa_balanced_grid", "pa_balanced_workspace_size", "pa_decode_balanced",
     "pa_decode_step", "pa_multi_workspace_size", "pa_decode_multi",
     "pa_cache_write_fp8", "pa_balanced_grid_fp8", "pa_decode_balanced_fp8",
-    "pa_decode_step_fp8",
+    "pa_decode_step_fp8", "pa_multi_balanced_grid", "pa_multi_balanced_workspace_size",
+    "pa_decode_multi_balanced",
     "pa_prefix_workspace_size", "pa_decode_shared_prefix", "STATUS",
 ]
 
@@ -79,6 +80,11 @@ def _load() -> ctypes.CDLL:
                                               i32, i32, i32, i32, i32, i32, f32, f32, f32,
                                               i32, vp, sz, vp]),
         "pa_prefix_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
+        "pa_multi_balanced_grid": (i32, [i32, i32, i32, i32, i32]),
+        "pa_multi_balanced_workspace_size": (sz, [i32, i32, i32, i32]),
+        "pa_decode_multi_balanced": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32,
+                                                    vp, i32, i32, i32, i32, i32, i32, f32,
+                                                    i32, vp, sz, vp]),
         "pa_decode_shared_prefix": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32,
                                                    i32, i32, i32, i32, f32, i32, vp, vp,
                                                    vp, i32, i32, i32, vp, sz, vp]),
@@ -140,6 +146,20 @@ def pa_balanced_grid_fp8(num_heads: int, num_kv_heads: int, head_size: int,
     """As pa_balanced_grid, for the decode over an fp8 pool."""
     return int(_lib().pa_balanced_grid_fp8(num_heads, num_kv_heads, head_size,
                                            block_size))
+
+
+def pa_multi_balanced_grid(num_heads: int, num_kv_heads: int, head_size: int,
+                           block_size: int, max_q_per_seq: int) -> int:
+    """Resident workgroups of the balanced multi-token kernel for this many
+    query rows per sequence (0 if unsupported or unknown)."""
+    return int(_lib().pa_multi_balanced_grid(num_heads, num_kv_heads, head_size,
+                                             block_size, max_q_per_seq))
+
+
+def pa_multi_balanced_workspace_size(num_seqs: int, num_kv_heads: int, head_size: int,
+                                     grid: int) -> int:
+    return int(_lib().pa_multi_balanced_workspace_size(num_seqs, num_kv_heads, head_size,
+                                                       grid))
 
 
 def pa_prefix_workspace_size(num_seqs: int, num_heads: int, head_size: int,
@@ -375,6 +395,31 @@ def pa_decode_multi(out, query, key_cache, value_cache, block_tables, cu_seqlens
         _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q", 1), Q, int(max_q_per_seq),
         _dev(context_lens, torch.int32, "context_lens", 1), S, H, Hkv, D, B, nb,
         float(scale), int(partition_size), ws, nbytes, _stream(stream)))
+
+
+def pa_decode_multi_balanced(out, query, key_cache, value_cache, block_tables,
+                             cu_seqlens_q, context_lens, max_q_per_seq: int, scale: float,
+                             grid: int, workspace, stream=None) -> None:
+    """pa_decode_multi on the balanced split, one kernel (T*g <= 16 per
+    sequence); workspace zero-filled before its first use."""
+    torch = _torch()
+    Q, H, D = query.shape
+    nb, B, Hkv, D2 = key_cache.shape
+    S = context_lens.shape[0]
+    if D2 != D or tuple(value_cache.shape) != (nb, B, Hkv, D) or tuple(out.shape) != (Q, H, D):
+        raise ValueError("pa_decode_multi_balanced: inconsistent shapes")
+    if block_tables.shape[0] != S or tuple(cu_seqlens_q.shape) != (S + 1,):
+        raise ValueError("pa_decode_multi_balanced: block_tables / cu_seqlens_q do not match")
+    ws = _dev(workspace, workspace.dtype, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("pa_decode_multi_balanced", _lib().pa_decode_multi_balanced(
+        _dev(out, torch.float16, "out", 3), _dev(query, torch.float16, "query", 3),
+        _dev(key_cache, torch.float16, "key_cache", 4),
+        _dev(value_cache, torch.float16, "value_cache", 4),
+        _dev(block_tables, torch.int32, "block_tables", 2), block_tables.shape[1],
+        _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q", 1), Q, int(max_q_per_seq),
+        _dev(context_lens, torch.int32, "context_lens", 1), S, H, Hkv, D, B, nb,
+        float(scale), int(grid), ws, nbytes, _stream(stream)))
 
 
 def pa_decode_reduce(out, workspace, context_lens, max_blocks_per_seq: int,

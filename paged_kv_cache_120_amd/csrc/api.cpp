@@ -55,6 +55,13 @@ int64_t max_partitions(int32_t max_blocks_per_seq, int32_t block_size,
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// Balanced-split workspaces: [counters int32 x S*H_kv] padded to 16 bytes,
+// then max, sum (fp32 [rows]) and out (fp32 [rows, D]), rows = (grid +
+// S*H_kv) * columns per pair (g for decode, 16 for multi-token rows).
+size_t balanced_header_bytes(int32_t num_seqs, int32_t num_kv_heads) {
+  return ((size_t)num_seqs * num_kv_heads * 4 + 15) & ~(size_t)15;
+}
+
 }  // namespace
 
 extern "C" {
@@ -477,6 +484,86 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache,
   return hip_status(pa::launch_multi_reduce(r, head_size, num_q_tokens, stream));
 }
 
+// the whole-line body when a sequence's rows x heads fit its columns
+static bool multi_whole_line(int32_t head_size, int32_t g, int32_t max_q) {
+  return (int64_t)max_q * g <= pa::split_columns(head_size, g);
+}
+
+int32_t pa_multi_balanced_grid(int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_size, int32_t block_size,
+                               int32_t max_q_per_seq) {
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+      !supported_head(head_size) || !supported_block(block_size) ||
+      !supported_group(num_heads / num_kv_heads) || max_q_per_seq <= 0 ||
+      (int64_t)max_q_per_seq * (num_heads / num_kv_heads) > 16)
+    return 0;
+  const int32_t g = num_heads / num_kv_heads;
+  return pa::multi_balanced_grid(head_size, block_size, g,
+                                 multi_whole_line(head_size, g, max_q_per_seq));
+}
+
+// [counters int32 x S*H_kv] padded to 16 bytes, then max, sum (fp32 [rows])
+// and out (fp32 [rows, D]) with rows = (grid + S*H_kv) * 16.
+size_t pa_multi_balanced_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
+                                        int32_t head_size, int32_t grid) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || head_size <= 0 || grid <= 0) return 0;
+  const uint64_t rows = ((uint64_t)grid + (uint64_t)num_seqs * num_kv_heads) * 16;
+  return balanced_header_bytes(num_seqs, num_kv_heads) +
+         (size_t)(rows * 8 + rows * head_size * 4);
+}
+
+pa_status pa_decode_multi_balanced(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* cu_seqlens_q, int32_t num_q_tokens, int32_t max_q_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+    int32_t num_blocks, float scale, int32_t grid, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  pa_status st = check_decode(query, key_cache, value_cache, block_tables,
+                              max_blocks_per_seq, context_lens, num_seqs,
+                              num_heads, num_kv_heads, head_size, block_size,
+                              num_blocks, scale);
+  if (st != PA_OK) return st;
+  if (num_q_tokens < 0 || max_q_per_seq <= 0 || grid <= 0 || grid > (1 << 20))
+    return PA_ERR_SHAPE;
+  const int32_t g = num_heads / num_kv_heads;
+  if ((int64_t)max_q_per_seq * g > 16) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_q_tokens == 0) return PA_OK;
+  if (!out || !cu_seqlens_q || !workspace) return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(workspace, 16) || !aligned(cu_seqlens_q, 4))
+    return PA_ERR_ALIGN;
+  if (workspace_bytes <
+      pa_multi_balanced_workspace_size(num_seqs, num_kv_heads, head_size, grid))
+    return PA_ERR_WORKSPACE;
+  const size_t rows = ((size_t)grid + (size_t)num_seqs * num_kv_heads) * 16;
+  char* ws = static_cast<char*>(workspace);
+  float* fmax = reinterpret_cast<float*>(ws + balanced_header_bytes(num_seqs, num_kv_heads));
+  pa::DecodeArgs a = {};
+  a.out = static_cast<_Float16*>(out);
+  a.ws_max = fmax;
+  a.ws_sum = fmax + rows;
+  a.ws_out = fmax + 2 * rows;
+  a.query = static_cast<const _Float16*>(query);
+  a.key_cache = static_cast<const char*>(key_cache);
+  a.value_cache = static_cast<const char*>(value_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.bal_count = reinterpret_cast<int*>(ws);
+  a.split = 1;
+  a.scale = scale;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.num_q_tokens = num_q_tokens;
+  return hip_status(pa::launch_multi_balanced(
+      a, head_size, block_size, g, grid,
+      multi_whole_line(head_size, g, max_q_per_seq), stream));
+}
+
 pa_status pa_decode_reduce(void* out, const void* workspace,
                            size_t workspace_bytes,
                            const int32_t* context_lens, int32_t num_seqs,
@@ -531,11 +618,6 @@ int32_t pa_balanced_grid_fp8(int32_t num_heads, int32_t num_kv_heads,
   return pa::balanced_grid(head_size, block_size, num_heads / num_kv_heads, 1);
 }
 
-// [counters int32 x S*H_kv] padded to 16 bytes, then max, sum (fp32 [rows])
-// and out (fp32 [rows, D]) with rows = (grid + S*H_kv) * g.
-static size_t balanced_header_bytes(int32_t num_seqs, int32_t num_kv_heads) {
-  return ((size_t)num_seqs * num_kv_heads * 4 + 15) & ~(size_t)15;
-}
 
 size_t pa_balanced_workspace_size(int32_t num_seqs, int32_t num_heads,
                                   int32_t num_kv_heads, int32_t head_size,

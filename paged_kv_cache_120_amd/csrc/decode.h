@@ -77,6 +77,14 @@ hipError_t launch_reduce(const ReduceArgs& a, int head_size, int num_seqs,
 hipError_t launch_multi(const DecodeArgs& a, int head_size, int block_size,
                         int group, dim3 grid, bool whole_line,
                         hipStream_t stream);
+// multi-token queries on the balanced split (T*g <= 16 rows x heads per
+// sequence, one kernel; whole_line: the split body, T*g <= split_columns());
+// grid = resident workgroups of that kernel
+hipError_t launch_multi_balanced(const DecodeArgs& a, int head_size,
+                                 int block_size, int group, int grid,
+                                 bool whole_line, hipStream_t stream);
+int multi_balanced_grid(int head_size, int block_size, int group,
+                        bool whole_line);
 // distinct (row, head) columns of the whole-line body for this shape
 int split_columns(int head_size, int group);
 hipError_t launch_multi_reduce(const ReduceArgs& a, int head_size,

@@ -1303,17 +1303,94 @@ __device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* wave_sum,
 }
 
 
-template <class Path, int D, int B, int G>
+// What a (sequence, kv head) pair of the balanced split computes, and where
+// its NC columns go.  DecodeCols: one query row per sequence, the pair's g
+// heads.  MultiCols: the sequence's T query rows x g heads (T*g <= NC), each
+// row with its causal key limit, on the whole-line matrix-core body (NC = 4
+// or 8 columns) or the 16-column one.
+template <class P, int D, int G>
+struct DecodeCols {
+  using Path = P;
+  static constexpr int NC = G;
+  template <class Sink>
+  __device__ static void run(const DecodeArgs& a, typename P::Smem& sm, int kvh,
+                             int s, int n, int ta, int tv, int last, Sink& sink) {
+    P::run(a, sm, kvh, s, ta, tv, last, sink);
+  }
+  // output rows of a pair: computed once per range, then per column
+  struct Out {
+    int64_t base;
+  };
+  __device__ static Out out_of(const DecodeArgs& a, int s, int kvh) {
+    return {((int64_t)s * a.num_heads + (int64_t)kvh * G) * D};
+  }
+  __device__ static int64_t out_elem(const DecodeArgs&, const Out& o, int c) {
+    return o.base + (int64_t)c * D;
+  }
+  // every column of a decode range has keys, so L > 0
+  __device__ static float finish(float O, float L) { return O / L; }
+  __device__ static void clear_rows(const DecodeArgs& a, int s) {
+    u32x4* o = reinterpret_cast<u32x4*>(a.out + (size_t)s * a.num_heads * D);
+    for (int k = 0; k < a.num_heads * D / 8; ++k) o[k] = (u32x4){0u, 0u, 0u, 0u};
+  }
+};
+
+template <class P, int NCOLS, int D, int G>
+struct MultiCols {
+  using Path = P;
+  static constexpr int NC = NCOLS;
+  // query row of column c (c / G-th of the sequence's rows), -1 if none
+  __device__ static int64_t row_of(const DecodeArgs& a, int s, int c) {
+    const int q0 = a.cu_seqlens_q[s];
+    const int T = a.cu_seqlens_q[s + 1] - q0;
+    const int qj = c / G;
+    if (q0 < 0 || qj >= T || q0 + qj >= a.num_q_tokens) return -1;
+    return (int64_t)q0 + qj;
+  }
+  template <class Sink>
+  __device__ static void run(const DecodeArgs& a, typename Path::Smem& sm, int kvh,
+                             int s, int n, int ta, int tv, int, Sink& sink) {
+    const int col = (threadIdx.x & 15) % NC;
+    const int64_t r = row_of(a, s, col);
+    const int T = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
+    const int pos = n - T + col / G;           // this row's position
+    const bool ok = r >= 0 && pos >= 0;
+    const int64_t qoff =
+        ok ? (r * a.num_heads + (int64_t)kvh * G + col % G) * D : -1;
+    Path::run_cols(a, sm, kvh, s, ta, tv, sink, qoff, ok ? pos : -1);
+  }
+  struct Out {
+    int s, kvh;
+  };
+  __device__ static Out out_of(const DecodeArgs&, int s, int kvh) { return {s, kvh}; }
+  __device__ static int64_t out_elem(const DecodeArgs& a, const Out& o, int c) {
+    const int64_t r = row_of(a, o.s, c);
+    return r < 0 ? -1 : (r * a.num_heads + (int64_t)o.kvh * G + c % G) * D;
+  }
+  // a row placed before the first key (T > n) has none: zeros
+  __device__ static float finish(float O, float L) { return L > 0.f ? O / L : 0.f; }
+  __device__ static void clear_rows(const DecodeArgs& a, int s) {
+    const int q0 = a.cu_seqlens_q[s];
+    int q1 = a.cu_seqlens_q[s + 1];
+    q1 = q1 < a.num_q_tokens ? q1 : a.num_q_tokens;
+    for (int r = q0 < 0 ? 0 : q0; r < q1; ++r) {
+      u32x4* o = reinterpret_cast<u32x4*>(a.out + (size_t)r * a.num_heads * D);
+      for (int k = 0; k < a.num_heads * D / 8; ++k) o[k] = (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
+};
+
+template <class Cols, int D, int B, int G>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(Path::kMinWaves))) void balanced_kernel(
+__attribute__((amdgpu_waves_per_eu(Cols::Path::kMinWaves))) void balanced_kernel(
     DecodeArgs a) {
-  __shared__ typename Path::Smem sm;
+  constexpr int NC = Cols::NC;
+  __shared__ typename Cols::Path::Smem sm;
   __shared__ int64_t wave_sum[kWaves];
   __shared__ int64_t found_start;
   __shared__ int found_seq;
   __shared__ int merge_here;
   const int S = a.num_seqs;
-  const int H = a.num_heads;
   const int Hkv = a.num_kv_heads;
   const int max_tok = a.max_blocks_per_seq * B;
   const int w = blockIdx.x;
@@ -1330,8 +1407,7 @@ __attribute__((amdgpu_waves_per_eu(Path::kMinWaves))) void balanced_kernel(
     const int64_t len = si < S ? span_len(ns, max_tok) : 0;
     if (w == 0 && ns <= 0) {
       if (a.slot_out) a.slot_out[si] = -1;
-      u32x4* o = reinterpret_cast<u32x4*>(a.out + (size_t)si * H * D);
-      for (int k = 0; k < H * D / 8; ++k) o[k] = (u32x4){0u, 0u, 0u, 0u};
+      Cols::clear_rows(a, si);
     }
     int64_t chunk = 0;
     const int64_t inc = block_scan(len, wave_sum, chunk);
@@ -1395,23 +1471,24 @@ __attribute__((amdgpu_waves_per_eu(Path::kMinWaves))) void balanced_kernel(
       const int64_t wl = (F + n - 1) / C;             // slice of the last token
       const int64_t q = (int64_t)s * Hkv + kvh;
       const int last = (a.new_key && tv == n) ? n - 1 : -1;
-      const size_t orow = ((size_t)s * H + (size_t)kvh * G) * D;
+      const typename Cols::Out orow = Cols::out_of(a, s, kvh);
       if (w0 == wl) {
         auto sink = [&](int gi, int d, float, float L, float O) {
-          a.out[orow + (size_t)gi * D + d] = (_Float16)(O / L);
+          const int64_t oe = Cols::out_elem(a, orow, gi);
+          if (oe >= 0) a.out[oe + d] = (_Float16)(Cols::finish(O, L));
         };
-        Path::run(a, sm, kvh, s, ta, tv, last, sink);
+        Cols::run(a, sm, kvh, s, n, ta, tv, last, sink);
       } else {
         const int64_t slot = (int64_t)w + q;
         auto sink = [&](int gi, int d, float mx, float L, float O) {
-          const size_t pi = (size_t)slot * G + gi;
+          const size_t pi = (size_t)slot * NC + gi;
           if (d == 0) {
             publish(a.ws_max + pi, mx * kLn2);
             publish(a.ws_sum + pi, L);
           }
           publish(a.ws_out + pi * D + d, O);
         };
-        Path::run(a, sm, kvh, s, ta, tv, last, sink);
+        Cols::run(a, sm, kvh, s, n, ta, tv, last, sink);
         // every thread's state stores acknowledged, then count this range
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -1421,9 +1498,11 @@ __attribute__((amdgpu_waves_per_eu(Path::kMinWaves))) void balanced_kernel(
                        (int)(wl - w0);
         __syncthreads();
         if (merge_here) {
-          for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+          for (int idx = threadIdx.x; idx < NC * D; idx += kThreads) {
             const int gi = idx / D;
             const int d = idx % D;
+            const int64_t oe = Cols::out_elem(a, orow, gi);
+            if (oe < 0) continue;
             float mx = -INFINITY, L = 0.f, O = 0.f;
             // kMergeBatch ranges' states in flight at once, then folded
             for (int64_t w1 = w0; w1 <= wl; w1 += kMergeBatch) {
@@ -1431,7 +1510,7 @@ __attribute__((amdgpu_waves_per_eu(Path::kMinWaves))) void balanced_kernel(
 #pragma unroll
               for (int k = 0; k < kMergeBatch; ++k) {
                 const int64_t wr = w1 + k <= wl ? w1 + k : wl;
-                const size_t pi = (size_t)(wr + q) * G + gi;
+                const size_t pi = (size_t)(wr + q) * NC + gi;
                 mp[k] = fetch(a.ws_max + pi);
                 lp[k] = fetch(a.ws_sum + pi);
                 op[k] = fetch(a.ws_out + pi * D + d);
@@ -1453,7 +1532,7 @@ __attribute__((amdgpu_waves_per_eu(Path::kMinWaves))) void balanced_kernel(
               }
               mx = mn;
             }
-            a.out[orow + idx] = (_Float16)(O / L);
+            a.out[oe + d] = (_Float16)(Cols::finish(O, L));
           }
           if (threadIdx.x == 0) a.bal_count[q] = 0;    // ready for next call
         }
@@ -1498,7 +1577,8 @@ struct PathFor<128, B, 4, EB> {
 };
 
 enum class Op { kPartition, kBalanced, kOccupancy, kMulti, kPrefix, kMultiSplit,
-                kPrefixSplit };
+                kPrefixSplit, kMultiBalanced, kMultiOccupancy, kMultiBalancedSplit,
+                kMultiSplitOccupancy };
 
 // EB: bytes per cached element (2: fp16 pool, 1: fp8 e4m3 pool).  The fp8
 // pool has the balanced kernel only.
@@ -1506,17 +1586,21 @@ template <int D, int B, int G, int EB>
 static hipError_t run_op(Op op, const DecodeArgs* a, dim3 grid,
                          hipStream_t st, int* occ) {
   using P = typename PathFor<D, B, G, EB>::type;
+  using DC = DecodeCols<P, D, G>;
   switch (op) {
     case Op::kBalanced:
-      hipLaunchKernelGGL((balanced_kernel<P, D, B, G>), grid, dim3(kThreads), 0, st, *a);
+      hipLaunchKernelGGL((balanced_kernel<DC, D, B, G>), grid, dim3(kThreads), 0, st, *a);
       return hipGetLastError();
     case Op::kOccupancy:
       return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          occ, reinterpret_cast<const void*>(&balanced_kernel<P, D, B, G>), kThreads, 0);
+          occ, reinterpret_cast<const void*>(&balanced_kernel<DC, D, B, G>), kThreads, 0);
     default:
       break;
   }
   if constexpr (EB == 2) {
+    using MC16 = MultiCols<MfmaPath<D, B, 16>, 16, D, G>;
+    constexpr int VG = split_cols<D, G>();
+    using MCS = MultiCols<MfmaSplitPath<D, B, VG, 2>, VG, D, G>;
     switch (op) {
       case Op::kPartition:
         hipLaunchKernelGGL((partition_kernel<P, D, B, G>), grid, dim3(kThreads), 0, st, *a);
@@ -1533,6 +1617,22 @@ static hipError_t run_op(Op op, const DecodeArgs* a, dim3 grid,
       case Op::kPrefixSplit:
         hipLaunchKernelGGL((prefix_split_kernel<D, B, G>), grid, dim3(kThreads), 0, st, *a);
         return hipGetLastError();
+      case Op::kMultiBalanced:
+        hipLaunchKernelGGL((balanced_kernel<MC16, D, B, G>), grid, dim3(kThreads), 0,
+                           st, *a);
+        return hipGetLastError();
+      case Op::kMultiOccupancy:
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            occ, reinterpret_cast<const void*>(&balanced_kernel<MC16, D, B, G>),
+            kThreads, 0);
+      case Op::kMultiBalancedSplit:
+        hipLaunchKernelGGL((balanced_kernel<MCS, D, B, G>), grid, dim3(kThreads), 0,
+                           st, *a);
+        return hipGetLastError();
+      case Op::kMultiSplitOccupancy:
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            occ, reinterpret_cast<const void*>(&balanced_kernel<MCS, D, B, G>),
+            kThreads, 0);
       default:
         break;
     }
@@ -1629,6 +1729,29 @@ hipError_t launch_prefix_marks(const DecodeArgs& a, int block_size,
   hipLaunchKernelGGL(prefix_marks_kernel, dim3(1), dim3(256), 0, stream, a,
                      part_start, block_size);
   return hipGetLastError();
+}
+
+hipError_t launch_multi_balanced(const DecodeArgs& a, int head_size,
+                                 int block_size, int group, int grid,
+                                 bool whole_line, hipStream_t stream) {
+  return dispatch(whole_line ? Op::kMultiBalancedSplit : Op::kMultiBalanced,
+                  head_size, block_size, group, &a, dim3(grid), stream, nullptr);
+}
+
+int multi_balanced_grid(int head_size, int block_size, int group,
+                        bool whole_line) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+      hipSuccess)
+    return 0;
+  int per_cu = 0;
+  if (dispatch(whole_line ? Op::kMultiSplitOccupancy : Op::kMultiOccupancy,
+               head_size, block_size, group, nullptr, dim3(1), nullptr,
+               &per_cu) != hipSuccess)
+    return 0;
+  return per_cu > 0 ? per_cu * cus : 0;
 }
 
 hipError_t launch_multi_reduce(const ReduceArgs& a, int head_size,

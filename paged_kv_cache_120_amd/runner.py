@@ -25,7 +25,8 @@ import torch
 from . import (pa_balanced_grid, pa_balanced_grid_fp8, pa_balanced_workspace_size,
                pa_cache_write, pa_cache_write_fp8, pa_copy_blocks, pa_decode,
                pa_decode_balanced, pa_decode_balanced_fp8, pa_decode_multi,
-               pa_decode_step_fp8,
+               pa_decode_step_fp8, pa_decode_multi_balanced, pa_multi_balanced_grid,
+               pa_multi_balanced_workspace_size,
                pa_decode_reduce, pa_decode_shared_prefix, pa_decode_splitk,
                pa_decode_step, pa_multi_workspace_size, pa_prefix_workspace_size,
                pa_slot_mapping, pa_splitk_workspace_size)
@@ -113,11 +114,30 @@ def upload_multi(w, device: str = "cuda", pool: Optional[torch.Tensor] = None) -
     nbytes = pa_multi_workspace_size(Q, H, D, w.max_blocks_per_seq, w.block_size,
                                      w.partition_size)
     st.multi_workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    g = H // w.num_kv_heads
+    st.multi_grid = 0
+    if st.max_q * g <= 16:
+        with torch.cuda.device(dev):
+            st.multi_grid = pa_multi_balanced_grid(H, w.num_kv_heads, D, w.block_size,
+                                                   st.max_q)
+    nb = pa_multi_balanced_workspace_size(w.num_seqs, w.num_kv_heads, D,
+                                          max(st.multi_grid, 1))
+    st.multi_bal_workspace = torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev)
     return st
 
 
-def multi_step(step: DeviceStep, stream=None) -> None:
-    """Attention of the step's query rows (their K/V already written)."""
+def multi_step(step: DeviceStep, stream=None, balanced=None) -> None:
+    """Attention of the step's query rows (their K/V already written):
+    pa_decode_multi_balanced when every sequence's rows x heads fit one
+    16-column tile (or ``balanced`` says so), else pa_decode_multi."""
+    if balanced is None:
+        balanced = step.multi_grid > 0
+    if balanced:
+        pa_decode_multi_balanced(step.out, step.query, step.key_cache, step.value_cache,
+                                 step.block_tables, step.cu_seqlens_q, step.context_lens,
+                                 step.max_q, step.scale, step.multi_grid,
+                                 step.multi_bal_workspace, stream=stream)
+        return
     pa_decode_multi(step.out, step.query, step.key_cache, step.value_cache,
                     step.block_tables, step.cu_seqlens_q, step.context_lens,
                     step.max_q, step.scale, step.partition_size,

@@ -397,24 +397,27 @@ MULTI_SMALL = ["c1_prefill", "c2_small_spec4", "c3_small_spec4", "c3_small_chunk
                "c5_b32_small_spec2"]
 
 
-def run_multi(w):
+def run_multi(w, balanced=None):
     pa, runner = _gpu()
     st = runner.upload_multi(w)
+    if balanced and st.multi_grid <= 0:
+        pytest.skip("rows x heads of a sequence exceed one 16-column tile")
     runner.apply_history(w, st)
     runner.write_step(st)
-    runner.multi_step(st)
+    runner.multi_step(st, balanced=balanced)
     torch.cuda.synchronize()
     return st
 
 
+@pytest.mark.parametrize("balanced", [False, True])
 @pytest.mark.parametrize("name", MULTI_SMALL + ["c2_spec4", "c3_spec4"])
-def test_multi_token_parity(name):
-    """pa_decode_multi (causal within each sequence's query chunk) against
-    oracle.decode_multi on every row and head; the pool after the chunk's
-    cache write is bit-exact."""
-    print(f"[multi] {name}", flush=True)
+def test_multi_token_parity(name, balanced):
+    """pa_decode_multi and pa_decode_multi_balanced (causal within each
+    sequence's query chunk) against oracle.decode_multi on every row and
+    head; the pool after the chunk's cache write is bit-exact."""
+    print(f"[multi] {name} balanced={balanced}", flush=True)
     w = workloads.make(name)
-    st = run_multi(w)
+    st = run_multi(w, balanced)
     kc, vc = oracle_pool(w, oracle)
     g = st.pool.cpu().numpy().view(np.uint16)
     assert (g[0] == kc).all() and (g[1] == vc).all()
@@ -426,13 +429,15 @@ def test_multi_token_parity(name):
 @pytest.mark.parametrize("D,B,H,Hkv,T", [(128, 16, 16, 8, 2), (64, 32, 8, 8, 8),
                                          (128, 16, 8, 8, 3), (64, 16, 16, 2, 1),
                                          (128, 64, 64, 8, 1), (128, 32, 32, 8, 5)])
-def test_multi_token_shapes(D, B, H, Hkv, T):
+@pytest.mark.parametrize("balanced", [False, True])
+def test_multi_token_shapes(D, B, H, Hkv, T, balanced):
     """Shapes that run the whole-line body (g*T within its 4 or 8 columns,
-    partial tiles) and the 16-column body (g = 4, T = 5)."""
-    print(f"[multi-shape] D{D} B{B} H{H}/{Hkv} T{T}", flush=True)
+    partial tiles) and the 16-column body (g = 4, T = 5); the balanced
+    kernel where rows x heads fit 16 columns."""
+    print(f"[multi-shape] D{D} B{B} H{H}/{Hkv} T{T} balanced={balanced}", flush=True)
     w = workloads.make("c2_small_spec4", D=D, B=B, H=H, Hkv=Hkv, q_len=T,
                        seed=D + B + H + T)
-    st = run_multi(w)
+    st = run_multi(w, balanced)
     kc, vc = oracle_pool(w, oracle)
     ref = oracle.decode_multi(w.query, kc, vc, w.block_tables, w.info["cu_seqlens_q"],
                               w.context_lens, w.scale)
@@ -443,13 +448,14 @@ def test_multi_and_prefix_repeat_calls_bitwise():
     """The multi-token and shared-prefix decodes give the same bits on
     repeated calls (no atomics in their reductions)."""
     pa, runner = _gpu()
-    w = workloads.make("c2_small_spec4")
-    st = run_multi(w)
-    first = st.out.clone()
-    for _ in range(3):
-        runner.multi_step(st)
-    torch.cuda.synchronize()
-    assert torch.equal(first.view(torch.int16), st.out.view(torch.int16))
+    for bal in (False, True):
+        w = workloads.make("c2_small_spec4")
+        st = run_multi(w, bal)
+        first = st.out.clone()
+        for _ in range(3):
+            runner.multi_step(st, balanced=bal)
+        torch.cuda.synchronize()
+        assert torch.equal(first.view(torch.int16), st.out.view(torch.int16))
     w = workloads.make("c4_small")
     st = runner.upload_prefix(w)
     runner.apply_history(w, st)
@@ -460,6 +466,36 @@ def test_multi_and_prefix_repeat_calls_bitwise():
         runner.prefix_decode(st)
     torch.cuda.synchronize()
     assert torch.equal(first.view(torch.int16), st.out.view(torch.int16))
+
+
+@pytest.mark.parametrize("grid", [1, 5, 300])
+def test_multi_balanced_any_grid_and_empty_sequences(grid):
+    """The balanced multi-token kernel at grids other than the resident one,
+    with a sequence of context 0 (its rows are zeros) and one without rows."""
+    pa, runner = _gpu()
+    w = workloads.make("c3_small_spec4")
+    st = run_multi(w, True)
+    cu = w.info["cu_seqlens_q"]
+    ctx = w.context_lens.copy()
+    ctx[2] = 0
+    st.context_lens.copy_(torch.from_numpy(ctx))
+    nb = pa.pa_multi_balanced_workspace_size(w.num_seqs, w.num_kv_heads, w.head_size, grid)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    st.out.fill_(3.0)
+    pa.pa_decode_multi_balanced(st.out, st.query, st.key_cache, st.value_cache,
+                                st.block_tables, st.cu_seqlens_q, st.context_lens,
+                                st.max_q, w.scale, grid, ws)
+    torch.cuda.synchronize()
+    out = st.out.cpu().numpy().astype(np.float64)
+    assert (out[cu[2]:cu[3]] == 0).all()
+    keep_seq = [i for i in range(w.num_seqs) if i != 2]
+    rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in keep_seq])
+    T = np.diff(cu)[keep_seq]
+    cu2 = np.concatenate([[0], np.cumsum(T)]).astype(np.int32)
+    kc, vc = oracle_pool(w, oracle)
+    ref = oracle.decode_multi(w.query[rows], kc, vc, w.block_tables[keep_seq], cu2,
+                              ctx[keep_seq], w.scale)
+    assert_attention_close(out[rows], ref, f"balanced multi grid={grid}")
 
 
 def test_multi_token_zero_length_sequence_and_partition_sizes():
