@@ -1312,6 +1312,7 @@ template <class P, int D, int G>
 struct DecodeCols {
   using Path = P;
   static constexpr int NC = G;
+  static constexpr int kMinWaves = P::kMinWaves;
   template <class Sink>
   __device__ static void run(const DecodeArgs& a, typename P::Smem& sm, int kvh,
                              int s, int n, int ta, int tv, int last, Sink& sink) {
@@ -1339,6 +1340,9 @@ template <class P, int NCOLS, int D, int G>
 struct MultiCols {
   using Path = P;
   static constexpr int NC = NCOLS;
+  // The 16-column body with per-row limits needs more than 128 registers;
+  // its 50 KB of LDS allows three workgroups per CU, so aim for three waves.
+  static constexpr int kMinWaves = NCOLS == 16 ? 3 : P::kMinWaves;
   // query row of column c (c / G-th of the sequence's rows), -1 if none
   __device__ static int64_t row_of(const DecodeArgs& a, int s, int c) {
     const int q0 = a.cu_seqlens_q[s];
@@ -1382,7 +1386,7 @@ struct MultiCols {
 
 template <class Cols, int D, int B, int G>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(Cols::Path::kMinWaves))) void balanced_kernel(
+__attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
     DecodeArgs a) {
   constexpr int NC = Cols::NC;
   __shared__ typename Cols::Path::Smem sm;
