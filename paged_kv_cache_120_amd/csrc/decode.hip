@@ -584,7 +584,12 @@ struct MfmaSplitPath {
   static constexpr int KL = D / LC;             // loads per row group
   static constexpr int KS = CPL / 8;            // MFMA k-steps per load
   static constexpr int DT = D / 16;
-  static constexpr int VS = D + 4;              // padded LDS row (halves)
+  // Padded LDS row (halves).  In a V^T read the 4 lane groups take rows U
+  // apart, 8 dwords each; a row of VS/2 dwords with U*VS/2 = 8 (mod 64)
+  // puts the groups on disjoint banks (D + 4 left g = 4 four-way and g = 8
+  // two-way conflicted).
+  static constexpr int VS = D + (G == 4 ? 16 : 8);
+  static_assert((U * VS / 2) % 64 == 8, "V^T reads free of bank conflicts");
   static constexpr int kMinWaves = 4;           // 128 VGPRs: 4 waves per SIMD
   static_assert(G == 8 || G == 4, "16 columns = g heads x R splits");
   static_assert(B % 16 == 0, "a tile must not straddle two blocks");
