@@ -208,6 +208,32 @@ def load_traffic(args, root: str):
         return None
 
 
+def load_counters(args, root: str):
+    """Per-launch hardware counters of the decode kernel (L2 hit rate, LDS
+    bank conflicts, matrix-core and vector instructions) from the committed
+    summary for this workload and mode, if it was taken on the current
+    kernel sources (else None)."""
+    path = os.path.join(root, "profiles",
+                        f"decode_{args.config}_{args.mode}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    t = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                t[k.strip()] = v.strip()
+    if t.pop("kernel_source_sha256_16", None) != kernel_source_hash(root):
+        return None
+    out = {}
+    for k, v in t.items():
+        try:
+            out[k] = float(v)
+        except ValueError:
+            continue
+    return out or None
+
+
 HOST_LINK_PEAK_GBS = 64.0     # PCIe 5.0 x16, one direction (nominal)
 
 
@@ -768,6 +794,9 @@ def main(argv=None) -> int:
             "kernel_ms": round(kms, 5), "algorithmic_bytes": kb,
         },
     }
+    counters = load_counters(args, ROOT)
+    if counters:
+        rec["counters"] = counters
     if calib:
         rec["copy_calibration"] = calib
     if not args.no_cpu_baseline:
