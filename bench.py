@@ -234,6 +234,42 @@ def load_counters(args, root: str):
     return out or None
 
 
+PROBE_BYTES = 4 << 30        # streaming-read probe buffer (well past the 256 MB MALL)
+
+
+def stream_probe(dev, launches: int = 20) -> dict:
+    """Read rate of one plain sequential pass over a 4 GiB buffer
+    (pa_stream_read, 16-byte non-temporal loads), timed with events on the
+    current stream at 2, 4 and 8 workgroups per CU; the fastest is the
+    device's streaming-read ceiling in this run."""
+    import torch
+    import paged_kv_cache_120_amd as pa
+    buf = torch.zeros(PROBE_BYTES, dtype=torch.uint8, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(4 * 8 * cus, dtype=torch.int32, device=dev)
+    best = None
+    for grid in (2 * cus, 4 * cus, 8 * cus):
+        for _ in range(3):
+            pa.pa_stream_read(buf, sink, grid)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(launches):
+            pa.pa_stream_read(buf, sink, grid)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        if best is None or ms < best[1]:
+            best = (grid, ms)
+    del buf, sink
+    grid, ms = best
+    gbs = PROBE_BYTES / (ms * 1e-3) / 1e9
+    return {"kernel": "stream_read_kernel", "bytes": PROBE_BYTES, "grid": grid,
+            "us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 HOST_LINK_PEAK_GBS = 64.0     # PCIe 5.0 x16, one direction (nominal)
 
 
@@ -759,6 +795,7 @@ def main(argv=None) -> int:
 
     gpu_out = steps[(args.steps - 1) % R].out.cpu().numpy()
     traffic = load_traffic(args, ROOT)
+    probe = stream_probe(dev)
 
     rec = {
         "metric": METRIC,
@@ -787,12 +824,15 @@ def main(argv=None) -> int:
         "kv_bytes_per_step": kvb,
         "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "pct_stream_probe": round(100 * value / probe["gbs"], 2),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": kname,
             "kernel_ms": round(kms, 5), "algorithmic_bytes": kb,
+            "frac_of_stream_probe": round(achieved / probe["gbs"], 4),
         },
+        "stream_probe": probe,
     }
     counters = load_counters(args, ROOT)
     if counters:

@@ -425,6 +425,22 @@ pa_status pa_decode_step(void* out, const void* query, const void* key,
                          void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/*
+ * pa_stream_read -- measurement probe, not part of the method: one plain
+ *   sequential read of `bytes` bytes at `buf` with 16-byte non-temporal
+ *   loads.  Its rate is the device's streaming-read ceiling, against which a
+ *   decode's KV read rate is compared beside the nominal HBM peak (a
+ *   bandwidth-bound path such as [BOOK] §4.1.2 describes).
+ *   buf   device, 16-byte aligned, bytes > 0 and a multiple of 16; read only
+ *   sink  device uint32 [grid * 4]: each wave stores the xor of what it read
+ *         (so the loads cannot be elided); contents otherwise meaningless
+ *   grid  workgroups of 256 threads, 1 .. 65535 (a few per CU saturates HBM)
+ *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (bytes 0 or grid out of range),
+ *   PA_ERR_ALIGN, PA_ERR_HIP.
+ */
+pa_status pa_stream_read(const void* buf, size_t bytes, uint32_t* sink,
+                         int32_t grid, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -91,6 +91,7 @@ def _load() -> ctypes.CDLL:
         "pa_decode_balanced_fp8": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32,
                                                   i32, i32, i32, i32, f32, f32, f32, i32,
                                                   vp, sz, vp]),
+        "pa_stream_read": (ctypes.c_int, [vp, sz, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -296,6 +297,21 @@ def pa_copy_blocks(key_cache, value_cache, src, dst, stream=None) -> None:
         _dev(value_cache, torch.float16, "value_cache", 4),
         _dev(src, torch.int32, "src", 1), _dev(dst, torch.int32, "dst", 1),
         src.numel(), nb, B, Hkv, D, _stream(stream)))
+
+
+def pa_stream_read(buf, sink, grid: int, stream=None) -> None:
+    """Measurement probe: one sequential read of the whole of ``buf`` (any
+    contiguous device tensor, a multiple of 16 bytes); ``sink`` is an int32
+    device tensor of at least grid * 4 elements that receives per-wave xors."""
+    torch = _torch()
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or \
+            not buf.is_contiguous():
+        raise ValueError("pa_stream_read: buf must be a contiguous device tensor")
+    if sink.numel() < 4 * int(grid):
+        raise ValueError("pa_stream_read: sink holds fewer than grid * 4 words")
+    _check("pa_stream_read", _lib().pa_stream_read(
+        buf.data_ptr(), buf.numel() * buf.element_size(),
+        _dev(sink, torch.int32, "sink", 1), int(grid), _stream(stream)))
 
 
 def pa_swap_blocks(src_key_cache, src_value_cache, dst_key_cache, dst_value_cache,

@@ -216,3 +216,16 @@ def test_binding_rejects_host_tensors(pa):
     cl = torch.ones((2,), dtype=torch.int32)
     with pytest.raises(ValueError):
         pa.pa_decode(x, x, kc, kc, bt, cl, 0.1, stream=0)
+
+
+def test_stream_read_probe_validation(pa):
+    """The read probe rejects bad arguments before any launch."""
+    L = pa.lib
+    assert L.pa_stream_read(None, 1 << 20, FAKE, 8, None) == 1        # PA_ERR_NULL
+    assert L.pa_stream_read(FAKE, 1 << 20, None, 8, None) == 1
+    assert L.pa_stream_read(FAKE, 0, FAKE, 8, None) == 2              # PA_ERR_SHAPE
+    assert L.pa_stream_read(FAKE, 1 << 20, FAKE, 0, None) == 2
+    assert L.pa_stream_read(FAKE, 1 << 20, FAKE, 65536, None) == 2
+    assert L.pa_stream_read(FAKE, (1 << 20) + 8, FAKE, 8, None) == 4  # PA_ERR_ALIGN
+    assert L.pa_stream_read(FAKE + 8, 1 << 20, FAKE, 8, None) == 4
+    assert L.pa_stream_read(FAKE, 1 << 20, FAKE + 2, 8, None) == 4
