@@ -4,17 +4,26 @@
 A step is one pass of the whole decode path over one batch: slot mapping of
 the new tokens, the cache write, then decode.  Default (--mode fused):
 pa_decode_step, where the balanced split-KV kernel also derives each new
-token's slot and writes its K/V, followed by the reduce.  Other modes run
-pa_slot_mapping + pa_cache_write and then balanced, fixed-partition split-KV
-(+ reduce) or single-pass decode.  Inputs are seeded synthetic
-workloads already resident in HBM.  Timed steps rotate over --rotate copies
-of the pool so repeated reads cannot be served by the 256 MB MALL or L2.
+token's slot and writes its K/V.  Other modes run pa_slot_mapping +
+pa_cache_write and then balanced, fixed-partition split-KV (+ reduce) or
+single-pass decode.  Inputs are seeded synthetic workloads already resident
+in HBM.  Timed steps rotate over --rotate copies of the pool so repeated
+reads cannot be served by the 256 MB MALL or L2.
 
-Prints ONE JSON line.  ``value`` is KV GB/s: the KV bytes the step must read
-(exactly context_len tokens per sequence, K and V) over the step time.
-``roofline`` rates the dominant kernel (the decode partition kernel) against
-HBM peak with its algorithmic bytes over its event-timed duration.
-``cpu_baseline`` is the float64 CPU oracle timed on the same workload.
+Prints ONE JSON line.  ``value`` is KV GB/s of the headline workload (the
+Llama-2-13B layer, c2): the KV bytes the step must read (exactly
+context_len tokens per sequence, K and V) over the step time.  ``roofline``
+rates the dominant kernel against HBM peak with the method's bytes over its
+event-timed duration; the partial states that cut (sequence, kv head) pairs
+hand between workgroups are reported beside, as ``handoff_bytes``, and are
+not counted as algorithmic.  With the default configuration the line also
+carries ``gqa_c3`` (the GQA decode workload, same measurements and parity
+on every sequence), ``long_c5`` (long-context decode in the fixed 512-token
+split-K form the workload names, beside the one-kernel form),
+``paging_overhead`` (the same decodes on a contiguous identity block table)
+and ``context`` (the pages' own system-level figures).  ``cpu_baseline`` is
+the float64 CPU oracle timed on the machine's host cores (all of them, and one),
+before the GPU is touched.
 """
 from __future__ import annotations
 
@@ -97,16 +106,24 @@ def balanced_split_ranges(w, grid: int) -> int:
 
 
 def balanced_kernel_bytes(w, grid: int, fused: bool) -> int:
-    """Algorithmic bytes of one balanced-kernel launch: KV rows, query, table
-    entries, output, partial states of cut pairs (written, then read by the
-    merging workgroup) and, for the fused step, this step's K/V rows (read
-    and written) and the slots."""
+    """Algorithmic bytes of one balanced-kernel launch, the method's own:
+    KV rows of exactly context_len tokens, query, table entries, output and,
+    for the fused step, this step's K/V rows (read and written) and the
+    slots.  The partial states of cut pairs are the kernel's, not the
+    method's: see balanced_handoff_bytes."""
     S, H, D = w.query.shape
     n = w.context_lens.astype(np.int64)
     table = int(((n + w.block_size - 1) // w.block_size).sum()) * 4
-    parts = 2 * balanced_split_ranges(w, grid) * w.group * (D + 2) * 4
     extra = (2 * 2 * S * w.num_kv_heads * D * 2 + S * 4) if fused else 0
-    return kv_bytes(w) + 2 * S * H * D * 2 + table + parts + extra
+    return kv_bytes(w) + 2 * S * H * D * 2 + table + extra
+
+
+def balanced_handoff_bytes(w, grid: int) -> int:
+    """Bytes of the partial states that cut (sequence, kv head) pairs hand
+    between workgroups in one balanced-kernel launch: each range of a cut
+    pair writes g (max, sum, out[D]) fp32 states and the merging range reads
+    them back."""
+    return 2 * balanced_split_ranges(w, grid) * w.group * (w.head_size + 2) * 4
 
 
 def single_kernel_bytes(w) -> int:
@@ -116,11 +133,20 @@ def single_kernel_bytes(w) -> int:
     return kv_bytes(w) + 2 * S * H * D * 2 + table
 
 
+def _parity(gpu_out, ref) -> dict:
+    """Elementwise tolerance check of GPU outputs against the oracle."""
+    got = np.asarray(gpu_out, np.float64)
+    err = np.abs(got - ref)
+    return {"seqs_checked": int(ref.shape[0]), "max_abs_err": float(err.max()),
+            "within_tolerance": bool(((err <= 2e-3) | (err <= 1e-2 * np.abs(ref))).all())}
+
+
 def cpu_baseline(w, gpu_out=None, min_s: float = 10.0, max_s: float = 30.0):
-    """The oracle (unchanged) on the host: cache write of the step's tokens
-    plus float64 decode of the whole batch, repeated until >= min_s.  The
-    first pass's outputs are also compared with ``gpu_out`` (one of the timed
-    GPU steps) when it is given."""
+    """The oracle (unchanged) on one host core: cache write of the step's
+    tokens plus float64 decode of the whole batch, repeated until >= min_s.
+    The first pass's outputs are also compared with ``gpu_out`` (one of the
+    timed GPU steps) when it is given.  Used by the secondary modes, which
+    run it after the GPU work."""
     try:
         from threadpoolctl import threadpool_limits
     except Exception:                                   # pragma: no cover
@@ -156,11 +182,7 @@ def cpu_baseline(w, gpu_out=None, min_s: float = 10.0, max_s: float = 30.0):
     parity = None
     if gpu_out is not None and first:
         idx = sorted(first)
-        ref = np.stack([first[i] for i in idx])
-        got = np.asarray(gpu_out, np.float64)[idx]
-        err = np.abs(got - ref)
-        parity = {"seqs_checked": len(idx), "max_abs_err": float(err.max()),
-                  "within_tolerance": bool(((err <= 2e-3) | (err <= 1e-2 * np.abs(ref))).all())}
+        parity = _parity(np.asarray(gpu_out)[idx], np.stack([first[i] for i in idx]))
     return parity, {
         "value": round(seqs / el, 3), "unit": "seqs/s", "cores": 1, "kind": "oracle",
         "kv_gbs_equiv": round(kv_bytes(w) * frac / el / 1e9, 4),
@@ -169,6 +191,102 @@ def cpu_baseline(w, gpu_out=None, min_s: float = 10.0, max_s: float = 30.0):
                    f"batch, cache write of its new tokens per pass), float64 NumPy, "
                    f"1 BLAS thread"),
     }
+
+
+# State the forked oracle workers read (set in the parent before the fork).
+_ORACLE = {}
+
+
+def _oracle_worker(job):
+    """One worker of the host-core oracle baseline: starting at sequence
+    ``first``, decode the batch's sequences in turn -- each pass begins with
+    the cache write of the step's new tokens -- until ``seconds`` have
+    passed.  Returns (decodes done, KV bytes read, {seq: first output})."""
+    first, seconds = job
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:                                   # pragma: no cover
+        pass
+    import oracle
+    w, kc, vc = _ORACLE["w"], _ORACLE["kc"], _ORACLE["vc"]
+    row = 2 * w.num_kv_heads * w.head_size * 2
+    done, nbytes, outs = 0, 0, {}
+    t0 = time.perf_counter()
+    i = first % w.num_seqs
+    while True:
+        if i == first % w.num_seqs:
+            oracle.apply_phases(kc, vc, [w.step_copies, w.step_write], w.block_size)
+        o = oracle.decode(w.query[i:i + 1], kc, vc, w.block_tables[i:i + 1],
+                          w.context_lens[i:i + 1], w.scale)
+        outs.setdefault(i, o[0])
+        done += 1
+        nbytes += int(w.context_lens[i]) * row
+        i = (i + 1) % w.num_seqs
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return done, nbytes, outs
+
+
+def host_cores() -> dict:
+    """Host cores this process may use: the affinity mask, os.cpu_count(),
+    and the workers used (the affinity count, at most 16: one GPU's share of
+    the host)."""
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:                              # pragma: no cover
+        aff = os.cpu_count() or 1
+    return {"sched_getaffinity": aff, "os_cpu_count": os.cpu_count(),
+            "workers": max(1, min(aff, 16))}
+
+
+def cpu_baseline_cores(w, seconds: float = 10.0, single_seconds: float = 5.0):
+    """The oracle (unchanged) timed on the host: first on one core, then on
+    every usable core (a process pool over sequences, one BLAS thread per
+    worker).  Must run before the GPU is initialised: the workers are
+    forked.  Returns (oracle outputs of every sequence, record)."""
+    import multiprocessing as mp
+    import oracle
+    kc = w.pool_init[0].copy()
+    vc = w.pool_init[1].copy()
+    oracle.apply_phases(kc, vc, list(w.history), w.block_size)
+    _ORACLE.update(w=w, kc=kc, vc=vc)
+    cores = host_cores()
+    ctx = mp.get_context("fork")
+    # one core (in a worker, so the parent keeps its thread settings)
+    with ctx.Pool(1) as pool:
+        t0 = time.perf_counter()
+        d1, b1, outs = pool.map(_oracle_worker, [(0, single_seconds)])[0]
+        el1 = time.perf_counter() - t0
+    n = cores["workers"]
+    with ctx.Pool(n) as pool:
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_worker, [(k * w.num_seqs // n, seconds) for k in range(n)])
+        eln = time.perf_counter() - t0
+    _ORACLE.clear()
+    dn = sum(r[0] for r in res)
+    bn = sum(r[1] for r in res)
+    for r in res:
+        for i, o in r[2].items():
+            outs.setdefault(i, o)
+    missing = [i for i in range(w.num_seqs) if i not in outs]
+    for i in missing:                                   # rarely: a very short run
+        outs[i] = oracle.decode(w.query[i:i + 1], kc, vc, w.block_tables[i:i + 1],
+                                w.context_lens[i:i + 1], w.scale)[0]
+    ref = np.stack([outs[i] for i in range(w.num_seqs)])
+    rec = {
+        "value": round(dn / eln, 3), "unit": "seqs/s", "cores": n, "kind": "oracle",
+        "kv_gbs_equiv": round(bn / eln / 1e9, 4), "seconds": round(eln, 2),
+        "single_core_value": round(d1 / el1, 3),
+        "single_core_kv_gbs_equiv": round(b1 / el1 / 1e9, 4),
+        "sched_getaffinity": cores["sched_getaffinity"],
+        "os_cpu_count": cores["os_cpu_count"],
+        "sample": (f"{dn} sequence decodes of the {w.num_seqs}-seq batch over {n} worker "
+                   f"processes (each pass starting with the cache write of the step's new "
+                   f"tokens), float64 NumPy, one BLAS thread per worker, ~{seconds:.0f} s; "
+                   f"single core: {d1} decodes in {el1:.1f} s"),
+    }
+    return ref, rec
 
 
 KERNEL_SOURCES = ["paged_kv_cache_120_amd/csrc/decode.hip",
@@ -185,44 +303,46 @@ def kernel_source_hash(root: str) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(args, root: str):
-    """HBM bytes per launch of the decode kernel from the committed counter
-    summary for this workload and mode, if it was taken on the current
-    kernel sources (else None)."""
-    path = os.path.join(root, "profiles",
-                        f"decode_{args.config}_{args.mode}_traffic.txt")
-    if not os.path.exists(path):
-        return None
+def _summary(path: str) -> dict:
     t = {}
     with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 t[k.strip()] = v.strip()
+    return t
+
+
+def load_traffic(config: str, mode: str, partition: int, root: str):
+    """HBM bytes per launch of the decode kernel, from the committed
+    rocprofv3 counter summary (FETCH_SIZE / WRITE_SIZE scaled by a copy of
+    known size) for this workload and mode, if it was taken on the current
+    kernel sources (else None).  Returns {"bytes", "source"}."""
+    rel = f"profiles/decode_{config}_{mode}_traffic.txt"
+    path = os.path.join(root, rel)
+    if not os.path.exists(path):
+        return None
+    t = _summary(path)
     if t.get("kernel_source_sha256_16") != kernel_source_hash(root) or \
-            t.get("partition_size") != str(args.partition):
+            t.get("partition_size") != str(partition):
         return None
     try:
-        return int(float(t["hbm_bytes_per_launch"]))
+        return {"bytes": int(float(t["hbm_bytes_per_launch"])),
+                "source": f"{rel} (rocprofv3 --pmc on these kernel sources)"}
     except (KeyError, ValueError):
         return None
 
 
-def load_counters(args, root: str):
+def load_counters(config: str, mode: str, root: str):
     """Per-launch hardware counters of the decode kernel (L2 hit rate, LDS
     bank conflicts, matrix-core and vector instructions) from the committed
-    summary for this workload and mode, if it was taken on the current
-    kernel sources (else None)."""
-    path = os.path.join(root, "profiles",
-                        f"decode_{args.config}_{args.mode}_counters.txt")
+    rocprofv3 summary for this workload and mode, if it was taken on the
+    current kernel sources (else None)."""
+    rel = f"profiles/decode_{config}_{mode}_counters.txt"
+    path = os.path.join(root, rel)
     if not os.path.exists(path):
         return None
-    t = {}
-    with open(path) as f:
-        for line in f:
-            if ":" in line and not line.startswith("#"):
-                k, v = line.split(":", 1)
-                t[k.strip()] = v.strip()
+    t = _summary(path)
     if t.pop("kernel_source_sha256_16", None) != kernel_source_hash(root):
         return None
     out = {}
@@ -231,6 +351,8 @@ def load_counters(args, root: str):
             out[k] = float(v)
         except ValueError:
             continue
+    if out:
+        out["source"] = f"{rel} (rocprofv3 --pmc on these kernel sources)"
     return out or None
 
 
@@ -400,12 +522,13 @@ def multi_bench(args, w, dev) -> int:
         n = w.context_lens.astype(np.int64)
         table = int(((n + w.block_size - 1) // w.block_size).sum()) * 4
         cols = Q / w.num_seqs * w.group
-        kb = int(kvb + 2 * Q * w.num_heads * w.head_size * 2 + table
-                 + 2 * balanced_split_ranges(w, steps[0].multi_grid) * cols
-                 * (w.head_size + 2) * 4)
+        kb = int(kvb + 2 * Q * w.num_heads * w.head_size * 2 + table)
+        handoff = int(2 * balanced_split_ranges(w, steps[0].multi_grid) * cols
+                      * (w.head_size + 2) * 4)
         kname = "balanced_kernel (multi-token rows)"
     else:
         kb = multi_kernel_bytes(w)
+        handoff = 0
         kname = "multi_kernel + multi_reduce_kernel"
     achieved = kb / (kms * 1e-3) / 1e9
     rec = {
@@ -427,7 +550,8 @@ def multi_bench(args, w, dev) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "kernel": kname,
-                     "kernel_ms": round(kms, 5), "algorithmic_bytes": kb},
+                     "kernel_ms": round(kms, 5), "algorithmic_bytes": kb,
+                     "handoff_bytes": handoff},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -514,6 +638,7 @@ def fp8_bench(args, w, dev) -> int:
     kvb = kv_bytes(w) // 2                         # one byte per element
     S, H, D = w.query.shape
     kb = balanced_kernel_bytes(w, steps[0].grid, False) - kv_bytes(w) // 2
+    handoff = balanced_handoff_bytes(w, steps[0].grid)
     achieved = kb / (kms * 1e-3) / 1e9
     value = kvb / (ms_step * 1e-3) / 1e9
     rec = {
@@ -536,7 +661,8 @@ def fp8_bench(args, w, dev) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "kernel": "balanced_kernel (fp8 KV)",
-                     "kernel_ms": round(kms, 5), "algorithmic_bytes": kb},
+                     "kernel_ms": round(kms, 5), "algorithmic_bytes": kb,
+                     "handoff_bytes": handoff},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -657,6 +783,186 @@ def prefix_bench(args, w, dev) -> int:
     return 0
 
 
+CONTEXT = {
+    "note": "the pages' own system-level figures, quoted as context; none is a target "
+            "and none was measured here",
+    "kv_utilisation": "contiguous allocation 20-40% -> paged about 96% (PagedAttention: "
+                      "KV Cache的虚拟内存, 内存碎片化与GPU浪费 and 一图解析, after Kwon et al.)",
+    "indirection_overhead": "block-table indirection costs a single-digit percent "
+                            "(same page, 一图解析); measured here: paging_overhead",
+    "concurrent_requests": "LLaMA-13B on an A100 80GB, input 1024 / output 256: 8 -> 24 "
+                           "concurrent requests (PagedAttention原理（下）, §4.4 table)",
+}
+
+
+def _timed(steps, fn, n: int, warm: int) -> float:
+    """Mean ms of fn over n launches on the rotated steps (after warm
+    untimed ones), between two events on the current stream."""
+    import torch
+    R = len(steps)
+    for i in range(warm):
+        fn(steps[i % R])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        fn(steps[i % R])
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def upload_rotated(w, dev, rotate: int):
+    """The workload on the device with its history replayed, plus
+    rotate - 1 copies of the pool (sharing the other inputs' values)."""
+    import torch
+    from paged_kv_cache_120_amd import runner
+    base = runner.upload(w, dev)
+    runner.apply_history(w, base)
+    torch.cuda.synchronize()
+    steps = [base] + [runner.upload(w, dev, pool=base.pool.clone())
+                      for _ in range(1, max(1, rotate))]
+    torch.cuda.synchronize()
+    return steps
+
+
+def dominant_call(mode: str):
+    """The dominant kernel of a step of this mode, launched alone."""
+    import paged_kv_cache_120_amd as pa
+    from paged_kv_cache_120_amd import runner
+
+    def f(st):
+        if mode == "splitk":
+            pa.pa_decode_splitk(st.query, st.key_cache, st.value_cache, st.block_tables,
+                                st.context_lens, st.scale, st.partition_size, st.workspace)
+        else:
+            runner.decode_step(st, "fused_only" if mode == "fused" else mode)
+    return f
+
+
+def decode_measure(w, steps, mode: str, n: int, warm: int) -> dict:
+    """Whole steps, then the dominant kernel alone, over the rotated steps;
+    leaves the outputs of one full step in steps[(n - 1) % R].out."""
+    import torch
+    from paged_kv_cache_120_amd import runner
+    ms = _timed(steps, lambda st: runner.full_step(st, mode=mode), n, warm)
+    kms = _timed(steps, dominant_call(mode), n, min(warm, 4))
+    last = steps[(n - 1) % len(steps)]
+    runner.full_step(last, mode=mode)
+    torch.cuda.synchronize()
+    return {"ms_step": ms, "kms": kms, "out": last.out.cpu().numpy()}
+
+
+def decode_record(w, mode: str, grid: int, ms_step: float, kms: float) -> dict:
+    """Step rate, KV rate and the dominant kernel's roofline for one decode
+    workload.  ``algorithmic_bytes`` are the method's bytes (frac uses only
+    these); the balanced kernel's partial-state handoff is reported apart."""
+    kvb = kv_bytes(w)
+    handoff = 0
+    if mode == "splitk":
+        kb, kname = split_kernel_bytes(w), "partition_kernel (split-KV)"
+    elif mode == "single":
+        kb, kname = single_kernel_bytes(w), "partition_kernel (single pass)"
+    else:
+        kb = balanced_kernel_bytes(w, grid, mode == "fused")
+        handoff = balanced_handoff_bytes(w, grid)
+        kname = "balanced_kernel" + (" (fused append)" if mode == "fused" else "")
+    achieved = kb / (kms * 1e-3) / 1e9
+    value = kvb / (ms_step * 1e-3) / 1e9
+    return {
+        "ms_per_step": round(ms_step, 5), "kv_bytes_per_step": kvb,
+        "kv_gbs": round(value, 2), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": kname, "kernel_ms": round(kms, 5),
+                     "algorithmic_bytes": kb, "handoff_bytes": handoff},
+    }
+
+
+def contiguous_steps(w, steps, dev):
+    """The same batch on an identity block table: sequence i's logical
+    blocks are physical blocks off_i, off_i + 1, ... (sequences laid end to
+    end), holding the same K/V bits as the paged pool.  One contiguous pool
+    per rotated step."""
+    import dataclasses
+    import torch
+    B, M = w.block_size, w.max_blocks_per_seq
+    n = np.minimum(np.maximum(w.context_lens.astype(np.int64), 0), M * B)
+    nb = (n + B - 1) // B
+    off = np.concatenate([[0], np.cumsum(nb)[:-1]])
+    bt = np.zeros_like(w.block_tables)
+    src, dst = [], []
+    for i in range(w.num_seqs):
+        k = int(nb[i])
+        bt[i, :k] = off[i] + np.arange(k)
+        src.append(w.block_tables[i, :k])
+        dst.append(off[i] + np.arange(k))
+    src_t = torch.from_numpy(np.concatenate(src).astype(np.int64)).to(dev)
+    dst_t = torch.from_numpy(np.concatenate(dst).astype(np.int64)).to(dev)
+    total = max(int(nb.sum()), w.num_blocks)
+    bt_dev = torch.from_numpy(bt).to(dev)
+    out = []
+    for st in steps:
+        pool = torch.zeros((2, total) + tuple(st.pool.shape[2:]), dtype=st.pool.dtype,
+                           device=dev)
+        pool[:, dst_t] = st.pool[:, src_t]
+        wr = dataclasses.replace(st.write, table=bt_dev,
+                                 slots=torch.empty_like(st.write.slots))
+        out.append(dataclasses.replace(st, pool=pool, block_tables=bt_dev, write=wr,
+                                       out=torch.empty_like(st.out),
+                                       bal_workspace=torch.zeros_like(st.bal_workspace)))
+    torch.cuda.synchronize()
+    return out
+
+
+def paging_overhead(w, steps, dev, n: int) -> dict:
+    """The fused step's kernel on the workload's scattered block table and on
+    an identity table with the same K/V bits (alternated, best of two runs
+    each); outputs must agree bit for bit."""
+    import torch
+    from paged_kv_cache_120_amd import runner
+    contig = contiguous_steps(w, steps, dev)
+    f = dominant_call("fused")
+    paged_ms, contig_ms = [], []
+    for _ in range(2):
+        paged_ms.append(_timed(steps, f, n, 4))
+        contig_ms.append(_timed(contig, f, n, 4))
+    f(steps[0])
+    f(contig[0])
+    torch.cuda.synchronize()
+    same = bool(torch.equal(steps[0].out.view(torch.int16), contig[0].out.view(torch.int16)))
+    p, c = min(paged_ms), min(contig_ms)
+    del contig
+    torch.cuda.empty_cache()
+    return {"paged_kernel_ms": round(p, 5), "contiguous_kernel_ms": round(c, 5),
+            "overhead_pct": round(100 * (p - c) / c, 2), "outputs_bit_identical": same,
+            "contiguous": "identity block table: each sequence's blocks consecutive, "
+                          "sequences end to end, same K/V bits and kernel"}
+
+
+def long_context_record(name: str, args, dev) -> dict:
+    """Long-context decode in the form the workload names (fixed 512-token
+    split-K partitions + reduce, with the cache write) beside the one-kernel
+    fused step."""
+    import torch
+    import workloads
+    w = workloads.make(name)
+    w.partition_size = 512
+    steps = upload_rotated(w, dev, args.rotate)
+    n = max(10, args.steps // 4)
+    sk = decode_measure(w, steps, "splitk", n, min(args.warmup, 5))
+    fu = decode_measure(w, steps, "fused", n, min(args.warmup, 5))
+    grid = steps[0].grid
+    del steps
+    torch.cuda.empty_cache()
+    return {"workload": WORKLOADS[name], "num_seqs": w.num_seqs,
+            "total_context_tokens": int(w.context_lens.sum()), "steps": n,
+            "splitk_512": decode_record(w, "splitk", grid, sk["ms_step"], sk["kms"]),
+            "fused": decode_record(w, "fused", grid, fu["ms_step"], fu["kms"])}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -678,6 +984,8 @@ def main(argv=None) -> int:
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--partition", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the --config workload (no gqa_c3, long_c5, paging_overhead)")
     ap.add_argument("--calibrate", type=int, default=0, metavar="PAIRS",
                     help="after timing, copy PAIRS unreferenced blocks with "
                          "pa_copy_blocks (known bytes) to calibrate HBM counters")
@@ -689,12 +997,32 @@ def main(argv=None) -> int:
               "GPUs). Run with --gpus 1.", file=sys.stderr)
         return 2
 
-    import torch
     import workloads
-    from paged_kv_cache_120_amd import runner
 
     w = workloads.make(args.config)
     w.partition_size = args.partition
+    simple = args.mode in ("swap", "fp8", "prefix", "multi") or "cu_seqlens_q" in w.info
+    extras = (not simple and not args.no_extras and args.config == "c2"
+              and args.mode == "fused")
+    w3 = None
+    if extras:
+        w3 = workloads.make("c3")
+        w3.partition_size = args.partition
+
+    # host-core oracle baselines first: their workers are forked, which must
+    # happen before this process touches the GPU
+    ref, cpu, ref3 = None, None, None
+    if not simple and not args.no_cpu_baseline:
+        ref, cpu = cpu_baseline_cores(w)
+    if w3 is not None:
+        import oracle
+        kc3, vc3 = w3.pool_init[0].copy(), w3.pool_init[1].copy()
+        oracle.apply_phases(kc3, vc3, list(w3.history) + [w3.step_copies, w3.step_write],
+                            w3.block_size)
+        ref3 = oracle.decode(w3.query, kc3, vc3, w3.block_tables, w3.context_lens, w3.scale)
+        del kc3, vc3
+
+    import torch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.mode == "swap":
@@ -710,22 +1038,15 @@ def main(argv=None) -> int:
             return 2
         return multi_bench(args, w, dev)
 
-    steps = []
-    base = runner.upload(w, dev)
-    runner.apply_history(w, base)
-    torch.cuda.synchronize()
-    steps.append(base)
-    for _ in range(1, max(1, args.rotate)):
-        st = runner.upload(w, dev, pool=base.pool.clone())
-        steps.append(st)
-    torch.cuda.synchronize()
-
+    from paged_kv_cache_120_amd import runner
+    import paged_kv_cache_120_amd as pa
+    steps = upload_rotated(w, dev, args.rotate)
     R = len(steps)
     for i in range(args.warmup):
         runner.full_step(steps[i % R], mode=args.mode)
     torch.cuda.synchronize()
 
-    # pass 1: whole steps
+    # the timed region: exactly --steps whole steps
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -736,31 +1057,13 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # pass 2: the dominant kernel alone, launched back to back over the same
-    # rotated inputs, between one pair of events on the launch stream
-    import paged_kv_cache_120_amd as pa
-
-    def dominant(st):
-        if args.mode == "splitk":
-            pa.pa_decode_splitk(st.query, st.key_cache, st.value_cache, st.block_tables,
-                                st.context_lens, st.scale, st.partition_size, st.workspace)
-        else:
-            runner.decode_step(st, "fused_only" if args.mode == "fused" else args.mode)
-
-    for i in range(min(args.warmup, 4)):
-        dominant(steps[i % R])
-    e2 = torch.cuda.Event(enable_timing=True)
-    e3 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e2.record()
-    for i in range(args.steps):
-        dominant(steps[i % R])
-    e3.record()
-    torch.cuda.synchronize()
-    kms = e2.elapsed_time(e3) / args.steps
+    # the dominant kernel alone, launched back to back over the same rotated
+    # inputs, between one pair of events on the launch stream
+    kms = _timed(steps, dominant_call(args.mode), args.steps, min(args.warmup, 4))
     # leave the outputs of a full step for the parity check
     runner.full_step(steps[(args.steps - 1) % R], mode=args.mode)
     torch.cuda.synchronize()
+    gpu_out = steps[(args.steps - 1) % R].out.cpu().numpy()
 
     calib = None
     if args.calibrate:
@@ -780,31 +1083,23 @@ def main(argv=None) -> int:
                  "read_bytes": int(2 * k * blk), "write_bytes": int(2 * k * blk)}
         del cal
 
-    kvb = kv_bytes(w)
-    if args.mode == "splitk":
-        kb, kname = split_kernel_bytes(w), "partition_kernel (split-KV)"
-    elif args.mode == "single":
-        kb, kname = single_kernel_bytes(w), "partition_kernel (single pass)"
-    else:
-        kb = balanced_kernel_bytes(w, steps[0].grid, args.mode == "fused")
-        kname = "balanced_kernel" + (" (fused append)" if args.mode == "fused" else "")
-    if args.mode == "single":
-        kname = "partition_kernel (single pass)"
-    achieved = kb / (kms * 1e-3) / 1e9
-    value = kvb / (ms_step * 1e-3) / 1e9
-
-    gpu_out = steps[(args.steps - 1) % R].out.cpu().numpy()
-    traffic = load_traffic(args, ROOT)
+    main_rec = decode_record(w, args.mode, steps[0].grid, ms_step, kms)
+    traffic = load_traffic(args.config, args.mode, args.partition, ROOT)
+    if traffic is not None:
+        main_rec["roofline"]["traffic"] = traffic["bytes"]
+        main_rec["roofline"]["traffic_source"] = traffic["source"]
     probe = stream_probe(dev)
+    main_rec["roofline"]["frac_of_stream_probe"] = round(
+        main_rec["roofline"]["achieved"] / probe["gbs"], 4)
 
     rec = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": main_rec["kv_gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": main_rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -821,26 +1116,51 @@ def main(argv=None) -> int:
             "balanced_grid": steps[0].grid,
         },
         "accumulate": "f32",
-        "kv_bytes_per_step": kvb,
-        "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
-        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "pct_stream_probe": round(100 * value / probe["gbs"], 2),
-        "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": kname,
-            "kernel_ms": round(kms, 5), "algorithmic_bytes": kb,
-            "frac_of_stream_probe": round(achieved / probe["gbs"], 4),
-        },
+        "kv_bytes_per_step": main_rec["kv_bytes_per_step"],
+        "seqs_per_s": main_rec["seqs_per_s"],
+        "pct_hbm_peak": main_rec["pct_hbm_peak"],
+        "pct_stream_probe": round(100 * main_rec["kv_gbs"] / probe["gbs"], 2),
+        "roofline": main_rec["roofline"],
         "stream_probe": probe,
     }
-    counters = load_counters(args, ROOT)
+    counters = load_counters(args.config, args.mode, ROOT)
     if counters:
-        rec["counters"] = counters
+        rec["counters_from_profile"] = counters
     if calib:
         rec["copy_calibration"] = calib
-    if not args.no_cpu_baseline:
-        rec["parity"], rec["cpu_baseline"] = cpu_baseline(w, gpu_out)
+    if ref is not None:
+        rec["parity"] = _parity(gpu_out, ref)
+    if extras:
+        rec["paging_overhead"] = {"c2": paging_overhead(w, steps, dev, max(20, args.steps // 2))}
+    del steps
+    torch.cuda.empty_cache()
+
+    if extras:
+        # the GQA decode workload, measured the same way
+        s3 = upload_rotated(w3, dev, args.rotate)
+        m3 = decode_measure(w3, s3, "fused", args.steps, args.warmup)
+        r3 = decode_record(w3, "fused", s3[0].grid, m3["ms_step"], m3["kms"])
+        t3 = load_traffic("c3", "fused", args.partition, ROOT)
+        if t3 is not None:
+            r3["roofline"]["traffic"] = t3["bytes"]
+            r3["roofline"]["traffic_source"] = t3["source"]
+        r3["roofline"]["frac_of_stream_probe"] = round(r3["roofline"]["achieved"] / probe["gbs"], 4)
+        c3c = load_counters("c3", "fused", ROOT)
+        gq = {"workload": WORKLOADS["c3"], "num_seqs": w3.num_seqs,
+              "num_heads": w3.num_heads, "num_kv_heads": w3.num_kv_heads,
+              "total_context_tokens": int(w3.context_lens.sum()), "seed": w3.seed,
+              "balanced_grid": s3[0].grid, "decode": "fused", "steps": args.steps, **r3,
+              "parity": _parity(m3["out"], ref3)}
+        if c3c:
+            gq["counters_from_profile"] = c3c
+        rec["gqa_c3"] = gq
+        rec["paging_overhead"]["c3"] = paging_overhead(w3, s3, dev, max(20, args.steps // 2))
+        del s3
+        torch.cuda.empty_cache()
+        rec["long_c5"] = {n: long_context_record(n, args, dev) for n in ("c5_b32", "c5_b64")}
+        rec["context"] = CONTEXT
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
     return 0
 

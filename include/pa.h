@@ -51,6 +51,13 @@ typedef int pa_status;
 #define PA_ERR_WORKSPACE 5     /* split-KV workspace too small */
 #define PA_ERR_HIP 6           /* the HIP runtime reported an error */
 
+/* Balanced-split workspaces (pa_decode_balanced, pa_decode_step, their fp8
+ * forms and pa_decode_multi_balanced) start with a fixed header of range
+ * counters: at most PA_BALANCED_MAX_PAIRS (sequence, kv head) pairs per
+ * call (more: PA_ERR_SHAPE). */
+#define PA_BALANCED_MAX_PAIRS (1 << 18)
+#define PA_BALANCED_COUNTER_BYTES (4 * PA_BALANCED_MAX_PAIRS)
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* pa_status_str(pa_status status);
 
@@ -226,19 +233,26 @@ pa_status pa_decode_reduce(void* out, const void* workspace,
  * slice is finished there; a pair cut across k slices leaves k partial
  * softmax states (max, sum, unnormalised output: the form of [BOOK] §4.6),
  * and whichever of its workgroups finishes last merges them with the §4.6
- * recurrence.  With `grid` = pa_balanced_grid(...) every workgroup is
- * resident from the start, so none waits and none straggles.
+ * recurrence.  Slice boundaries and the merge order depend only on the
+ * shape, so repeated calls give bit-identical outputs.  With `grid` =
+ * pa_balanced_grid(...) every workgroup is resident from the start, so
+ * none waits on another.
  *
  * pa_balanced_grid: workgroups of the balanced kernel that the current
  *   device holds at once for this shape (0 if unsupported or unknown).
  * pa_balanced_workspace_size: bytes of device workspace for `grid`
- *   workgroups (0 on bad arguments).  Layout: int32 counters
- *   [num_seqs * num_kv_heads] padded to 16 bytes, then fp32 max [rows],
- *   sum [rows], out [rows, head_size] with rows = (grid + num_seqs *
- *   num_kv_heads) * group.
- *   The counters must be zero before the first call (zero-fill the whole
- *   workspace once); every completed call leaves them zero.  Calls that
- *   share a workspace must not overlap.
+ *   workgroups (0 on bad arguments, or when num_seqs * num_kv_heads
+ *   exceeds PA_BALANCED_MAX_PAIRS).  Layout: a fixed header of
+ *   PA_BALANCED_COUNTER_BYTES holding int32 range counters (pair
+ *   i * num_kv_heads + kv head uses counter i * num_kv_heads + kv head),
+ *   then fp32 max [rows], sum [rows], out [rows, head_size] with rows =
+ *   (grid + num_seqs * num_kv_heads) * group.
+ *   Zero-fill the workspace once before its first call; every completed
+ *   call leaves all counters zero, and since the header does not depend on
+ *   the call's shape, the same workspace then serves any later call, of
+ *   any shape, whose size requirement it meets (a serving loop can size it
+ *   for its largest batch and reuse it for every batch).  Calls that share
+ *   a workspace must not overlap.
  * pa_decode_balanced: arguments as pa_decode plus grid (> 0) and the
  *   workspace (16-byte aligned, >= pa_balanced_workspace_size).  Same
  *   preconditions and guards as pa_decode.
@@ -273,11 +287,14 @@ pa_status pa_decode_balanced(void* out, const void* query,
  *   max_q_per_seq to pa_decode_multi_balanced, which picks the whole-line
  *   matrix-core body when max_q_per_seq * g fits its 4 or 8 columns and
  *   the 16-column body otherwise.
- * pa_multi_balanced_workspace_size: int32 counters [num_seqs *
- *   num_kv_heads] padded to 16 bytes, then fp32 max/sum [rows] and out
- *   [rows, head_size], rows = (grid + num_seqs * num_kv_heads) * 16.  Zero-
- *   fill once before the first call; each completed call leaves the
- *   counters zero; calls sharing a workspace must not overlap.
+ * pa_multi_balanced_workspace_size: the same fixed counter header as
+ *   pa_balanced_workspace_size, then fp32 max/sum [rows] and out [rows,
+ *   head_size], rows = (grid + num_seqs * num_kv_heads) * 16 (0 when
+ *   num_seqs * num_kv_heads exceeds PA_BALANCED_MAX_PAIRS).  Zero-fill once
+ *   before the first call; each completed call leaves the counters zero, so
+ *   the workspace serves later calls of any shape it is large enough for
+ *   (a decode workspace of the same size may be shared with it); calls
+ *   sharing a workspace must not overlap.
  * Other arguments as pa_decode_multi ([BOOK] §4.5 (2)).
  */
 int32_t pa_multi_balanced_grid(int32_t num_heads, int32_t num_kv_heads,

@@ -20,32 +20,62 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # no packed-fp32 instructions anywhere in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+# hipcc's host pass does not know the device-only target feature above
+NOISE = "'-packed-fp32-ops' is not a recognized feature"
+
+
+def includes(extra_inc=()):
+    return [*[a for d in extra_inc for a in ("-I", d)],
+            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+
+
 def command(out: str = LIB, extra=()):
-    return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # no packed-fp32 instructions anywhere in device code
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wall", "-Wno-unused-function",
-        "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-        *extra,
-        *[os.path.join(HERE, s) for s in SOURCES],
-        "-o", out,
-    ]
+    """One hipcc line compiling and linking every source (for reference)."""
+    return [hipcc(), *FLAGS, "-shared", *includes(), *extra,
+            *[os.path.join(HERE, s) for s in SOURCES], "-o", out]
 
 
-def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
-    tmp = out + ".tmp"
-    cmd = command(tmp, extra)
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    # hipcc's host pass does not know the device-only target feature above
-    noise = "'-packed-fp32-ops' is not a recognized feature"
-    msg = "\n".join(l for l in r.stdout.splitlines() if noise not in l)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                            text=True)
+
+
+def _finish(p):
+    out, _ = p.communicate()
+    msg = "\n".join(l for l in out.splitlines() if NOISE not in l)
     if msg.strip():
         print(msg, file=sys.stderr)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode})")
+    return p.returncode
+
+
+def build(verbose: bool = False, out: str = LIB, extra=(), sources=None,
+          extra_inc=()) -> str:
+    """Compile each source to an object in parallel, then link the shared
+    library (written to a temporary name, then moved into place)."""
+    import tempfile
+    srcs = [os.path.join(HERE, s) for s in SOURCES] if sources is None else list(sources)
+    with tempfile.TemporaryDirectory(prefix="pagedkv_build_") as tmpd:
+        objs, procs = [], []
+        for src in srcs:
+            obj = os.path.join(tmpd, os.path.basename(src) + ".o")
+            objs.append(obj)
+            procs.append(_run([hipcc(), *FLAGS, *includes(extra_inc), *extra, "-c", src,
+                               "-o", obj], verbose))
+        codes = [_finish(p) for p in procs]
+        if any(codes):
+            raise RuntimeError(f"hipcc failed ({codes})")
+        tmp = out + ".tmp"
+        p = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", *objs, "-o", tmp], verbose)
+        if _finish(p) != 0:
+            raise RuntimeError("link failed")
     os.replace(tmp, out)
     return out
 

@@ -55,11 +55,30 @@ int64_t max_partitions(int32_t max_blocks_per_seq, int32_t block_size,
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-// Balanced-split workspaces: [counters int32 x S*H_kv] padded to 16 bytes,
-// then max, sum (fp32 [rows]) and out (fp32 [rows, D]), rows = (grid +
-// S*H_kv) * columns per pair (g for decode, 16 for multi-token rows).
-size_t balanced_header_bytes(int32_t num_seqs, int32_t num_kv_heads) {
-  return ((size_t)num_seqs * num_kv_heads * 4 + 15) & ~(size_t)15;
+// Balanced-split workspaces: a fixed header of kCounterSlots int32 range
+// counters (pair q = seq * H_kv + kv head uses counter q), then max, sum
+// (fp32 [rows]) and out (fp32 [rows, D]), rows = (grid + S*H_kv) * columns
+// per pair (g for decode, 16 for multi-token rows).  The header does not
+// depend on the call's shape, so one zero-filled workspace can serve calls
+// of any shape in any order: every counter is zero between calls, and no
+// call ever stores partial states over a counter.
+constexpr size_t kCounterSlots = PA_BALANCED_MAX_PAIRS;
+constexpr size_t kCounterBytes = PA_BALANCED_COUNTER_BYTES;
+static_assert(kCounterBytes == kCounterSlots * 4 && kCounterBytes % 16 == 0,
+              "state region stays 16-byte aligned");
+
+bool counters_fit(int32_t num_seqs, int32_t num_kv_heads) {
+  return (uint64_t)num_seqs * (uint64_t)num_kv_heads <= kCounterSlots;
+}
+
+// state rows of a balanced-split workspace with `cols` columns per pair
+uint64_t balanced_rows(int32_t num_seqs, int32_t num_kv_heads, int32_t grid,
+                       int32_t cols) {
+  return ((uint64_t)grid + (uint64_t)num_seqs * num_kv_heads) * (uint64_t)cols;
+}
+
+void set_balanced(pa::DecodeArgs& a, char* ws) {
+  a.bal_count = reinterpret_cast<int*>(ws);
 }
 
 }  // namespace
@@ -502,14 +521,15 @@ int32_t pa_multi_balanced_grid(int32_t num_heads, int32_t num_kv_heads,
                                  multi_whole_line(head_size, g, max_q_per_seq));
 }
 
-// [counters int32 x S*H_kv] padded to 16 bytes, then max, sum (fp32 [rows])
-// and out (fp32 [rows, D]) with rows = (grid + S*H_kv) * 16.
+// the fixed counter header, then max, sum (fp32 [rows]) and out (fp32
+// [rows, D]) with rows = (grid + S*H_kv) * 16.
 size_t pa_multi_balanced_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
                                         int32_t head_size, int32_t grid) {
-  if (num_seqs < 0 || num_kv_heads <= 0 || head_size <= 0 || grid <= 0) return 0;
-  const uint64_t rows = ((uint64_t)grid + (uint64_t)num_seqs * num_kv_heads) * 16;
-  return balanced_header_bytes(num_seqs, num_kv_heads) +
-         (size_t)(rows * 8 + rows * head_size * 4);
+  if (num_seqs < 0 || num_kv_heads <= 0 || head_size <= 0 || grid <= 0 ||
+      !counters_fit(num_seqs, num_kv_heads))
+    return 0;
+  const uint64_t rows = balanced_rows(num_seqs, num_kv_heads, grid, 16);
+  return kCounterBytes + (size_t)(rows * 8 + rows * head_size * 4);
 }
 
 pa_status pa_decode_multi_balanced(
@@ -525,7 +545,8 @@ pa_status pa_decode_multi_balanced(
                               num_heads, num_kv_heads, head_size, block_size,
                               num_blocks, scale);
   if (st != PA_OK) return st;
-  if (num_q_tokens < 0 || max_q_per_seq <= 0 || grid <= 0 || grid > (1 << 20))
+  if (num_q_tokens < 0 || max_q_per_seq <= 0 || grid <= 0 || grid > (1 << 20) ||
+      !counters_fit(num_seqs, num_kv_heads))
     return PA_ERR_SHAPE;
   const int32_t g = num_heads / num_kv_heads;
   if ((int64_t)max_q_per_seq * g > 16) return PA_ERR_UNSUPPORTED;
@@ -536,9 +557,9 @@ pa_status pa_decode_multi_balanced(
   if (workspace_bytes <
       pa_multi_balanced_workspace_size(num_seqs, num_kv_heads, head_size, grid))
     return PA_ERR_WORKSPACE;
-  const size_t rows = ((size_t)grid + (size_t)num_seqs * num_kv_heads) * 16;
+  const size_t rows = balanced_rows(num_seqs, num_kv_heads, grid, 16);
   char* ws = static_cast<char*>(workspace);
-  float* fmax = reinterpret_cast<float*>(ws + balanced_header_bytes(num_seqs, num_kv_heads));
+  float* fmax = reinterpret_cast<float*>(ws + kCounterBytes);
   pa::DecodeArgs a = {};
   a.out = static_cast<_Float16*>(out);
   a.ws_max = fmax;
@@ -554,7 +575,7 @@ pa_status pa_decode_multi_balanced(
   a.num_kv_heads = num_kv_heads;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
-  a.bal_count = reinterpret_cast<int*>(ws);
+  set_balanced(a, ws);
   a.split = 1;
   a.scale = scale;
   a.cu_seqlens_q = cu_seqlens_q;
@@ -623,12 +644,12 @@ size_t pa_balanced_workspace_size(int32_t num_seqs, int32_t num_heads,
                                   int32_t num_kv_heads, int32_t head_size,
                                   int32_t grid) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
-      grid <= 0 || num_heads % num_kv_heads != 0)
+      grid <= 0 || num_heads % num_kv_heads != 0 ||
+      !counters_fit(num_seqs, num_kv_heads))
     return 0;
-  const uint64_t rows = ((uint64_t)grid + (uint64_t)num_seqs * num_kv_heads) *
-                        (uint64_t)(num_heads / num_kv_heads);
-  return balanced_header_bytes(num_seqs, num_kv_heads) +
-         (size_t)(rows * 8 + rows * head_size * 4);
+  const uint64_t rows = balanced_rows(num_seqs, num_kv_heads, grid,
+                                      num_heads / num_kv_heads);
+  return kCounterBytes + (size_t)(rows * 8 + rows * head_size * 4);
 }
 
 static pa_status balanced_impl(void* out, const void* query, void* key_cache,
@@ -648,7 +669,8 @@ static pa_status balanced_impl(void* out, const void* query, void* key_cache,
                               num_heads, num_kv_heads, head_size, block_size,
                               num_blocks, scale);
   if (st != PA_OK) return st;
-  if (grid <= 0 || grid > (1 << 20)) return PA_ERR_SHAPE;
+  if (grid <= 0 || grid > (1 << 20) || !counters_fit(num_seqs, num_kv_heads))
+    return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (!out || !workspace) return PA_ERR_NULL;
   if (!aligned(out, 16) || !aligned(workspace, 16) ||
@@ -659,10 +681,9 @@ static pa_status balanced_impl(void* out, const void* query, void* key_cache,
                                                    num_kv_heads, head_size, grid))
     return PA_ERR_WORKSPACE;
   const int32_t g = num_heads / num_kv_heads;
-  const size_t rows = ((size_t)grid + (size_t)num_seqs * num_kv_heads) * g;
+  const size_t rows = balanced_rows(num_seqs, num_kv_heads, grid, g);
   char* ws = static_cast<char*>(workspace);
-  float* fmax = reinterpret_cast<float*>(
-      ws + balanced_header_bytes(num_seqs, num_kv_heads));
+  float* fmax = reinterpret_cast<float*>(ws + kCounterBytes);
   pa::DecodeArgs a = {};
   a.out = static_cast<_Float16*>(out);
   a.ws_max = fmax;
@@ -678,7 +699,7 @@ static pa_status balanced_impl(void* out, const void* query, void* key_cache,
   a.num_kv_heads = num_kv_heads;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
-  a.bal_count = reinterpret_cast<int*>(ws);
+  set_balanced(a, ws);
   a.new_key = static_cast<const _Float16*>(key);
   a.new_value = static_cast<const _Float16*>(value);
   a.slot_out = slot_mapping;

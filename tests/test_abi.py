@@ -70,7 +70,25 @@ def test_workspace_size(pa):
     assert pa.pa_splitk_workspace_size(1, 0, 64, 5, 16, 48) == 0
 
 
+def test_balanced_workspace_layout(pa):
+    # the counter header is the same for every shape, so one zero-filled
+    # workspace serves later calls of any shape it is large enough for
+    for S, H, Hkv, D, grid in [(32, 40, 40, 128, 1024), (64, 32, 8, 128, 1024),
+                               (3, 4, 4, 64, 1), (8, 64, 8, 128, 1024)]:
+        g = H // Hkv
+        rows = (grid + S * Hkv) * g
+        assert pa.pa_balanced_workspace_size(S, H, Hkv, D, grid) == HEADER + rows * (2 + D) * 4
+    # too many pairs for the header
+    assert pa.pa_balanced_workspace_size(1 << 16, 8, 8, 128, 1024) == 0
+    assert pa.pa_balanced_workspace_size((1 << 15), 8, 8, 128, 1024) > 0
+
+
 FAKE = 1 << 20          # a well-aligned non-null address that is never dereferenced
+
+# balanced-split workspaces: fixed header of one counter per (sequence, kv
+# head) pair, up to 2^18 pairs, then the states of the grid's slices and
+# one spare row per pair
+HEADER = 4 * (1 << 18)
 
 
 def _decode(pa, **kw):
@@ -194,7 +212,7 @@ def test_shared_prefix_validation(pa):
 def test_multi_balanced_validation(pa):
     L = pa.lib
     need = pa.pa_multi_balanced_workspace_size(2, 2, 128, 64)
-    assert need == 16 + (64 + 4) * 16 * (2 + 128) * 4
+    assert need == HEADER + (64 + 4) * 16 * (2 + 128) * 4
     d = L.pa_decode_multi_balanced
     a = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 8]
     b = [FAKE, 2, 8, 2, 128, 16, 10, 0.1]

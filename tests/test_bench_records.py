@@ -2,7 +2,6 @@
 LDS conflicts) only while they were taken on the current kernel sources, and
 its host-side count of split ranges follows the balanced kernel's slicing
 (CPU only)."""
-import argparse
 import os
 import shutil
 
@@ -22,10 +21,6 @@ def _copy_tree(tmp_path):
     return tmp_path
 
 
-def _args(cfg):
-    return argparse.Namespace(config=cfg, mode="fused", partition=512)
-
-
 def test_counters_follow_the_source_hash(tmp_path):
     root = _copy_tree(tmp_path)
     h = bench.kernel_source_hash(str(root))
@@ -33,13 +28,14 @@ def test_counters_follow_the_source_hash(tmp_path):
         "# comment: ignored\n"
         f"kernel_source_sha256_16: {h}\n"
         "l2_hit_rate_pct: 4.79\nlds_bank_conflict_pct: 49.11\nnote: text\n")
-    c = bench.load_counters(_args("c3"), str(root))
+    c = bench.load_counters("c3", "fused", str(root))
+    assert c.pop("source").startswith("profiles/decode_c3_fused_counters.txt")
     assert c == {"l2_hit_rate_pct": 4.79, "lds_bank_conflict_pct": 49.11}
     # another kernel source: the summary no longer describes it
     with open(root / bench.KERNEL_SOURCES[0], "a") as f:
         f.write("\n// changed\n")
-    assert bench.load_counters(_args("c3"), str(root)) is None
-    assert bench.load_counters(_args("c2"), str(root)) is None   # no file
+    assert bench.load_counters("c3", "fused", str(root)) is None
+    assert bench.load_counters("c2", "fused", str(root)) is None   # no file
 
 
 def test_traffic_follows_the_source_hash(tmp_path):
@@ -48,10 +44,12 @@ def test_traffic_follows_the_source_hash(tmp_path):
     p = root / "profiles" / "decode_c2_fused_traffic.txt"
     p.write_text(f"kernel_source_sha256_16: {h}\npartition_size: 512\n"
                  "hbm_bytes_per_launch: 793156835\n")
-    assert bench.load_traffic(_args("c2"), str(root)) == 793156835
+    t = bench.load_traffic("c2", "fused", 512, str(root))
+    assert t["bytes"] == 793156835 and "rocprofv3" in t["source"]
+    assert bench.load_traffic("c2", "fused", 1024, str(root)) is None
     p.write_text(f"kernel_source_sha256_16: {'0' * 16}\npartition_size: 512\n"
                  "hbm_bytes_per_launch: 793156835\n")
-    assert bench.load_traffic(_args("c2"), str(root)) is None
+    assert bench.load_traffic("c2", "fused", 512, str(root)) is None
 
 
 def test_split_ranges_brute_force():
@@ -85,3 +83,29 @@ def test_split_ranges_brute_force():
                     want += len(owners) if len(owners) > 1 else 0
                 flat += sp
         assert got == want, (trial, got, want)
+
+
+def test_roofline_counts_method_bytes_only():
+    """The roofline's algorithmic bytes are the method's (K/V of exactly
+    context_len tokens, query, output, table, the appended rows and slots);
+    the partial-state handoff of cut pairs is reported apart."""
+    import workloads
+    w = workloads.make("c3_small")
+    S, H, D = w.query.shape
+    n = w.context_lens.astype(np.int64)
+    kv = int(n.sum()) * 2 * w.num_kv_heads * D * 2
+    table = int(((n + w.block_size - 1) // w.block_size).sum()) * 4
+    appended = 2 * 2 * S * w.num_kv_heads * D * 2 + S * 4
+    assert bench.balanced_kernel_bytes(w, 64, True) == kv + 2 * S * H * D * 2 + table + appended
+    assert bench.balanced_kernel_bytes(w, 64, False) == kv + 2 * S * H * D * 2 + table
+    ho = bench.balanced_handoff_bytes(w, 64)
+    assert ho == 2 * bench.balanced_split_ranges(w, 64) * w.group * (D + 2) * 4 and ho > 0
+    rec = bench.decode_record(w, "fused", 64, 0.01, 0.008)
+    rf = rec["roofline"]
+    assert rf["handoff_bytes"] == ho
+    assert abs(rf["frac"] - rf["algorithmic_bytes"] / 0.008e-3 / 1e9 / 8000.0) < 1e-3
+
+
+def test_host_cores_are_reported():
+    c = bench.host_cores()
+    assert c["sched_getaffinity"] >= 1 and 1 <= c["workers"] <= 16
