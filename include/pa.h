@@ -443,6 +443,37 @@ pa_status pa_decode_step(void* out, const void* query, const void* key,
                          hipStream_t stream);
 
 /*
+ * pa_decode_step_noalloc -- pa_decode_step for callers that cannot allocate
+ *   device memory: code under HIP graph capture, tight serving loops and
+ *   harnesses that forbid hipMalloc.  The same arguments and result as
+ *   pa_decode_step (same kernel, same grid from pa_balanced_grid), without
+ *   the workspace: the range counters and partial states live in a static
+ *   device array of PA_NOALLOC_SCRATCH_BYTES that the library holds on each
+ *   device it runs on until the process ends.  The call allocates nothing
+ *   (no hipMalloc, no library allocation); the caller still passes inputs
+ *   and outputs.
+ *   Limits: at most PA_NOALLOC_MAX_PAIRS (sequence, kv head) pairs, and
+ *   (grid + num_seqs * num_kv_heads) * group * (head_size + 2) * 4 bytes of
+ *   partial states at most PA_NOALLOC_SCRATCH_BYTES - 4 *
+ *   PA_NOALLOC_MAX_PAIRS; larger shapes return PA_ERR_WORKSPACE before
+ *   anything is enqueued.  fp16 pools only.
+ *   The first call on a device clears the array's counters and waits for
+ *   that on `stream`, so it must not be made during graph capture; later
+ *   calls only enqueue.  Every call on a device shares that device's array
+ *   and leaves its counters zero: calls that overlap on one device (other
+ *   streams, other host threads) race and give wrong results.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define PA_NOALLOC_MAX_PAIRS (1 << 16)
+pa_status pa_decode_step_noalloc(
+    void* out, const void* query, const void* key, const void* value,
+    void* key_cache, void* value_cache, int32_t* slot_mapping,
+    const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+    int32_t num_blocks, float scale, int32_t grid, hipStream_t stream);
+
+/*
  * pa_stream_read -- measurement probe, not part of the method: one plain
  *   sequential read of `bytes` bytes at `buf` with 16-byte non-temporal
  *   loads.  Its rate is the device's streaming-read ceiling, against which a

@@ -23,7 +23,8 @@ __all__ = [
     "pa_cache_write_fp8", "pa_balanced_grid_fp8", "pa_decode_balanced_fp8",
     "pa_decode_step_fp8", "pa_multi_balanced_grid", "pa_multi_balanced_workspace_size",
     "pa_decode_multi_balanced",
-    "pa_prefix_workspace_size", "pa_decode_shared_prefix", "STATUS",
+    "pa_prefix_workspace_size", "pa_decode_shared_prefix", "pa_decode_step_noalloc",
+    "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +93,9 @@ def _load() -> ctypes.CDLL:
                                                   i32, i32, i32, i32, f32, f32, f32, i32,
                                                   vp, sz, vp]),
         "pa_stream_read": (ctypes.c_int, [vp, sz, vp, i32, vp]),
+        "pa_decode_step_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                                  i32, i32, i32, i32, i32, i32, f32, i32,
+                                                  vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -571,3 +575,22 @@ def pa_decode_step(out, query, key, value, key_cache, value_cache, block_tables,
         _dev(value, torch.float16, "value", 3), kc, vc, sm, bt, M, cl, S, H, Hkv, D,
         B, nb, float(scale), int(grid), ws, nbytes, _stream(stream)))
 
+
+
+def pa_decode_step_noalloc(out, query, key, value, key_cache, value_cache, block_tables,
+                           context_lens, scale: float, grid: int, slot_mapping=None,
+                           stream=None) -> None:
+    """pa_decode_step without a workspace: the library's static device
+    array holds the range counters and partial states (no allocation)."""
+    torch = _torch()
+    (q, kc, vc, bt, cl), (S, H, Hkv, D, B, nb, M) = _decode_common(
+        query, key_cache, value_cache, block_tables, context_lens)
+    if tuple(out.shape) != (S, H, D) or tuple(key.shape) != (S, Hkv, D) \
+            or tuple(value.shape) != (S, Hkv, D):
+        raise ValueError("pa_decode_step_noalloc: shapes")
+    sm = None if slot_mapping is None else _dev(slot_mapping, torch.int32,
+                                                "slot_mapping", 1)
+    _check("pa_decode_step_noalloc", _lib().pa_decode_step_noalloc(
+        _dev(out, torch.float16, "out", 3), q, _dev(key, torch.float16, "key", 3),
+        _dev(value, torch.float16, "value", 3), kc, vc, sm, bt, M, cl, S, H, Hkv, D,
+        B, nb, float(scale), int(grid), _stream(stream)))

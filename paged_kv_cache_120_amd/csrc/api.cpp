@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "api_internal.h"
 #include "decode.h"
 
 namespace {
@@ -652,6 +653,75 @@ size_t pa_balanced_workspace_size(int32_t num_seqs, int32_t num_heads,
   return kCounterBytes + (size_t)(rows * 8 + rows * head_size * 4);
 }
 
+}  // extern "C"
+
+namespace pa {
+
+// The balanced decode (with the fused append when key/value are given)
+// whose range counters (counter_slots int32, zero between calls) and
+// partial states (state_bytes) live at caller-given device addresses.
+pa_status balanced_run(void* out, const void* query, void* key_cache,
+                       void* value_cache, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                       int32_t head_size, int32_t block_size, int32_t num_blocks,
+                       float scale, int32_t grid, int* counters,
+                       size_t counter_slots, float* states, size_t state_bytes,
+                       const void* key, const void* value, int32_t* slot_mapping,
+                       hipStream_t stream, int elem_bytes, float k_scale,
+                       float v_scale, bool launch) {
+  pa_status st = check_decode(query, key_cache, value_cache, block_tables,
+                              max_blocks_per_seq, context_lens, num_seqs,
+                              num_heads, num_kv_heads, head_size, block_size,
+                              num_blocks, scale);
+  if (st != PA_OK) return st;
+  if (grid <= 0 || grid > (1 << 20) || !counters_fit(num_seqs, num_kv_heads))
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || (launch && (!counters || !states))) return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(states, 16) || !aligned(counters, 4) ||
+      (key && (!aligned(key, 16) || !aligned(value, 16))) ||
+      (slot_mapping && !aligned(slot_mapping, 4)))
+    return PA_ERR_ALIGN;
+  const int32_t g = num_heads / num_kv_heads;
+  const size_t rows = balanced_rows(num_seqs, num_kv_heads, grid, g);
+  if ((uint64_t)num_seqs * num_kv_heads > counter_slots ||
+      state_bytes < rows * 8 + rows * (size_t)head_size * 4)
+    return PA_ERR_WORKSPACE;
+  if (!launch) return PA_OK;
+  pa::DecodeArgs a = {};
+  a.out = static_cast<_Float16*>(out);
+  a.ws_max = states;
+  a.ws_sum = states + rows;
+  a.ws_out = states + 2 * rows;
+  a.query = static_cast<const _Float16*>(query);
+  a.key_cache = static_cast<const char*>(key_cache);
+  a.value_cache = static_cast<const char*>(value_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.bal_count = counters;
+  a.new_key = static_cast<const _Float16*>(key);
+  a.new_value = static_cast<const _Float16*>(value);
+  a.slot_out = slot_mapping;
+  a.split = 1;
+  a.scale = scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.inv_k_scale = 1.f / k_scale;
+  a.inv_v_scale = 1.f / v_scale;
+  return hip_status(pa::launch_balanced(a, head_size, block_size, g, grid,
+                                        stream, elem_bytes));
+}
+
+}  // namespace pa
+
+extern "C" {
+
 static pa_status balanced_impl(void* out, const void* query, void* key_cache,
                                void* value_cache, const int32_t* block_tables,
                                int32_t max_blocks_per_seq,
@@ -664,53 +734,15 @@ static pa_status balanced_impl(void* out, const void* query, void* key_cache,
                                int32_t* slot_mapping, hipStream_t stream,
                                int elem_bytes = 2, float k_scale = 1.f,
                                float v_scale = 1.f) {
-  pa_status st = check_decode(query, key_cache, value_cache, block_tables,
-                              max_blocks_per_seq, context_lens, num_seqs,
-                              num_heads, num_kv_heads, head_size, block_size,
-                              num_blocks, scale);
-  if (st != PA_OK) return st;
-  if (grid <= 0 || grid > (1 << 20) || !counters_fit(num_seqs, num_kv_heads))
-    return PA_ERR_SHAPE;
-  if (num_seqs == 0) return PA_OK;
-  if (!out || !workspace) return PA_ERR_NULL;
-  if (!aligned(out, 16) || !aligned(workspace, 16) ||
-      (key && (!aligned(key, 16) || !aligned(value, 16))) ||
-      (slot_mapping && !aligned(slot_mapping, 4)))
-    return PA_ERR_ALIGN;
-  if (workspace_bytes < pa_balanced_workspace_size(num_seqs, num_heads,
-                                                   num_kv_heads, head_size, grid))
-    return PA_ERR_WORKSPACE;
-  const int32_t g = num_heads / num_kv_heads;
-  const size_t rows = balanced_rows(num_seqs, num_kv_heads, grid, g);
+  // the workspace: the fixed counter header, then the states
   char* ws = static_cast<char*>(workspace);
-  float* fmax = reinterpret_cast<float*>(ws + kCounterBytes);
-  pa::DecodeArgs a = {};
-  a.out = static_cast<_Float16*>(out);
-  a.ws_max = fmax;
-  a.ws_sum = fmax + rows;
-  a.ws_out = fmax + 2 * rows;
-  a.query = static_cast<const _Float16*>(query);
-  a.key_cache = static_cast<const char*>(key_cache);
-  a.value_cache = static_cast<const char*>(value_cache);
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.num_blocks = num_blocks;
-  a.num_seqs = num_seqs;
-  set_balanced(a, ws);
-  a.new_key = static_cast<const _Float16*>(key);
-  a.new_value = static_cast<const _Float16*>(value);
-  a.slot_out = slot_mapping;
-  a.split = 1;
-  a.scale = scale;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  a.inv_k_scale = 1.f / k_scale;
-  a.inv_v_scale = 1.f / v_scale;
-  return hip_status(pa::launch_balanced(a, head_size, block_size, g, grid,
-                                        stream, elem_bytes));
+  return pa::balanced_run(
+      out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+      context_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+      num_blocks, scale, grid, reinterpret_cast<int*>(ws), kCounterSlots,
+      ws ? reinterpret_cast<float*>(ws + kCounterBytes) : nullptr,
+      workspace_bytes >= kCounterBytes ? workspace_bytes - kCounterBytes : 0, key,
+      value, slot_mapping, stream, elem_bytes, k_scale, v_scale, true);
 }
 
 pa_status pa_decode_balanced(void* out, const void* query, const void* key_cache,

@@ -247,3 +247,21 @@ def test_stream_read_probe_validation(pa):
     assert L.pa_stream_read(FAKE, (1 << 20) + 8, FAKE, 8, None) == 4  # PA_ERR_ALIGN
     assert L.pa_stream_read(FAKE + 8, 1 << 20, FAKE, 8, None) == 4
     assert L.pa_stream_read(FAKE, 1 << 20, FAKE + 2, 8, None) == 4
+
+
+def test_noalloc_limits_checked_before_the_device(pa):
+    """pa_decode_step_noalloc rejects shapes beyond its static array (and
+    other bad arguments) before it touches the device."""
+    L = pa.lib
+    d = L.pa_decode_step_noalloc
+
+    def call(S=2, H=8, Hkv=2, D=128, grid=16, key=FAKE):
+        return d(FAKE, FAKE, key, FAKE, FAKE, FAKE, None, FAKE, 8, FAKE, S, H, Hkv, D, 16,
+                 10, 0.1, grid, None)
+    assert call(S=1024, H=128, Hkv=128) == 5      # 131072 pairs > PA_NOALLOC_MAX_PAIRS
+    assert call(S=2, H=64, Hkv=8, grid=10000) == 5  # states beyond the static array
+    assert call(key=None) == 1
+    assert call(H=6, Hkv=4) == 2
+    assert call(D=96) == 3
+    assert call(grid=0) == 2
+    assert call(S=0) == 0                           # empty batch: nothing enqueued
