@@ -50,6 +50,38 @@ typedef int pa_status;
 #define PA_ERR_ALIGN 4         /* a pointer is not aligned as required */
 #define PA_ERR_WORKSPACE 5     /* split-KV workspace too small */
 #define PA_ERR_HIP 6           /* the HIP runtime reported an error */
+#define PA_ERR_CHECK 7         /* PA_CHECK=1 only: a device-side precondition fails */
+
+/*
+ * Validation mode.  With the environment variable PA_CHECK set to 1 (read
+ * at every call), the decode calls (pa_decode, pa_decode_splitk,
+ * pa_decode_balanced, pa_decode_step, their fp8 forms, pa_decode_multi,
+ * pa_decode_multi_balanced, pa_decode_shared_prefix,
+ * pa_decode_step_noalloc) and the cache writes first run a validation pass
+ * on the device, wait for it on `stream` (the one case where a call
+ * synchronises; so not under graph capture), and return PA_ERR_CHECK with
+ * nothing else enqueued if it finds a violated precondition:
+ *   PA_CHECK_CONTEXT         context_lens[i] > max_blocks_per_seq * block_size
+ *   PA_CHECK_TABLE           a table entry a decode reads (logical blocks
+ *                            below ceil(context_lens[i] / block_size)) is
+ *                            outside [0, num_blocks)
+ *   PA_CHECK_SLOT_RANGE      a cache-write slot >= num_blocks * block_size
+ *   PA_CHECK_DUPLICATE_SLOT  two tokens write the same slot (the cache
+ *                            write's slot_mapping, or the slots a fused
+ *                            step derives: two sequences whose last token
+ *                            falls in one shared block position)
+ * pa_last_check() returns these bits for the last pass on the calling host
+ * thread.  The shared-prefix groups and cu_seqlens_q are not checked.
+ * [P5] §4.1 recounts a block table shared by all requests whose concurrent
+ * updates scrambled the logical-to-physical mapping; this mode catches the
+ * marks such a bug leaves in the inputs: ids outside the pool and two tokens
+ * writing one slot.
+ */
+#define PA_CHECK_CONTEXT 1u
+#define PA_CHECK_TABLE 2u
+#define PA_CHECK_SLOT_RANGE 4u
+#define PA_CHECK_DUPLICATE_SLOT 8u
+uint32_t pa_last_check(void);
 
 /* Balanced-split workspaces (pa_decode_balanced, pa_decode_step, their fp8
  * forms and pa_decode_multi_balanced) start with a fixed header of range

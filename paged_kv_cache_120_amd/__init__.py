@@ -24,7 +24,7 @@ __all__ = [
     "pa_decode_step_fp8", "pa_multi_balanced_grid", "pa_multi_balanced_workspace_size",
     "pa_decode_multi_balanced",
     "pa_prefix_workspace_size", "pa_decode_shared_prefix", "pa_decode_step_noalloc",
-    "STATUS",
+    "pa_last_check", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +32,7 @@ library_path = os.path.join(_HERE, "libpagedkv.so")
 
 STATUS = {
     0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
-    4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP",
+    4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_CHECK",
 }
 
 
@@ -93,6 +93,7 @@ def _load() -> ctypes.CDLL:
                                                   i32, i32, i32, i32, f32, f32, f32, i32,
                                                   vp, sz, vp]),
         "pa_stream_read": (ctypes.c_int, [vp, sz, vp, i32, vp]),
+        "pa_last_check": (ctypes.c_uint32, []),
         "pa_decode_step_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
                                                   i32, i32, i32, i32, i32, i32, f32, i32,
                                                   vp]),
@@ -118,6 +119,11 @@ def __getattr__(name):
     if name == "lib":
         return _lib()
     raise AttributeError(name)
+
+
+def pa_last_check() -> int:
+    """PA_CHECK_* bits of the last PA_CHECK=1 validation pass on this thread."""
+    return int(_lib().pa_last_check())
 
 
 def pa_status_str(status: int) -> str:

@@ -56,6 +56,17 @@ int64_t max_partitions(int32_t max_blocks_per_seq, int32_t block_size,
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// PA_CHECK=1: the device-side preconditions of a decode over these tables
+// (and, for a fused step, the slots it writes), checked before any launch
+pa_status checked_tables(const int32_t* block_tables, int32_t M,
+                         const int32_t* context_lens, int32_t num_seqs,
+                         int32_t num_blocks, int32_t block_size, bool appends,
+                         hipStream_t stream) {
+  if (!pa::check_mode()) return PA_OK;
+  return pa::device_check(block_tables, M, context_lens, num_seqs, num_blocks,
+                          block_size, appends, nullptr, 0, stream);
+}
+
 // Balanced-split workspaces: a fixed header of kCounterSlots int32 range
 // counters (pair q = seq * H_kv + kv head uses counter q), then max, sum
 // (fp32 [rows]) and out (fp32 [rows, D]), rows = (grid + S*H_kv) * columns
@@ -95,6 +106,7 @@ const char* pa_status_str(pa_status s) {
     case PA_ERR_ALIGN: return "PA_ERR_ALIGN";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
     case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_CHECK: return "PA_ERR_CHECK";
   }
   return "PA_ERR_UNKNOWN";
 }
@@ -146,6 +158,11 @@ pa_status pa_cache_write(const void* key, const void* value, void* key_cache,
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) ||
       !aligned(value_cache, 16) || !aligned(slot_mapping, 4))
     return PA_ERR_ALIGN;
+  if (pa::check_mode()) {
+    const pa_status c = pa::device_check(nullptr, 0, nullptr, 0, num_blocks, block_size,
+                                         false, slot_mapping, num_tokens, stream);
+    if (c != PA_OK) return c;
+  }
   return hip_status(pa::launch_cache_write(
       key, value, key_cache, value_cache, slot_mapping, num_tokens,
       (int64_t)num_blocks * block_size, (int)cpr, stream));
@@ -170,6 +187,11 @@ pa_status pa_cache_write_fp8(const void* key, const void* value,
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) ||
       !aligned(value_cache, 16) || !aligned(slot_mapping, 4))
     return PA_ERR_ALIGN;
+  if (pa::check_mode()) {
+    const pa_status c = pa::device_check(nullptr, 0, nullptr, 0, num_blocks, block_size,
+                                         false, slot_mapping, num_tokens, stream);
+    if (c != PA_OK) return c;
+  }
   return hip_status(pa::launch_cache_write_fp8(
       key, value, key_cache, value_cache, slot_mapping, num_tokens,
       (int64_t)num_blocks * block_size, (int)cpr, 1.f / k_scale, 1.f / v_scale,
@@ -247,6 +269,9 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
   a.max_partitions = 1;
   a.split = 0;
   a.scale = scale;
+  st = checked_tables(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                      num_blocks, block_size, false, stream);
+  if (st != PA_OK) return st;
   dim3 grid(num_kv_heads, num_seqs, 1);
   return hip_status(pa::launch_decode(a, head_size, block_size,
                                       num_heads / num_kv_heads, grid, stream));
@@ -307,6 +332,9 @@ pa_status pa_decode_splitk(const void* query, const void* key_cache,
   a.max_partitions = (int)pm;
   a.split = 1;
   a.scale = scale;
+  st = checked_tables(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                      num_blocks, block_size, false, stream);
+  if (st != PA_OK) return st;
   dim3 grid(num_kv_heads, num_seqs, (unsigned)pm);
   return hip_status(pa::launch_decode(a, head_size, block_size,
                                       num_heads / num_kv_heads, grid, stream));
@@ -393,6 +421,9 @@ pa_status pa_decode_shared_prefix(
   a.grp_max_parts = (int)(gp < pm ? gp : pm);
   a.grp_max_members = (int)(tiles * per_tile);
   a.q_tiles = (int)(tiles > 0 ? tiles : 1);
+  st = checked_tables(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                      num_blocks, block_size, false, stream);
+  if (st != PA_OK) return st;
   st = hip_status(pa::launch_prefix_marks(a, block_size, part_start, stream));
   if (st != PA_OK) return st;
   if (num_groups > 0 && tiles > 0 && a.grp_max_parts > 0) {
@@ -485,6 +516,9 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache,
   a.cu_seqlens_q = cu_seqlens_q;
   a.q_tiles = (int)tiles;
   a.num_q_tokens = num_q_tokens;
+  st = checked_tables(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                      num_blocks, block_size, false, stream);
+  if (st != PA_OK) return st;
   dim3 grid(num_kv_heads, (unsigned)(num_seqs * tiles), (unsigned)pm);
   st = hip_status(pa::launch_multi(a, head_size, block_size, g, grid,
                                    whole_line, stream));
@@ -581,6 +615,9 @@ pa_status pa_decode_multi_balanced(
   a.scale = scale;
   a.cu_seqlens_q = cu_seqlens_q;
   a.num_q_tokens = num_q_tokens;
+  st = checked_tables(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                      num_blocks, block_size, false, stream);
+  if (st != PA_OK) return st;
   return hip_status(pa::launch_multi_balanced(
       a, head_size, block_size, g, grid,
       multi_whole_line(head_size, g, max_q_per_seq), stream));
@@ -689,6 +726,9 @@ pa_status balanced_run(void* out, const void* query, void* key_cache,
       state_bytes < rows * 8 + rows * (size_t)head_size * 4)
     return PA_ERR_WORKSPACE;
   if (!launch) return PA_OK;
+  st = checked_tables(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                      num_blocks, block_size, key != nullptr, stream);
+  if (st != PA_OK) return st;
   pa::DecodeArgs a = {};
   a.out = static_cast<_Float16*>(out);
   a.ws_max = states;

@@ -27,4 +27,18 @@ pa_status balanced_run(void* out, const void* query, void* key_cache,
                        hipStream_t stream, int elem_bytes, float k_scale,
                        float v_scale, bool launch);
 
+// PA_CHECK=1 in the environment (read at every call)
+bool check_mode();
+
+// The validation pass of PA_CHECK=1, run on `stream` and waited for: for
+// the num_seqs sequences (when block_tables is given) context length <=
+// M * block_size and every table entry a decode reads in [0, num_blocks);
+// for the slots -- the explicit list `slots` [num_slots], or (derived_slots)
+// the slot a fused step writes for each sequence -- in range and pairwise
+// distinct.  PA_ERR_CHECK if any check fails (pa_last_check() says which).
+pa_status device_check(const int32_t* block_tables, int32_t M,
+                       const int32_t* context_lens, int32_t num_seqs,
+                       int32_t num_blocks, int32_t block_size, bool derived_slots,
+                       const int32_t* slots, int32_t num_slots, hipStream_t stream);
+
 }  // namespace pa
