@@ -28,7 +28,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libpagedkv.so")
+# PAGEDKV_LIBRARY names another build of the same library (for instance a
+# sanitizer build of the host code); the default is the in-tree build
+library_path = os.environ.get("PAGEDKV_LIBRARY") or os.path.join(_HERE, "libpagedkv.so")
 
 STATUS = {
     0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",

@@ -112,3 +112,46 @@ def test_nonfinite_garbage_mode():
     w = workloads.make("c1", garbage="nonfinite")
     f = w.pool_init.view(np.float16).astype(np.float32)
     assert not np.isfinite(f).all()
+
+
+def test_pool_exhaustion_raises_memory_error():
+    """The generator's allocator refuses to hand out more blocks than the
+    pool holds (the scheduler's allocation failing when no block is free)."""
+    with pytest.raises(MemoryError):
+        workloads.make("c2_small", pool=("freelist_nb", 40))
+    with pytest.raises(MemoryError):
+        workloads.make("c4_small", pool=("freelist_nb", 100))
+
+
+def test_reference_count_cannot_underflow():
+    fl = workloads._FreeList(np.arange(4), 4)
+    b = fl.pop()
+    fl.drop(b)
+    assert fl.ref[b] == 0
+    with pytest.raises(ValueError):
+        fl.drop(b)
+
+
+@pytest.mark.parametrize("name", ["c4_small", "c4_r0_small", "c4"])
+def test_copy_on_write_reference_counts(name):
+    """Shared prompt blocks: every full block is held by all samples; the
+    partial last block is copied for all but one sample, whose in-place write
+    leaves the original with exactly one reference; copies are private."""
+    w = workloads.make(name)
+    B, n_s, P = w.block_size, w.info["samples"], w.info["prompts"]
+    assert (w.ref_cnt >= 0).all()
+    copies = [ph for ph in w.history if hasattr(ph, "src")]
+    if w.step_copies is not None:
+        copies.append(w.step_copies)
+    src = np.concatenate([c.src for c in copies]) if copies else np.zeros(0, np.int32)
+    dst = np.concatenate([c.dst for c in copies]) if copies else np.zeros(0, np.int32)
+    partial = (w.info["prompt_len"] % B) != 0
+    assert len(src) == int(partial.sum()) * (n_s - 1)
+    assert len(set(dst.tolist())) == len(dst) and (w.ref_cnt[dst] == 1).all()
+    pt, pu = w.info["prompt_tables"], w.info["prompt_used"]
+    for p in range(P):
+        full = int(w.info["prompt_len"][p]) // B
+        assert (w.ref_cnt[pt[p, :full]] == n_s).all()
+        if partial[p]:
+            assert w.ref_cnt[pt[p, pu[p] - 1]] == 1
+            assert (src == pt[p, pu[p] - 1]).sum() == n_s - 1

@@ -171,6 +171,13 @@ class _FreeList:
         self.ref[b] += 1
         return b
 
+    def drop(self, b: int) -> None:
+        """One reference to block b released (copy-on-write repoints a table
+        entry); a block nobody references cannot be released again."""
+        if self.ref[b] <= 0:
+            raise ValueError(f"reference count of block {b} would go below zero")
+        self.ref[b] -= 1
+
 
 def _ceil_div(a: int, b: int) -> int:
     return (a + b - 1) // b
@@ -462,7 +469,7 @@ def _make_prefix(name: str, spec: dict, seed: int, garbage: str) -> Workload:
             new = fl.pop()
             copies.append((blk, new))
             tables[i, lb] = new
-            fl.ref[blk] -= 1
+            fl.drop(blk)
 
     lens = np.zeros(S, np.int64)
     hist_rows, hist_pos = [], []
