@@ -204,11 +204,19 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
                     float scale, hipStream_t stream);
 
 /*
- * Split-KV workspace.  With Pmax = ceil(max_blocks_per_seq * block_size /
- * partition_size), the workspace holds, in this order and back to back:
+ * Split-KV workspace.  The three partial-state arrays of the split form --
+ * per partition its maximum, its sum of exponentials and its unnormalised
+ * output, the (m, s, O) state that [BOOK] §4.6 merges blockwise -- travel as
+ * ONE caller-owned buffer instead of three pointers, so that a caller sizes,
+ * allocates and passes a single object and the pair of calls cannot be
+ * handed mismatched arrays.  With Pmax = ceil(max_blocks_per_seq *
+ * block_size / partition_size) (256 for 128K-token contexts split into
+ * 512-token partitions), it holds, in this order and back to back:
  *   max_logits fp32 [num_seqs, num_heads, Pmax]
  *   exp_sums   fp32 [num_seqs, num_heads, Pmax]
  *   tmp_out    fp32 [num_seqs, num_heads, Pmax, head_size]
+ * The caller owns it; the library neither keeps nor frees it, and reads or
+ * writes only the entries of non-empty partitions.
  * pa_splitk_workspace_size returns its size in bytes (0 on bad arguments).
  */
 size_t pa_splitk_workspace_size(int32_t num_seqs, int32_t num_heads,

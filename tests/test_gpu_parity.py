@@ -169,6 +169,33 @@ def test_nonfinite_garbage_is_never_read(mode):
     check_all(w, mode)
 
 
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("name", ["c3_small", "c5_b32_small"])
+def test_weights_near_the_lazy_reference_ceiling(name, mode):
+    """The matrix-core bodies round softmax weights to fp16 for P.V.  The
+    first 64 keys of every 512-token window score 0; the first batch of each
+    of a workgroup's four waves (16 keys each at D = 128) that starts a
+    sequence or a 512-token split partition falls there and sets the wave's
+    reference to 0.  Every other key scores 62 * scale * log2(e) = 7.9 in
+    base 2, just below the point where the reference would move (8), so most
+    of the weight is carried by weights of 2^7.9 on values of 1: the fp16
+    rounding of the weights is as large, and as uniform in sign, as the
+    bound allows.  (Balanced slices start at any 16-token boundary; a slice
+    whose first batch scores 7.9 takes that as its reference.)"""
+    print(f"[lazy-ceiling] {name} {mode}", flush=True)
+    w = workloads.make(name)
+    assert w.head_size == 128 and w.partition_size % 512 == 0
+    w.query[...] = np.float16(1.0)
+    for ph in [p for p in w.history if hasattr(p, "seq")] + [w.step_write]:
+        early = ph.pos % 512 < 64
+        ph.key[early] = np.float16(0.0)
+        ph.key[~early] = np.float16(62.0 / 128.0)     # q.k = 62 (exact in fp16)
+        ph.value[~early] = np.float16(1.0)
+    s2 = 62.0 * float(w.scale) * np.log2(np.e)
+    assert 7.5 < s2 < 8.0
+    check_all(w, mode)
+
+
 @pytest.mark.parametrize("P", [16, 64, 256, 1024, 4096])
 def test_splitk_partition_sizes(P):
     w = workloads.make("c3_small")
