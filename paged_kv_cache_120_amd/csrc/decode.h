@@ -78,8 +78,10 @@ hipError_t launch_multi(const DecodeArgs& a, int head_size, int block_size,
                         int group, dim3 grid, bool whole_line,
                         hipStream_t stream);
 // multi-token queries on the balanced split (T*g <= 16 rows x heads per
-// sequence, one kernel; whole_line: the split body, T*g <= split_columns());
-// grid = resident workgroups of that kernel
+// sequence, one kernel), always the whole-line body: whole_line true gives
+// it split_columns() columns (T*g <= split_columns()), false 16 distinct
+// columns with repeated score passes; grid = resident workgroups of that
+// kernel
 hipError_t launch_multi_balanced(const DecodeArgs& a, int head_size,
                                  int block_size, int group, int grid,
                                  bool whole_line, hipStream_t stream);

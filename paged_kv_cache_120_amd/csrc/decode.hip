@@ -19,7 +19,8 @@
 //                       (possibly several ranges); the last range of a split
 //                       pair to finish merges its partial states;
 //   reduce_kernel    -- merges the fixed partitions of split-KV with the
-//                       §4.6 recurrence.
+//                       §4.6 recurrence, many partitions in flight per
+//                       workgroup.
 //
 // Common to both bodies: K/V rows are read with 16-byte buffer loads whose
 // resource is rebased per physical block (64-bit base in SGPRs) with a record
@@ -390,6 +391,9 @@ struct MfmaPath {
   static constexpr int DT = D / 16;             // channel tiles of O^T
   static constexpr int VS = D + 4;              // padded LDS row (halves)
   static constexpr int kMinWaves = 4;           // 128 VGPRs: 4 waves per SIMD
+  // With per-row key limits the 16-column body needs more than 128
+  // registers; its 50 KB of LDS allows three workgroups per CU anyway.
+  static constexpr int kColsMinWaves = G == 16 ? 3 : kMinWaves;
   static_assert(B % 16 == 0, "a tile must not straddle two blocks");
   static_assert(G <= 16, "one MFMA column per query row");
 
@@ -573,7 +577,15 @@ struct MfmaPath {
 // T(j) = (j/U)*g + (lane/16)*U + j%U of the tile (U = 4/R), and the P.V
 // k-order follows T, which only changes which LDS rows V^T reads.
 // CPL channels per lane per load: min(16 bytes, D/(4R) channels), >= 8.
-template <int D, int B, int G, int EB>
+//
+// Full (F = true): all 16 columns distinct, for query columns of several
+// tokens (multi-token rows).  The split still indexes the score product's
+// columns, so the scores take R MFMA passes, pass k with B column n = query
+// column k*G + n%G on split n/G; after the R-lane sum, lane column n keeps
+// pass n/G, i.e. the score of its own column n.  Softmax and P.V then run
+// once for 16 distinct columns: the loads stay whole-line and only the
+// score product is repeated.
+template <int D, int B, int G, int EB, bool F = false>
 struct MfmaSplitPath {
   static constexpr int R = 16 / G;              // channel splits = rows per token
   static constexpr int U = 4 / R;               // useful D values per lane per MFMA
@@ -591,17 +603,32 @@ struct MfmaSplitPath {
   static constexpr int VS = D + (G == 4 ? 16 : 8);
   static_assert((U * VS / 2) % 64 == 8, "V^T reads free of bank conflicts");
   static constexpr int kMinWaves = 4;           // 128 VGPRs: 4 waves per SIMD
+  static constexpr int kColsMinWaves = kMinWaves;
+  static constexpr int NS = F ? R : 1;          // score passes
+  static constexpr int NCOL = F ? 16 : G;       // distinct columns
   static_assert(G == 8 || G == 4, "16 columns = g heads x R splits");
+  static_assert(!F || EB == 2, "full columns: multi-token rows of an fp16 pool");
   static_assert(B % 16 == 0, "a tile must not straddle two blocks");
   static_assert(CPL >= 8 && CPL % 8 == 0 && KL * LC == D, "line chunks cover the row");
   using Raw = std::conditional_t<CPL * EB == 16, u32x4, u32x2>;
 
-  struct Smem {
+  struct SmemSplit {
     _Float16 vs[kWaves][TB][VS];
     float acc[kWaves][G][D];
     float m[kWaves][G];
     float l[kWaves][G];
   };
+  // 16 columns: the V staging rows are dead once every wave has left its
+  // loop, so the per-wave results take their place (4 workgroups per CU)
+  struct SmemFull {
+    union {
+      _Float16 vs[kWaves][TB][VS];
+      float acc[kWaves][16][D];
+    };
+    float m[kWaves][16];
+    float l[kWaves][16];
+  };
+  using Smem = std::conditional_t<F, SmemFull, SmemSplit>;
 
   __device__ static Raw load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     if constexpr (CPL * EB == 16) return load16(r, off);
@@ -639,14 +666,15 @@ struct MfmaSplitPath {
   template <class Sink>
   __device__ static void run(const DecodeArgs& a, Smem& sm, int kvh, int seq,
                              int t0, int t1, int last, Sink& sink) {
+    static_assert(!F, "decode columns are the g heads");
     const int hd = (threadIdx.x & 15) % G;
     const int64_t qoff =
         ((int64_t)seq * a.num_heads + (int64_t)kvh * G + hd) * D;
     body<false>(a, sm, kvh, seq, t0, t1, last, sink, qoff, 0x7fffffff);
   }
 
-  // The same over G columns given by the caller (fp16 pools): the lanes of
-  // column c = (lane%16)%G pass the same query-row element offset qoff
+  // The same over NCOL columns given by the caller (fp16 pools): the lanes
+  // of column c = (lane%16)%NCOL pass the same query-row element offset qoff
   // (-1: an unused column, zero query) and key limit lim (keys t <= lim).
   template <class Sink>
   __device__ static void run_cols(const DecodeArgs& a, Smem& sm, int kvh,
@@ -666,19 +694,30 @@ struct MfmaSplitPath {
     const int q = col / G;                      // B column: split
     if (last >= 0) append_token<D, B, EB>(a, kvh, seq, last);
 
-    // B operand of load kl, k-step s: column hd's query row, channels
-    // kl*LC + q*4*CPL + grp*CPL + s*8 .. +7
-    f16x8 qb[KL][KS];
+    // B operand of pass k, load kl, k-step s: the query row of column
+    // k*G + col%G (F) or col%G, channels kl*LC + q*4*CPL + grp*CPL + s*8 ..
+    f16x8 qb[NS][KL][KS];
 #pragma unroll
-    for (int kl = 0; kl < KL; ++kl)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (!kCols || qoff >= 0)
-          v = *reinterpret_cast<const u32x4*>(
-              a.query + qoff + kl * LC + q * 4 * CPL + grp * CPL + s * 8);
-        qb[kl][s] = __builtin_bit_cast(f16x8, v);
+    for (int k = 0; k < NS; ++k) {
+      int64_t qk = qoff;
+      if constexpr (F) {       // as lane (grp, k*G + col%G) holds it
+        const int src = (lane & 48) | (k * G + col % G);
+        const uint64_t u = (uint64_t)qoff;
+        const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)u, src);
+        const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(u >> 32), src);
+        qk = (int64_t)(((uint64_t)hi << 32) | lo);
       }
+#pragma unroll
+      for (int kl = 0; kl < KL; ++kl)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (!kCols || qk >= 0)
+            v = *reinterpret_cast<const u32x4*>(
+                a.query + qk + kl * LC + q * 4 * CPL + grp * CPL + s * 8);
+          qb[k][kl][s] = __builtin_bit_cast(f16x8, v);
+        }
+    }
 
     BlockWindow bw;
     bw.init(a.block_tables + (size_t)seq * a.max_blocks_per_seq, t0 / B,
@@ -739,33 +778,42 @@ struct MfmaSplitPath {
             }
       }
 
-      // scores of column col % G: slot j = token tile0 + T(j)
+      // scores of this lane's column (col % G; col under F): slot j =
+      // token tile0 + T(j)
       float sc[MT][4];
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
         for (int rg = 0; rg < R; ++rg) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          float pv[U];
 #pragma unroll
-          for (int kl = 0; kl < KL; ++kl)
+          for (int k = 0; k < NS; ++k) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                  __builtin_bit_cast(f16x8, part(kr[mi][rg][kl], s)), qb[kl][s], acc,
-                  0, 0, 0);
-          // rows 4grp + j: token (4grp + j)/R, split j%R; keep split q
-          const float av[4] = {acc[0], acc[1], acc[2], acc[3]};
+            for (int kl = 0; kl < KL; ++kl)
+#pragma unroll
+              for (int s = 0; s < KS; ++s)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    __builtin_bit_cast(f16x8, part(kr[mi][rg][kl], s)), qb[k][kl][s],
+                    acc, 0, 0, 0);
+            // rows 4grp + j: token (4grp + j)/R, split j%R; keep split q
+            const float av[4] = {acc[0], acc[1], acc[2], acc[3]};
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+              float p = av[R * u];
+#pragma unroll
+              for (int j = 1; j < R; ++j) p = q == j ? av[j + R * u] : p;
+              // sum over the R lanes of column col % G (bitwise equal in each)
+              if constexpr (R >= 2) p += dpp<kRowRor8>(p);
+              if constexpr (R >= 4) p += dpp<kRowRor4>(p);
+              pv[u] = (NS == 1 || q == k) ? p : pv[u];
+            }
+          }
 #pragma unroll
           for (int u = 0; u < U; ++u) {
-            float p = av[R * u];
-#pragma unroll
-            for (int k = 1; k < R; ++k) p = q == k ? av[k + R * u] : p;
-            // sum over the R lanes of column col % G (bitwise equal in each)
-            if constexpr (R >= 2) p += dpp<kRowRor8>(p);
-            if constexpr (R >= 4) p += dpp<kRowRor4>(p);
             const int tok = base + mi * 16 + rg * G + grp * U + u;
             sc[mi][rg * U + u] =
-                (tok < t1 && (!kCols || tok <= lim)) ? p * sl2 : -INFINITY;
+                (tok < t1 && (!kCols || tok <= lim)) ? pv[u] * sl2 : -INFINITY;
           }
         }
       }
@@ -842,7 +890,8 @@ struct MfmaSplitPath {
     }
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    if (col < G) {
+    if constexpr (F) __syncthreads();   // acc overlays every wave's V rows
+    if (col < NCOL) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -853,7 +902,7 @@ struct MfmaSplitPath {
         sm.l[wave][col] = l;
       }
     }
-    merge_waves<D, G>(sm, sink);
+    merge_waves<D, NCOL>(sm, sink);
   }
 };
 
@@ -903,32 +952,80 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(DecodeArgs a) {
   Path::run(a, sm, kvh, seq, t0, t1, last, sink);
 }
 
-// One workgroup of D threads per (query head, sequence): fold the fixed
-// partitions in order with the online-softmax recurrence.
+// Fold np partition states (m_p, s_p, O_p), rows base .. base+np-1 of the
+// workspace, into one normalised fp16 output row with the §4.6 merge:
+// M = max m_p, S = sum s_p e^(m_p - M), out = sum e^(m_p - M) O_p / S.
+// kFoldThreads threads; a row of O is read by D/2 lanes with 8-byte loads
+// (one wave per row at D = 128), so the workgroup folds kFoldThreads/(D/2)
+// rows at once and each lane keeps several rows in flight: the fold is
+// bound by the workspace read, not by one load's latency per partition.
+// Row slot r folds rows r, r + RPP, ...; the RPP partial sums are then
+// added in slot order, so the result does not depend on timing.
+constexpr int kFoldThreads = 512;
+
 template <int D>
-__global__ __launch_bounds__(D) void reduce_kernel(ReduceArgs a) {
+__device__ __forceinline__ void fold_states(const ReduceArgs& a, size_t base,
+                                            int np, _Float16* out_row) {
+  constexpr int LPR = D / 2;                    // lanes per row
+  constexpr int RPP = kFoldThreads / LPR;       // rows per pass
+  constexpr int NW = kFoldThreads / 64;
+  __shared__ float wmax[NW];
+  __shared__ float2 acc[RPP][LPR];
+  __shared__ float sacc[RPP];
+  const int t = threadIdx.x;
+  float mx = -INFINITY;
+  for (int p = t; p < np; p += kFoldThreads) mx = fmaxf(mx, a.ws_max[base + p]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((t & 63) == 0) wmax[t >> 6] = mx;
+  __syncthreads();
+  mx = wmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) mx = fmaxf(mx, wmax[w]);
+
+  const int r = t / LPR, c = t % LPR;
+  float sum = 0.f;
+  float2 o = make_float2(0.f, 0.f);
+#pragma unroll 4
+  for (int p = r; p < np; p += RPP) {
+    const float f = fast_exp2((a.ws_max[base + p] - mx) * kLog2e);
+    sum += a.ws_sum[base + p] * f;
+    const float2 v = reinterpret_cast<const float2*>(a.ws_out + (base + p) * D)[c];
+    o.x += v.x * f;
+    o.y += v.y * f;
+  }
+  acc[r][c] = o;
+  if (c == 0) sacc[r] = sum;
+  __syncthreads();
+  if (t < LPR) {
+    float S = 0.f, ox = 0.f, oy = 0.f;
+#pragma unroll
+    for (int q = 0; q < RPP; ++q) {
+      S += sacc[q];
+      ox += acc[q][t].x;
+      oy += acc[q][t].y;
+    }
+    out_row[2 * t] = (_Float16)(ox / S);
+    out_row[2 * t + 1] = (_Float16)(oy / S);
+  }
+}
+
+// One workgroup per (query head, sequence): fold the sequence's non-empty
+// fixed partitions.
+template <int D>
+__global__ __launch_bounds__(kFoldThreads) void reduce_kernel(ReduceArgs a) {
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
-  const int d = threadIdx.x;
   const int H = a.num_heads;
   int n = a.context_lens[seq];
   n = n < a.max_tokens ? n : a.max_tokens;
-  _Float16* o = a.out + ((size_t)seq * H + h) * D + d;
+  _Float16* o = a.out + ((size_t)seq * H + h) * D;
   if (n <= 0) {
-    *o = (_Float16)0.f;
+    if (threadIdx.x < D) o[threadIdx.x] = (_Float16)0.f;
     return;
   }
   const int np = (n + a.partition_size - 1) / a.partition_size;
-  const size_t base = ((size_t)seq * H + h) * a.max_partitions;
-  float mx = -INFINITY;
-  for (int p = 0; p < np; ++p) mx = fmaxf(mx, a.ws_max[base + p]);
-  float S = 0.f, O = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float f = fast_exp2((a.ws_max[base + p] - mx) * kLog2e);
-    S += a.ws_sum[base + p] * f;
-    O += a.ws_out[(base + p) * D + d] * f;
-  }
-  *o = (_Float16)(O / S);
+  fold_states<D>(a, ((size_t)seq * H + h) * a.max_partitions, np, o);
 }
 
 // Columns of the whole-line body for query tokens or group members: VG =
@@ -1189,13 +1286,12 @@ __global__ __launch_bounds__(kThreads) void multi_split_kernel(DecodeArgs a) {
   Path::run_cols(a, sm, kvh, seq, t0, t1, sink, qoff, ok ? pos0 + qj : -1);
 }
 
-// One workgroup of D threads per (query head, query row): fold the
-// partitions that hold the row's keys 0 .. pos (its causal limit).
+// One workgroup per (query head, query row): fold the partitions that hold
+// the row's keys 0 .. pos (its causal limit).
 template <int D>
-__global__ __launch_bounds__(D) void multi_reduce_kernel(ReduceArgs a) {
+__global__ __launch_bounds__(kFoldThreads) void multi_reduce_kernel(ReduceArgs a) {
   const int h = blockIdx.x;
   const int r = blockIdx.y;
-  const int d = threadIdx.x;
   const int H = a.num_heads;
   int lo = 0, hi = a.num_seqs - 1;              // sequence holding row r
   while (lo < hi) {
@@ -1207,23 +1303,14 @@ __global__ __launch_bounds__(D) void multi_reduce_kernel(ReduceArgs a) {
   int n = a.context_lens[lo];
   n = n < a.max_tokens ? n : a.max_tokens;
   const int pos = n - T + (r - a.cu_seqlens_q[lo]);
-  _Float16* o = a.out + ((size_t)r * H + h) * D + d;
+  _Float16* o = a.out + ((size_t)r * H + h) * D;
   if (n <= 0 || pos < 0) {
-    *o = (_Float16)0.f;
+    if (threadIdx.x < D) o[threadIdx.x] = (_Float16)0.f;
     return;
   }
   int np = pos / a.partition_size + 1;
   np = np < a.max_partitions ? np : a.max_partitions;
-  const size_t base = ((size_t)r * H + h) * a.max_partitions;
-  float mx = -INFINITY;
-  for (int q = 0; q < np; ++q) mx = fmaxf(mx, a.ws_max[base + q]);
-  float S = 0.f, O = 0.f;
-  for (int q = 0; q < np; ++q) {
-    const float f = fast_exp2((a.ws_max[base + q] - mx) * kLog2e);
-    S += a.ws_sum[base + q] * f;
-    O += a.ws_out[(base + q) * D + d] * f;
-  }
-  *o = (_Float16)(O / S);
+  fold_states<D>(a, ((size_t)r * H + h) * a.max_partitions, np, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -1345,9 +1432,7 @@ template <class P, int NCOLS, int D, int G>
 struct MultiCols {
   using Path = P;
   static constexpr int NC = NCOLS;
-  // The 16-column body with per-row limits needs more than 128 registers;
-  // its 50 KB of LDS allows three workgroups per CU, so aim for three waves.
-  static constexpr int kMinWaves = NCOLS == 16 ? 3 : P::kMinWaves;
+  static constexpr int kMinWaves = P::kColsMinWaves;
   // query row of column c (c / G-th of the sequence's rows), -1 if none
   __device__ static int64_t row_of(const DecodeArgs& a, int s, int c) {
     const int q0 = a.cu_seqlens_q[s];
@@ -1586,8 +1671,8 @@ struct PathFor<128, B, 4, EB> {
 };
 
 enum class Op { kPartition, kBalanced, kOccupancy, kMulti, kPrefix, kMultiSplit,
-                kPrefixSplit, kMultiBalanced, kMultiOccupancy, kMultiBalancedSplit,
-                kMultiSplitOccupancy };
+                kPrefixSplit, kMultiBalancedFull, kMultiFullOccupancy,
+                kMultiBalancedSplit, kMultiSplitOccupancy };
 
 // EB: bytes per cached element (2: fp16 pool, 1: fp8 e4m3 pool).  The fp8
 // pool has the balanced kernel only.
@@ -1607,9 +1692,9 @@ static hipError_t run_op(Op op, const DecodeArgs* a, dim3 grid,
       break;
   }
   if constexpr (EB == 2) {
-    using MC16 = MultiCols<MfmaPath<D, B, 16>, 16, D, G>;
     constexpr int VG = split_cols<D, G>();
     using MCS = MultiCols<MfmaSplitPath<D, B, VG, 2>, VG, D, G>;
+    using MCF = MultiCols<MfmaSplitPath<D, B, 8, 2, true>, 16, D, G>;
     switch (op) {
       case Op::kPartition:
         hipLaunchKernelGGL((partition_kernel<P, D, B, G>), grid, dim3(kThreads), 0, st, *a);
@@ -1626,13 +1711,13 @@ static hipError_t run_op(Op op, const DecodeArgs* a, dim3 grid,
       case Op::kPrefixSplit:
         hipLaunchKernelGGL((prefix_split_kernel<D, B, G>), grid, dim3(kThreads), 0, st, *a);
         return hipGetLastError();
-      case Op::kMultiBalanced:
-        hipLaunchKernelGGL((balanced_kernel<MC16, D, B, G>), grid, dim3(kThreads), 0,
+      case Op::kMultiBalancedFull:
+        hipLaunchKernelGGL((balanced_kernel<MCF, D, B, G>), grid, dim3(kThreads), 0,
                            st, *a);
         return hipGetLastError();
-      case Op::kMultiOccupancy:
+      case Op::kMultiFullOccupancy:
         return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            occ, reinterpret_cast<const void*>(&balanced_kernel<MC16, D, B, G>),
+            occ, reinterpret_cast<const void*>(&balanced_kernel<MCF, D, B, G>),
             kThreads, 0);
       case Op::kMultiBalancedSplit:
         hipLaunchKernelGGL((balanced_kernel<MCS, D, B, G>), grid, dim3(kThreads), 0,
@@ -1743,7 +1828,7 @@ hipError_t launch_prefix_marks(const DecodeArgs& a, int block_size,
 hipError_t launch_multi_balanced(const DecodeArgs& a, int head_size,
                                  int block_size, int group, int grid,
                                  bool whole_line, hipStream_t stream) {
-  return dispatch(whole_line ? Op::kMultiBalancedSplit : Op::kMultiBalanced,
+  return dispatch(whole_line ? Op::kMultiBalancedSplit : Op::kMultiBalancedFull,
                   head_size, block_size, group, &a, dim3(grid), stream, nullptr);
 }
 
@@ -1756,7 +1841,7 @@ int multi_balanced_grid(int head_size, int block_size, int group,
       hipSuccess)
     return 0;
   int per_cu = 0;
-  if (dispatch(whole_line ? Op::kMultiSplitOccupancy : Op::kMultiOccupancy,
+  if (dispatch(whole_line ? Op::kMultiSplitOccupancy : Op::kMultiFullOccupancy,
                head_size, block_size, group, nullptr, dim3(1), nullptr,
                &per_cu) != hipSuccess)
     return 0;
@@ -1768,10 +1853,10 @@ hipError_t launch_multi_reduce(const ReduceArgs& a, int head_size,
   dim3 grid(a.num_heads, num_q_tokens);
   switch (head_size) {
     case 64:
-      hipLaunchKernelGGL(multi_reduce_kernel<64>, grid, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL(multi_reduce_kernel<64>, grid, dim3(kFoldThreads), 0, stream, a);
       return hipGetLastError();
     case 128:
-      hipLaunchKernelGGL(multi_reduce_kernel<128>, grid, dim3(128), 0, stream, a);
+      hipLaunchKernelGGL(multi_reduce_kernel<128>, grid, dim3(kFoldThreads), 0, stream, a);
       return hipGetLastError();
   }
   return hipErrorInvalidValue;
@@ -1782,10 +1867,10 @@ hipError_t launch_reduce(const ReduceArgs& a, int head_size, int num_seqs,
   dim3 grid(a.num_heads, num_seqs);
   switch (head_size) {
     case 64:
-      hipLaunchKernelGGL(reduce_kernel<64>, grid, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL(reduce_kernel<64>, grid, dim3(kFoldThreads), 0, stream, a);
       return hipGetLastError();
     case 128:
-      hipLaunchKernelGGL(reduce_kernel<128>, grid, dim3(128), 0, stream, a);
+      hipLaunchKernelGGL(reduce_kernel<128>, grid, dim3(kFoldThreads), 0, stream, a);
       return hipGetLastError();
   }
   return hipErrorInvalidValue;

@@ -484,12 +484,16 @@ def test_multi_token_parity(name, balanced):
 
 @pytest.mark.parametrize("D,B,H,Hkv,T", [(128, 16, 16, 8, 2), (64, 32, 8, 8, 8),
                                          (128, 16, 8, 8, 3), (64, 16, 16, 2, 1),
-                                         (128, 64, 64, 8, 1), (128, 32, 32, 8, 5)])
+                                         (128, 64, 64, 8, 1), (128, 32, 32, 8, 5),
+                                         (64, 16, 16, 4, 3), (128, 16, 16, 8, 3),
+                                         (128, 32, 16, 2, 2)])
 @pytest.mark.parametrize("balanced", [False, True])
 def test_multi_token_shapes(D, B, H, Hkv, T, balanced):
-    """Shapes that run the whole-line body (g*T within its 4 or 8 columns,
-    partial tiles) and the 16-column body (g = 4, T = 5); the balanced
-    kernel where rows x heads fit 16 columns."""
+    """Shapes that run the whole-line body with g*T within its 4 or 8
+    columns (partial tiles), the whole-line body with 16 distinct columns
+    (balanced, g*T up to 16, some columns unused: g = 4 T = 3 at D = 64,
+    g = 2 T = 3, g = 8 T = 2) and the 16-column body (g = 4, T = 5); the
+    balanced kernel where rows x heads fit 16 columns."""
     print(f"[multi-shape] D{D} B{B} H{H}/{Hkv} T{T} balanced={balanced}", flush=True)
     w = workloads.make("c2_small_spec4", D=D, B=B, H=H, Hkv=Hkv, q_len=T,
                        seed=D + B + H + T)
