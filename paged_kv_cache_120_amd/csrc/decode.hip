@@ -589,7 +589,11 @@ template <int D, int B, int G, int EB, bool F = false>
 struct MfmaSplitPath {
   static constexpr int R = 16 / G;              // channel splits = rows per token
   static constexpr int U = 4 / R;               // useful D values per lane per MFMA
-  static constexpr int MT = D == 128 ? 1 : 2;   // 16-token tiles per batch
+  // 16-token tiles per batch.  The 16-column form at D = 128 takes two
+  // (twice the bytes in flight per wave, three waves per SIMD): measured on
+  // MI355X 4% faster on speculative verify (g = 4, 4 query tokens), while
+  // the decode bodies keep one and four waves (32 tokens lose 3% on GQA-4).
+  static constexpr int MT = (D == 128 && !F) ? 1 : 2;
   static constexpr int TB = 16 * MT;
   static constexpr int CPL = (16 / EB) < D / (4 * R) ? (16 / EB) : D / (4 * R);
   static constexpr int LC = R * 4 * CPL;        // channels of one line chunk
@@ -602,7 +606,7 @@ struct MfmaSplitPath {
   // two-way conflicted).
   static constexpr int VS = D + (G == 4 ? 16 : 8);
   static_assert((U * VS / 2) % 64 == 8, "V^T reads free of bank conflicts");
-  static constexpr int kMinWaves = 4;           // 128 VGPRs: 4 waves per SIMD
+  static constexpr int kMinWaves = (D == 128 && F) ? 3 : 4;  // 168 / 128 VGPRs
   static constexpr int kColsMinWaves = kMinWaves;
   static constexpr int NS = F ? R : 1;          // score passes
   static constexpr int NCOL = F ? 16 : G;       // distinct columns
@@ -955,26 +959,29 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(DecodeArgs a) {
 // Fold np partition states (m_p, s_p, O_p), rows base .. base+np-1 of the
 // workspace, into one normalised fp16 output row with the §4.6 merge:
 // M = max m_p, S = sum s_p e^(m_p - M), out = sum e^(m_p - M) O_p / S.
-// kFoldThreads threads; a row of O is read by D/2 lanes with 8-byte loads
-// (one wave per row at D = 128), so the workgroup folds kFoldThreads/(D/2)
-// rows at once and each lane keeps several rows in flight: the fold is
-// bound by the workspace read, not by one load's latency per partition.
-// Row slot r folds rows r, r + RPP, ...; the RPP partial sums are then
-// added in slot order, so the result does not depend on timing.
-constexpr int kFoldThreads = 512;
+// NT threads; a row of O is read by D/2 lanes with 8-byte loads (one wave
+// per row at D = 128), so the workgroup folds NT/(D/2) rows at once and each
+// lane keeps several rows in flight: the fold is bound by the workspace
+// read, not by one load's latency per partition.  Row slot r folds rows r,
+// r + RPP, ...; the RPP partial sums are then added in slot order, so the
+// result does not depend on timing.  Launches pick NT = 512 when rows may
+// hold many partitions (long contexts) and 128 otherwise, where wider
+// workgroups would mostly idle.
+template <int NT>
+constexpr int fold_rows_per_pass(int D) { return NT / (D / 2); }
 
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void fold_states(const ReduceArgs& a, size_t base,
                                             int np, _Float16* out_row) {
   constexpr int LPR = D / 2;                    // lanes per row
-  constexpr int RPP = kFoldThreads / LPR;       // rows per pass
-  constexpr int NW = kFoldThreads / 64;
+  constexpr int RPP = fold_rows_per_pass<NT>(D);
+  constexpr int NW = NT / 64;
   __shared__ float wmax[NW];
   __shared__ float2 acc[RPP][LPR];
   __shared__ float sacc[RPP];
   const int t = threadIdx.x;
   float mx = -INFINITY;
-  for (int p = t; p < np; p += kFoldThreads) mx = fmaxf(mx, a.ws_max[base + p]);
+  for (int p = t; p < np; p += NT) mx = fmaxf(mx, a.ws_max[base + p]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   if ((t & 63) == 0) wmax[t >> 6] = mx;
@@ -1012,8 +1019,8 @@ __device__ __forceinline__ void fold_states(const ReduceArgs& a, size_t base,
 
 // One workgroup per (query head, sequence): fold the sequence's non-empty
 // fixed partitions.
-template <int D>
-__global__ __launch_bounds__(kFoldThreads) void reduce_kernel(ReduceArgs a) {
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void reduce_kernel(ReduceArgs a) {
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const int H = a.num_heads;
@@ -1025,7 +1032,7 @@ __global__ __launch_bounds__(kFoldThreads) void reduce_kernel(ReduceArgs a) {
     return;
   }
   const int np = (n + a.partition_size - 1) / a.partition_size;
-  fold_states<D>(a, ((size_t)seq * H + h) * a.max_partitions, np, o);
+  fold_states<D, NT>(a, ((size_t)seq * H + h) * a.max_partitions, np, o);
 }
 
 // Columns of the whole-line body for query tokens or group members: VG =
@@ -1288,8 +1295,8 @@ __global__ __launch_bounds__(kThreads) void multi_split_kernel(DecodeArgs a) {
 
 // One workgroup per (query head, query row): fold the partitions that hold
 // the row's keys 0 .. pos (its causal limit).
-template <int D>
-__global__ __launch_bounds__(kFoldThreads) void multi_reduce_kernel(ReduceArgs a) {
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void multi_reduce_kernel(ReduceArgs a) {
   const int h = blockIdx.x;
   const int r = blockIdx.y;
   const int H = a.num_heads;
@@ -1310,7 +1317,7 @@ __global__ __launch_bounds__(kFoldThreads) void multi_reduce_kernel(ReduceArgs a
   }
   int np = pos / a.partition_size + 1;
   np = np < a.max_partitions ? np : a.max_partitions;
-  fold_states<D>(a, ((size_t)r * H + h) * a.max_partitions, np, o);
+  fold_states<D, NT>(a, ((size_t)r * H + h) * a.max_partitions, np, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -1848,32 +1855,40 @@ int multi_balanced_grid(int head_size, int block_size, int group,
   return per_cu > 0 ? per_cu * cus : 0;
 }
 
-hipError_t launch_multi_reduce(const ReduceArgs& a, int head_size,
-                               int num_q_tokens, hipStream_t stream) {
-  dim3 grid(a.num_heads, num_q_tokens);
+// the partition folds: kMulti picks the per-query-row form
+template <bool kMulti, int D, int NT>
+static void fold_launch(const ReduceArgs& a, dim3 grid, hipStream_t stream) {
+  if constexpr (kMulti)
+    hipLaunchKernelGGL((multi_reduce_kernel<D, NT>), grid, dim3(NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((reduce_kernel<D, NT>), grid, dim3(NT), 0, stream, a);
+}
+
+template <bool kMulti>
+static hipError_t launch_fold(const ReduceArgs& a, int head_size, dim3 grid,
+                              hipStream_t stream) {
+  const bool wide = a.max_partitions >= 32;
   switch (head_size) {
     case 64:
-      hipLaunchKernelGGL(multi_reduce_kernel<64>, grid, dim3(kFoldThreads), 0, stream, a);
+      if (wide) fold_launch<kMulti, 64, 512>(a, grid, stream);
+      else fold_launch<kMulti, 64, 128>(a, grid, stream);
       return hipGetLastError();
     case 128:
-      hipLaunchKernelGGL(multi_reduce_kernel<128>, grid, dim3(kFoldThreads), 0, stream, a);
+      if (wide) fold_launch<kMulti, 128, 512>(a, grid, stream);
+      else fold_launch<kMulti, 128, 128>(a, grid, stream);
       return hipGetLastError();
   }
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_multi_reduce(const ReduceArgs& a, int head_size,
+                               int num_q_tokens, hipStream_t stream) {
+  return launch_fold<true>(a, head_size, dim3(a.num_heads, num_q_tokens), stream);
+}
+
 hipError_t launch_reduce(const ReduceArgs& a, int head_size, int num_seqs,
                          hipStream_t stream) {
-  dim3 grid(a.num_heads, num_seqs);
-  switch (head_size) {
-    case 64:
-      hipLaunchKernelGGL(reduce_kernel<64>, grid, dim3(kFoldThreads), 0, stream, a);
-      return hipGetLastError();
-    case 128:
-      hipLaunchKernelGGL(reduce_kernel<128>, grid, dim3(kFoldThreads), 0, stream, a);
-      return hipGetLastError();
-  }
-  return hipErrorInvalidValue;
+  return launch_fold<false>(a, head_size, dim3(a.num_heads, num_seqs), stream);
 }
 
 }  // namespace pa
