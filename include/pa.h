@@ -324,9 +324,9 @@ pa_status pa_decode_balanced(void* out, const void* query,
  * first key (T > n), get zeros.
  * pa_multi_balanced_grid: resident workgroups of this kernel for this
  *   max_q_per_seq (0 if unsupported or unknown); pass the same
- *   max_q_per_seq to pa_decode_multi_balanced, which picks the whole-line
- *   matrix-core body when max_q_per_seq * g fits its 4 or 8 columns and
- *   the 16-column body otherwise.
+ *   max_q_per_seq to pa_decode_multi_balanced, which picks the matrix-core
+ *   body with 4 or 8 columns when max_q_per_seq * g fits them and its
+ *   16-column form otherwise.
  * pa_multi_balanced_workspace_size: the same fixed counter header as
  *   pa_balanced_workspace_size, then fp32 max/sum [rows] and out [rows,
  *   head_size], rows = (grid + num_seqs * num_kv_heads) * 16 (0 when

@@ -372,8 +372,9 @@ pa_status pa_decode_shared_prefix(
   const int64_t pm = max_partitions(max_blocks_per_seq, block_size, partition_size);
   if (pm > 65535) return PA_ERR_SHAPE;        // grid.z
   const int32_t g = num_heads / num_kv_heads;
-  // members per prefix tile: the whole-line body when it needs no more
-  // tiles than the 16-column body
+  // members per prefix tile: the narrow form of the matrix-core body
+  // (split_columns/g members) when it needs no more tiles than the
+  // 16-column form
   const int64_t per16 = 16 / g;
   const int64_t perw = pa::split_columns(head_size, g) / g;
   const int64_t tiles16 = (max_group_size + per16 - 1) / per16;
@@ -477,8 +478,9 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache,
     return PA_ERR_SHAPE;
   if (num_seqs == 0 || num_q_tokens == 0) return PA_OK;
   const int32_t g = num_heads / num_kv_heads;
-  // the whole-line body (split_columns/g query tokens per tile) when it needs
-  // no more tiles, i.e. no more K/V passes, than the 16-column body
+  // the narrow form of the matrix-core body (split_columns/g query tokens
+  // per tile) when it needs no more tiles, i.e. no more K/V passes, than the
+  // 16-column form
   const int64_t per16 = 16 / g;
   const int64_t perw = pa::split_columns(head_size, g) / g;
   const int64_t tiles16 = (max_q_per_seq + per16 - 1) / per16;

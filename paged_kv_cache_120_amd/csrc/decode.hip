@@ -9,8 +9,11 @@
 // A workgroup (4 waves) processes a token range [t0, t1) of one (kv head,
 // sequence) and serves all g query heads of that kv head, so each K/V byte is
 // fetched from HBM once and reused g times.  Two range bodies exist:
-//   ValuPath -- vector ALU, dot products reduced with DPP (g = 1, 2, 4);
-//   MfmaPath -- both contractions on the matrix cores (g = 8).
+//   ValuPath      -- vector ALU, dot products reduced with DPP (g = 1, 2,
+//                    and 4 at head size 64);
+//   MfmaSplitPath -- both contractions on the matrix cores (g = 8, g = 4 at
+//                    head size 128, and 16 columns of (query token, head)
+//                    or (member, head) pairs).
 // Kernels driving them:
 //   partition_kernel -- one range per workgroup: a whole sequence (single
 //                       pass) or one fixed partition (split-KV);
@@ -365,208 +368,21 @@ struct ValuPath {
 // Matrix-core range bodies
 // ---------------------------------------------------------------------------
 //
-// MfmaPath: 16 MFMA columns given by the caller (the multi-token kernel's
-// (query token, head) pairs).  Per wave, a batch is MT tiles of 16 tokens (one at D = 128, which keeps
-// the kernel within 128 VGPRs: four waves per SIMD).  Two MFMA shapes:
-//   S^T (16 tokens x 16 heads) = K x Q^T with the 16x16x32 fp16 MFMA (lane l
-//        holds A[l%16][8(l/16)+i], B[8(l/16)+i][l%16], D[4(l/16)+i][l%16]):
-//        A is a 16-byte load of token l%16, channels 32kk + 8(l/16)..; B is
-//        the group's query heads (zero past g); D/32 MFMAs per tile;
-//   O^T (16 channels x 16 heads) += V^T x P^T with the 16x16x16 fp16 MFMA
-//        (lane l holds A[l%16][4(l/16)+i], B[4(l/16)+i][l%16]), D/16 MFMAs
-//        per tile.
-// P^T needs no data movement: the four S^T values a lane holds (tokens
-// 4(l/16)+i of head l%16) are exactly its B slots.  V^T is the transposed V
-// tile, so V goes through LDS: each lane stores its 16-byte rows, then
-// gathers its column (4 tokens of one channel) with 2-byte reads; rows are
-// padded by 8 bytes so the four lane groups of a read hit disjoint banks.
-// Every per-head quantity (running max, sum, rescale factor) lives in the
-// lanes owning that head's column, and O^T's rows are channels, so the
-// rescale is lane-local.
-template <int D, int B, int G>
-struct MfmaPath {
-  static constexpr int MT = D == 128 ? 1 : 2;   // 16-token tiles per batch
-  static constexpr int TB = 16 * MT;
-  static constexpr int KK = D / 32;             // MFMA k-steps over channels
-  static constexpr int DT = D / 16;             // channel tiles of O^T
-  static constexpr int VS = D + 4;              // padded LDS row (halves)
-  static constexpr int kMinWaves = 4;           // 128 VGPRs: 4 waves per SIMD
-  // With per-row key limits the 16-column body needs more than 128
-  // registers; its 50 KB of LDS allows three workgroups per CU anyway.
-  static constexpr int kColsMinWaves = G == 16 ? 3 : kMinWaves;
-  static_assert(B % 16 == 0, "a tile must not straddle two blocks");
-  static_assert(G <= 16, "one MFMA column per query row");
-
-  struct Smem {
-    _Float16 vs[kWaves][TB][VS];
-    float acc[kWaves][G][D];
-    float m[kWaves][G];
-    float l[kWaves][G];
-  };
-
-  // Keys [t0, t1) of head kvh (t0 a multiple of 16) for 16 columns given
-  // by the caller: this lane's column reads the query row at element offset
-  // qoff (-1: an unused column, zero query) and attends to keys t <= lim
-  // only (the causal limit of a query token).
-  template <class Sink>
-  __device__ static void run_cols(const DecodeArgs& a, Smem& sm, int kvh,
-                                  int seq, int t0, int t1, Sink& sink,
-                                  int64_t qoff, int lim) {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int col = lane & 15;                  // token row (A) / column (B, D)
-    const int grp = lane >> 4;                  // lane group 0..3
-
-    f16x8 qb[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (qoff >= 0)
-        v = *reinterpret_cast<const u32x4*>(a.query + qoff + kk * 32 + grp * 8);
-      qb[kk] = __builtin_bit_cast(f16x8, v);
-    }
-
-    BlockWindow bw;
-    bw.init(a.block_tables + (size_t)seq * a.max_blocks_per_seq, t0 / B,
-            (t1 + B - 1) / B, lane);
-    const uint32_t row_stride = (uint32_t)a.num_kv_heads * D * 2;
-    const uint64_t blk_bytes = (uint64_t)B * row_stride;
-    const char* kbase = a.key_cache + (size_t)kvh * D * 2;
-    const char* vbase = a.value_cache + (size_t)kvh * D * 2;
-    const float sl2 = a.scale * kLog2e;
-
-    float m = -INFINITY;                        // reference of head `col`
-    float mt = -INFINITY;                       // its true running max
-    float l = 0.f;                              // this lane's share of the sum
-    f32x4 o[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    _Float16* vw = &sm.vs[wave][0][0];
-
-    for (int base = t0 + wave * TB; base < t1; base += kWaves * TB) {
-      bw.cover(base / B, (base + TB - 1) / B, lane);
-      u32x4 kr[MT][KK], vr[MT][KK];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int tile0 = base + mt * 16;       // wave-uniform
-        const int lb = tile0 / B;
-        const int blk = bw.block(lb);
-        const __amdgpu_buffer_rsrc_t rk = block_rsrc<B>(
-            kbase, blk, lb, t1, row_stride, blk_bytes, a.num_blocks);
-        const __amdgpu_buffer_rsrc_t rv = block_rsrc<B>(
-            vbase, blk, lb, t1, row_stride, blk_bytes, a.num_blocks);
-        const uint32_t off =
-            (uint32_t)(tile0 % B + col) * row_stride + grp * 16;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          kr[mt][kk] = load16<kLoadCached>(rk, off + kk * 64);   // half lines
-          vr[mt][kk] = load16<kLoadCached>(rv, off + kk * 64);
-        }
-      }
-
-      // scores: the lane holds tokens tile0 + 4grp + i of head `col`
-      float sc[MT][4];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              __builtin_bit_cast(f16x8, kr[mt][kk]), qb[kk], acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = base + mt * 16 + grp * 4 + i;
-          sc[mt][i] = (tok < t1 && tok <= lim) ? acc[i] * sl2 : -INFINITY;
-        }
-      }
-
-      // V tile to LDS in token-major rows (two 8-byte stores per chunk)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          _Float16* dst = vw + (mt * 16 + col) * VS + kk * 32 + grp * 8;
-          const u32x4 v = vr[mt][kk];
-          reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
-          reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
-        }
-
-      // online softmax for head `col` (max over the batch and the 4 groups)
-      float bm = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[mt][i]);
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      // lazy reference: rescale only when the batch max exceeds it by more
-      // than kSlack (weights stay <= 2^kSlack, well inside fp16)
-      mt = fmaxf(mt, bm);
-      if (__builtin_amdgcn_ballot_w64(bm > m + kSlack)) {
-        const float mn = fmaxf(m, mt);
-        const float al = fast_exp2(m - (mn == -INFINITY ? 0.f : mn));
-        l *= al;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
-        m = mn;
-      }
-      const float sh = m == -INFINITY ? 0.f : m;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sc[mt][i] = fast_exp2(sc[mt][i] - sh);
-          l += sc[mt][i];
-        }
-
-      // O^T += V^T P^T, one k-step of 16 tokens per tile
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f16x4 pb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pb[i] = (_Float16)sc[mt][i];
-        const _Float16* vrow = vw + (mt * 16 + grp * 4) * VS + col;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          f16x4 va;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) va[i] = vrow[i * VS + dt * 16];
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, o[dt], 0, 0, 0);
-        }
-      }
-    }
-
-    // state relative to the true max; the sum over the 4 lane groups; then
-    // merge the waves through LDS
-    {
-      const float f = mt == -INFINITY ? 1.f : fast_exp2(m - mt);
-      l *= f;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= f;
-      m = mt;
-    }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (col < G) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sm.acc[wave][col][dt * 16 + grp * 4 + i] = o[dt][i];
-      if (grp == 0) {
-        sm.m[wave][col] = m;
-        sm.l[wave][col] = l;
-      }
-    }
-    merge_waves<D, G>(sm, sink);
-  }
-};
-
-// MfmaSplitPath: the decode body for a group of g = 8 or 4 on the matrix
-// cores, with whole-line K/V loads.  MfmaPath's operand layout loads 64
-// bytes of each of 16 rows per instruction (half lines).  Here MFMA row i is
-// token i/R and channel split i%R of each line chunk (R = 16/g), so one
-// instruction fetches g tokens x R*64 contiguous bytes.  For the product to
+// MfmaSplitPath: the range body on the matrix cores (groups of g = 8, and 4
+// at head size 128; multi-token and shared-prefix columns).  Two MFMA
+// shapes, lane l holding A[l%16][k], B[k][l%16] for k in its group l/16's
+// slice of K, and D[4(l/16)+i][l%16]:
+//   S^T (16 rows x 16 columns) = K x Q^T with the 16x16x32 fp16 MFMA (A: 8
+//        channels of a row per lane, B: the query channels of a column);
+//   O^T (16 channels x 16 columns) += V^T x P^T with the 16x16x16 fp16
+//        MFMA; P^T needs no data movement (the four scores a lane holds are
+//        its B slots), V^T goes through LDS: token-major rows stored with
+//        8-byte writes, gathered a column (4 tokens of one channel) at a
+//        time with 2-byte reads.
+// With one token per MFMA row a load instruction would fetch 64 bytes of
+// each of 16 rows (half lines).  Here MFMA row i is token i/R and channel
+// split i%R of each line chunk (R = 16/g), so one instruction fetches g
+// tokens x R*64 contiguous bytes.  For the product to
 // stay a matrix product, the split also indexes the columns: the 16 B
 // columns are (head n%g, split n/g).  Column (h, q) multiplies every row by
 // head h's channels of split q; only the rows of split q are kept, and the R
@@ -575,7 +391,10 @@ struct MfmaPath {
 // and P.V, and only columns < g are stored.  A tile of 16 tokens takes R
 // MFMA row groups of g tokens; a lane's four score slots are tokens
 // T(j) = (j/U)*g + (lane/16)*U + j%U of the tile (U = 4/R), and the P.V
-// k-order follows T, which only changes which LDS rows V^T reads.
+// k-order follows T, which only changes which LDS rows V^T reads.  Every
+// per-column quantity (running max, sum, rescale factor) lives in the lanes
+// owning that column, and O^T's rows are channels, so the rescale is
+// lane-local.
 // CPL channels per lane per load: min(16 bytes, D/(4R) channels), >= 8.
 //
 // Full (F = true): all 16 columns distinct, for query columns of several
@@ -1058,8 +877,9 @@ constexpr int split_cols() {
 // head, partition) state goes to the workspace and multi_reduce_kernel folds
 // the partitions of each row.
 template <int D, int B, int G>
-__global__ __launch_bounds__(kThreads) void multi_kernel(DecodeArgs a) {
-  using Path = MfmaPath<D, B, 16>;
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    MfmaSplitPath<D, B, 8, 2, true>::kMinWaves))) void multi_kernel(DecodeArgs a) {
+  using Path = MfmaSplitPath<D, B, 8, 2, true>;
   constexpr int QT = 16 / G;                   // query tokens per tile
   __shared__ typename Path::Smem sm;
   const int kvh = blockIdx.x;
@@ -1155,8 +975,9 @@ __global__ __launch_bounds__(256) void prefix_marks_kernel(DecodeArgs a,
 }
 
 template <int D, int B, int G>
-__global__ __launch_bounds__(kThreads) void prefix_kernel(DecodeArgs a) {
-  using Path = MfmaPath<D, B, 16>;
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    MfmaSplitPath<D, B, 8, 2, true>::kMinWaves))) void prefix_kernel(DecodeArgs a) {
+  using Path = MfmaSplitPath<D, B, 8, 2, true>;
   constexpr int MPT = 16 / G;                  // members per tile
   __shared__ typename Path::Smem sm;
   const int kvh = blockIdx.x;
@@ -1246,8 +1067,8 @@ __global__ __launch_bounds__(kThreads) void prefix_split_kernel(DecodeArgs a) {
   Path::run_cols(a, sm, kvh, lead, t0, t1, sink, qoff, ok ? n - 1 : -1);
 }
 
-// multi_kernel on the whole-line body: VG/g query tokens per tile (used
-// when that needs no more tiles than the 16-column body).
+// multi_kernel on the narrow form of the matrix-core body: VG/g query tokens
+// per tile (used when that needs no more tiles than the 16-column form).
 template <int D, int B, int G>
 __global__ __launch_bounds__(kThreads) void multi_split_kernel(DecodeArgs a) {
   constexpr int VG = split_cols<D, G>();
@@ -1405,8 +1226,8 @@ __device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* wave_sum,
 // What a (sequence, kv head) pair of the balanced split computes, and where
 // its NC columns go.  DecodeCols: one query row per sequence, the pair's g
 // heads.  MultiCols: the sequence's T query rows x g heads (T*g <= NC), each
-// row with its causal key limit, on the whole-line matrix-core body (NC = 4
-// or 8 columns) or the 16-column one.
+// row with its causal key limit, on the matrix-core body with NC = 4 or 8
+// columns (one score pass) or 16 (R score passes).
 template <class P, int D, int G>
 struct DecodeCols {
   using Path = P;
