@@ -27,14 +27,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
 }
 
 // Cache policy of K/V loads (the buffer instruction's aux bits).  Rows are
-// read once per decode step, so a load that fetches whole 128-byte lines uses
-// the non-temporal policy (kLoadNt, aux bit 1 -> `nt`): on MI355X this lifts
-// a paged 256-byte-segment read stream from ~6.0 to ~6.8 TB/s.  A load that
-// fetches half lines (the matrix-core operand layout: 64 bytes of each of 16
-// rows) uses the default policy (kLoadCached), so the second half of each
-// line, loaded by the next instruction, hits in the vector L1 (c5: +5%).
+// read once per decode step and every load fetches whole 128-byte lines, so
+// they use the non-temporal policy (kLoadNt, aux bit 1 -> `nt`): on MI355X
+// this lifts a paged 256-byte-segment read stream from ~6.0 to ~6.8 TB/s.
 constexpr int kLoadNt = 2;
-constexpr int kLoadCached = 0;
 
 template <int AUX = kLoadNt>
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r,

@@ -72,8 +72,8 @@ hipError_t launch_decode(const DecodeArgs& a, int head_size, int block_size,
                          int group, dim3 grid, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_size, int num_seqs,
                          hipStream_t stream);
-// whole_line: the whole-line body with split_columns() columns per tile
-// instead of the 16-column body
+// whole_line: the matrix-core body with split_columns() columns per tile
+// instead of its 16-column form
 hipError_t launch_multi(const DecodeArgs& a, int head_size, int block_size,
                         int group, dim3 grid, bool whole_line,
                         hipStream_t stream);
