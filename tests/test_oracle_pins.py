@@ -696,3 +696,43 @@ def test_fp8_decode_equals_fp16_decode_of_the_dequantised_pool():
     pairs = [(2, 7), (0, 0), (1, 3)]
     sub = oracle.decode_fp8(q, kc, vc, bt, cl, 0.125, ks, vs, pairs=pairs)
     assert np.allclose(sub, np.stack([ref[i, h] for i, h in pairs]), rtol=1e-12, atol=1e-14)
+
+
+def test_fp8_phases_copy_on_write():
+    """apply_phases_fp8 on a write, then a copy-on-write step ([P5] §4.3: the
+    writer gets a private copy of a shared block, the other sharers keep the
+    original): the copied block holds exactly the source's codes, a chained
+    copy (A -> B, then B -> C in a later phase) leaves C equal to A, every
+    block the phases do not name keeps its codes, and a decode through a
+    table that points at the copy gives the same result as one through the
+    original block."""
+    from workloads import CopyPhase, WritePhase
+    rng = np.random.default_rng(12)
+    nb, B, Hkv, D, H = 6, 4, 2, 8, 4
+    kc = rng.integers(0, 256, (nb, B, Hkv, D), dtype=np.uint8)
+    kc[kc == 0x7F] = 0
+    kc[kc == 0xFF] = 0
+    vc = kc[::-1].copy()
+    before_k, before_v = kc.copy(), vc.copy()
+    table = np.array([[2, 4]], np.int32)
+    key = (rng.standard_normal((6, Hkv, D)) * 3).astype(np.float16)
+    val = (rng.standard_normal((6, Hkv, D)) * 3).astype(np.float16)
+    write = WritePhase(table, np.zeros(6, np.int32), np.arange(6, dtype=np.int32), key, val)
+    # within a phase no destination is also a source (the copy's
+    # precondition); the chain runs over two phases
+    first = CopyPhase(np.array([2], np.int32), np.array([0], np.int32))
+    second = CopyPhase(np.array([0], np.int32), np.array([5], np.int32))
+    oracle.apply_phases_fp8(kc, vc, [write, first, None, second], B, 0.05, 0.04)
+    # rows 0..3 of block 2 and 0..1 of block 4 were written; 2 -> 0, then 0 -> 5
+    assert (kc[0] == kc[2]).all() and (vc[0] == vc[2]).all()
+    assert (kc[5] == kc[2]).all() and (vc[5] == vc[2]).all()
+    for b in (1, 3):
+        assert (kc[b] == before_k[b]).all() and (vc[b] == before_v[b]).all()
+    assert (kc[4, 2:] == before_k[4, 2:]).all()          # past the written rows
+    assert not (kc[2] == before_k[2]).all()             # the write landed
+    q = rng.standard_normal((1, H, D)).astype(np.float16)
+    orig = oracle.decode_fp8(q, kc, vc, np.array([[2, 4]], np.int32),
+                             np.array([6], np.int32), 0.25, 0.05, 0.04)
+    via_copy = oracle.decode_fp8(q, kc, vc, np.array([[5, 4]], np.int32),
+                                 np.array([6], np.int32), 0.25, 0.05, 0.04)
+    assert (orig == via_copy).all()
