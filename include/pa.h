@@ -317,11 +317,16 @@ pa_status pa_decode_balanced(void* out, const void* query,
  * Multi-token queries on the balanced split: pa_decode_multi's result
  * (same rows, causal limits and tolerance) in ONE kernel, with the work of
  * every (sequence, kv head) pair cut into equal slices as for
- * pa_decode_balanced and cut pairs merged in-kernel.  A sequence's T query
- * rows x g heads share one pass over its keys, so T * g <= 16 is required
- * (max_q_per_seq * g > 16: PA_ERR_UNSUPPORTED; use pa_decode_multi).
- * Rows of a sequence with context_lens <= 0, and rows placed before the
- * first key (T > n), get zeros.
+ * pa_decode_balanced and cut pairs merged in-kernel.  Up to 16 of a
+ * sequence's query rows x g heads share one pass over its keys (a column
+ * tile); with max_q_per_seq * g > 16 (chunked prefill) each (sequence, kv
+ * head) carries ceil(max_q_per_seq * g / 16) tiles, laid end to end in the
+ * balanced split, and a sequence with T rows uses ceil(T * g / 16) of
+ * them.  Rows of a sequence with context_lens <= 0, and rows placed before
+ * the first key (T > n), get zeros.  Precondition: no sequence has more
+ * than max_q_per_seq rows (rows past it are not computed).  Each tile reads
+ * the pair's keys again; from two tiles up the two-kernel pa_decode_multi,
+ * whose partitions the hardware dispatcher balances, measured faster.
  * pa_multi_balanced_grid: resident workgroups of this kernel for this
  *   max_q_per_seq (0 if unsupported or unknown); pass the same
  *   max_q_per_seq to pa_decode_multi_balanced, which picks the matrix-core
@@ -334,7 +339,14 @@ pa_status pa_decode_balanced(void* out, const void* query,
  *   before the first call; each completed call leaves the counters zero, so
  *   the workspace serves later calls of any shape it is large enough for
  *   (a decode workspace of the same size may be shared with it); calls
- *   sharing a workspace must not overlap.
+ *   sharing a workspace must not overlap.  Sized for one column tile per
+ *   (sequence, kv head), i.e. max_q_per_seq * g <= 16.
+ * pa_multi_balanced_workspace_size_tiles: the same for any max_q_per_seq:
+ *   rows = (grid + num_seqs * num_kv_heads * tiles) * 16 with tiles = 1
+ *   when max_q_per_seq * g fits the 4 or 8 columns, else
+ *   ceil(max_q_per_seq * g / 16); 0 when num_seqs * num_kv_heads * tiles
+ *   exceeds PA_BALANCED_MAX_PAIRS.  pa_decode_multi_balanced requires this
+ *   size (equal to pa_multi_balanced_workspace_size for one tile).
  * Other arguments as pa_decode_multi ([BOOK] §4.5 (2)).
  */
 int32_t pa_multi_balanced_grid(int32_t num_heads, int32_t num_kv_heads,
@@ -342,6 +354,10 @@ int32_t pa_multi_balanced_grid(int32_t num_heads, int32_t num_kv_heads,
                                int32_t max_q_per_seq);
 size_t pa_multi_balanced_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
                                         int32_t head_size, int32_t grid);
+size_t pa_multi_balanced_workspace_size_tiles(int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads,
+                                              int32_t head_size, int32_t grid,
+                                              int32_t max_q_per_seq);
 pa_status pa_decode_multi_balanced(
     void* out, const void* query, const void* key_cache, const void* value_cache,
     const int32_t* block_tables, int32_t max_blocks_per_seq,

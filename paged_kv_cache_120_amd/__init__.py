@@ -22,6 +22,7 @@ __all__ = [
     "pa_decode_step", "pa_multi_workspace_size", "pa_decode_multi",
     "pa_cache_write_fp8", "pa_balanced_grid_fp8", "pa_decode_balanced_fp8",
     "pa_decode_step_fp8", "pa_multi_balanced_grid", "pa_multi_balanced_workspace_size",
+    "pa_multi_balanced_workspace_size_tiles",
     "pa_decode_multi_balanced",
     "pa_prefix_workspace_size", "pa_decode_shared_prefix", "pa_decode_step_noalloc",
     "pa_last_check", "STATUS",
@@ -85,6 +86,7 @@ def _load() -> ctypes.CDLL:
         "pa_prefix_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
         "pa_multi_balanced_grid": (i32, [i32, i32, i32, i32, i32]),
         "pa_multi_balanced_workspace_size": (sz, [i32, i32, i32, i32]),
+        "pa_multi_balanced_workspace_size_tiles": (sz, [i32, i32, i32, i32, i32, i32]),
         "pa_decode_multi_balanced": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32,
                                                     vp, i32, i32, i32, i32, i32, i32, f32,
                                                     i32, vp, sz, vp]),
@@ -173,6 +175,15 @@ def pa_multi_balanced_workspace_size(num_seqs: int, num_kv_heads: int, head_size
                                      grid: int) -> int:
     return int(_lib().pa_multi_balanced_workspace_size(num_seqs, num_kv_heads, head_size,
                                                        grid))
+
+
+def pa_multi_balanced_workspace_size_tiles(num_seqs: int, num_heads: int,
+                                           num_kv_heads: int, head_size: int, grid: int,
+                                           max_q_per_seq: int) -> int:
+    """Workspace of pa_decode_multi_balanced for any max_q_per_seq (one
+    counter and state row group per (sequence, kv head, column tile))."""
+    return int(_lib().pa_multi_balanced_workspace_size_tiles(
+        num_seqs, num_heads, num_kv_heads, head_size, grid, max_q_per_seq))
 
 
 def pa_prefix_workspace_size(num_seqs: int, num_heads: int, head_size: int,

@@ -540,9 +540,17 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache,
   return hip_status(pa::launch_multi_reduce(r, head_size, num_q_tokens, stream));
 }
 
-// the whole-line body when a sequence's rows x heads fit its columns
+// the narrow form of the matrix-core body when a sequence's rows x heads
+// fit its columns, else the 16-column form
 static bool multi_whole_line(int32_t head_size, int32_t g, int32_t max_q) {
   return (int64_t)max_q * g <= pa::split_columns(head_size, g);
+}
+
+// column tiles per (sequence, kv head) of the balanced multi-token kernel:
+// one for the narrow form, ceil(max_q * g / 16) for the 16-column form
+static int64_t multi_tiles(int32_t head_size, int32_t g, int32_t max_q) {
+  if (multi_whole_line(head_size, g, max_q)) return 1;
+  return ((int64_t)max_q * g + 15) / 16;
 }
 
 int32_t pa_multi_balanced_grid(int32_t num_heads, int32_t num_kv_heads,
@@ -551,7 +559,7 @@ int32_t pa_multi_balanced_grid(int32_t num_heads, int32_t num_kv_heads,
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
       !supported_head(head_size) || !supported_block(block_size) ||
       !supported_group(num_heads / num_kv_heads) || max_q_per_seq <= 0 ||
-      (int64_t)max_q_per_seq * (num_heads / num_kv_heads) > 16)
+      max_q_per_seq > 65535)
     return 0;
   const int32_t g = num_heads / num_kv_heads;
   return pa::multi_balanced_grid(head_size, block_size, g,
@@ -569,6 +577,22 @@ size_t pa_multi_balanced_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
   return kCounterBytes + (size_t)(rows * 8 + rows * head_size * 4);
 }
 
+// the same layout with a counter and a state row group per (sequence, kv
+// head, column tile)
+size_t pa_multi_balanced_workspace_size_tiles(int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads,
+                                              int32_t head_size, int32_t grid,
+                                              int32_t max_q_per_seq) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+      num_heads % num_kv_heads != 0 || head_size <= 0 || grid <= 0 ||
+      max_q_per_seq <= 0 || max_q_per_seq > 65535)
+    return 0;
+  const int64_t tl = multi_tiles(head_size, num_heads / num_kv_heads, max_q_per_seq);
+  if ((uint64_t)num_seqs * num_kv_heads * tl > kCounterSlots) return 0;
+  const uint64_t rows = ((uint64_t)grid + (uint64_t)num_seqs * num_kv_heads * tl) * 16;
+  return kCounterBytes + (size_t)(rows * 8 + rows * head_size * 4);
+}
+
 pa_status pa_decode_multi_balanced(
     void* out, const void* query, const void* key_cache, const void* value_cache,
     const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -582,19 +606,21 @@ pa_status pa_decode_multi_balanced(
                               num_heads, num_kv_heads, head_size, block_size,
                               num_blocks, scale);
   if (st != PA_OK) return st;
-  if (num_q_tokens < 0 || max_q_per_seq <= 0 || grid <= 0 || grid > (1 << 20) ||
-      !counters_fit(num_seqs, num_kv_heads))
+  if (num_q_tokens < 0 || max_q_per_seq <= 0 || max_q_per_seq > 65535 ||
+      grid <= 0 || grid > (1 << 20))
     return PA_ERR_SHAPE;
   const int32_t g = num_heads / num_kv_heads;
-  if ((int64_t)max_q_per_seq * g > 16) return PA_ERR_UNSUPPORTED;
+  const int64_t tl = multi_tiles(head_size, g, max_q_per_seq);
+  if ((uint64_t)num_seqs * num_kv_heads * tl > kCounterSlots) return PA_ERR_SHAPE;
   if (num_seqs == 0 || num_q_tokens == 0) return PA_OK;
   if (!out || !cu_seqlens_q || !workspace) return PA_ERR_NULL;
   if (!aligned(out, 16) || !aligned(workspace, 16) || !aligned(cu_seqlens_q, 4))
     return PA_ERR_ALIGN;
   if (workspace_bytes <
-      pa_multi_balanced_workspace_size(num_seqs, num_kv_heads, head_size, grid))
+      pa_multi_balanced_workspace_size_tiles(num_seqs, num_heads, num_kv_heads,
+                                             head_size, grid, max_q_per_seq))
     return PA_ERR_WORKSPACE;
-  const size_t rows = balanced_rows(num_seqs, num_kv_heads, grid, 16);
+  const size_t rows = ((size_t)grid + (size_t)num_seqs * num_kv_heads * tl) * 16;
   char* ws = static_cast<char*>(workspace);
   float* fmax = reinterpret_cast<float*>(ws + kCounterBytes);
   pa::DecodeArgs a = {};
@@ -617,6 +643,7 @@ pa_status pa_decode_multi_balanced(
   a.scale = scale;
   a.cu_seqlens_q = cu_seqlens_q;
   a.num_q_tokens = num_q_tokens;
+  a.q_tiles = (int)tl;
   st = checked_tables(block_tables, max_blocks_per_seq, context_lens, num_seqs,
                       num_blocks, block_size, false, stream);
   if (st != PA_OK) return st;

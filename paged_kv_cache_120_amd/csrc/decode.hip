@@ -1233,16 +1233,20 @@ struct DecodeCols {
   using Path = P;
   static constexpr int NC = G;
   static constexpr int kMinWaves = P::kMinWaves;
+  // one column tile (the g heads) per (sequence, kv head)
+  __device__ static int tiles(const DecodeArgs&, int) { return 1; }
+  __device__ static int max_tiles(const DecodeArgs&) { return 1; }
   template <class Sink>
   __device__ static void run(const DecodeArgs& a, typename P::Smem& sm, int kvh,
-                             int s, int n, int ta, int tv, int last, Sink& sink) {
+                             int s, int, int n, int ta, int tv, int last,
+                             Sink& sink) {
     P::run(a, sm, kvh, s, ta, tv, last, sink);
   }
   // output rows of a pair: computed once per range, then per column
   struct Out {
     int64_t base;
   };
-  __device__ static Out out_of(const DecodeArgs& a, int s, int kvh) {
+  __device__ static Out out_of(const DecodeArgs& a, int s, int kvh, int) {
     return {((int64_t)s * a.num_heads + (int64_t)kvh * G) * D};
   }
   __device__ static int64_t out_elem(const DecodeArgs&, const Out& o, int c) {
@@ -1261,32 +1265,47 @@ struct MultiCols {
   using Path = P;
   static constexpr int NC = NCOLS;
   static constexpr int kMinWaves = P::kColsMinWaves;
-  // query row of column c (c / G-th of the sequence's rows), -1 if none
-  __device__ static int64_t row_of(const DecodeArgs& a, int s, int c) {
+  static constexpr int RT = NCOLS / G;         // query rows per column tile
+  __device__ static int max_tiles(const DecodeArgs& a) {
+    return a.q_tiles > 1 ? a.q_tiles : 1;
+  }
+  // column tiles of sequence s: its T rows, RT per tile (none without rows)
+  // (at most max_tiles: rows past max_q_per_seq break a precondition and are
+  // left alone rather than given another pair's counter)
+  __device__ static int tiles(const DecodeArgs& a, int s) {
+    const int T = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
+    const int t = T > 0 ? (T + RT - 1) / RT : 0;
+    return t < max_tiles(a) ? t : max_tiles(a);
+  }
+  // query row of column c of tile t (row t*RT + c/G of the sequence's
+  // rows), -1 if none
+  __device__ static int64_t row_of(const DecodeArgs& a, int s, int c, int t) {
     const int q0 = a.cu_seqlens_q[s];
     const int T = a.cu_seqlens_q[s + 1] - q0;
-    const int qj = c / G;
+    const int qj = t * RT + c / G;
     if (q0 < 0 || qj >= T || q0 + qj >= a.num_q_tokens) return -1;
     return (int64_t)q0 + qj;
   }
   template <class Sink>
   __device__ static void run(const DecodeArgs& a, typename Path::Smem& sm, int kvh,
-                             int s, int n, int ta, int tv, int, Sink& sink) {
+                             int s, int t, int n, int ta, int tv, int, Sink& sink) {
     const int col = (threadIdx.x & 15) % NC;
-    const int64_t r = row_of(a, s, col);
+    const int64_t r = row_of(a, s, col, t);
     const int T = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
-    const int pos = n - T + col / G;           // this row's position
+    const int pos = n - T + t * RT + col / G;  // this row's position
     const bool ok = r >= 0 && pos >= 0;
     const int64_t qoff =
         ok ? (r * a.num_heads + (int64_t)kvh * G + col % G) * D : -1;
     Path::run_cols(a, sm, kvh, s, ta, tv, sink, qoff, ok ? pos : -1);
   }
   struct Out {
-    int s, kvh;
+    int s, kvh, t;
   };
-  __device__ static Out out_of(const DecodeArgs&, int s, int kvh) { return {s, kvh}; }
+  __device__ static Out out_of(const DecodeArgs&, int s, int kvh, int t) {
+    return {s, kvh, t};
+  }
   __device__ static int64_t out_elem(const DecodeArgs& a, const Out& o, int c) {
-    const int64_t r = row_of(a, o.s, c);
+    const int64_t r = row_of(a, o.s, c, o.t);
     return r < 0 ? -1 : (r * a.num_heads + (int64_t)o.kvh * G + c % G) * D;
   }
   // a row placed before the first key (T > n) has none: zeros
@@ -1326,7 +1345,7 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
   for (int s0 = 0; s0 < S; s0 += kThreads) {
     const int si = s0 + (int)threadIdx.x;
     const int ns = si < S ? a.context_lens[si] : 1;
-    const int64_t len = si < S ? span_len(ns, max_tok) : 0;
+    const int64_t len = si < S ? span_len(ns, max_tok) * Cols::tiles(a, si) : 0;
     if (w == 0 && ns <= 0) {
       if (a.slot_out) a.slot_out[si] = -1;
       Cols::clear_rows(a, si);
@@ -1356,7 +1375,9 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
     int64_t run = 0;
     for (int s0 = 0; s0 < S; s0 += kThreads) {
       const int si = s0 + (int)threadIdx.x;
-      const int64_t len = si < S ? span_len(a.context_lens[si], max_tok) * Hkv : 0;
+      const int64_t len =
+          si < S ? span_len(a.context_lens[si], max_tok) * Cols::tiles(a, si) * Hkv
+                 : 0;
       int64_t chunk = 0;
       const int64_t inc = block_scan(len, wave_sum, chunk);
       if (len > 0 && run + inc - len <= start && start < run + inc) {
@@ -1372,18 +1393,23 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
   int64_t E = found_start;               // flat start of sequence s
   if (s < 0) return;                     // unreachable while start < total
 
+  const int TL = Cols::max_tiles(a);
   int64_t pos = start;
   while (pos < end && s < S) {
     int n = a.context_lens[s];
     n = n < max_tok ? n : max_tok;
     const int64_t np = span_len(n, max_tok);
-    if (np == 0) {
+    const int tl = Cols::tiles(a, s);
+    if (np == 0 || tl == 0) {
       ++s;
       continue;
     }
-    const int kvh = (int)((pos - E) / np);
-    const int64_t F = E + (int64_t)kvh * np + kPairCost;   // flat token 0
-    const int64_t pair_end = E + (int64_t)(kvh + 1) * np;
+    // the sequence's units: kv head-major, then column tile
+    const int64_t u = (pos - E) / np;
+    const int kvh = (int)(u / tl);
+    const int tile = (int)(u % tl);
+    const int64_t F = E + u * np + kPairCost;          // flat token 0
+    const int64_t pair_end = E + (u + 1) * np;
     const int64_t seg_end = end < pair_end ? end : pair_end;
     const int ta = (int)(pos > F ? pos - F : 0);
     const int tb = (int)(seg_end > F ? seg_end - F : 0);
@@ -1391,15 +1417,15 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
     if (ta < tv) {
       const int64_t w0 = F / C;
       const int64_t wl = (F + n - 1) / C;             // slice of the last token
-      const int64_t q = (int64_t)s * Hkv + kvh;
+      const int64_t q = ((int64_t)s * Hkv + kvh) * TL + tile;
       const int last = (a.new_key && tv == n) ? n - 1 : -1;
-      const typename Cols::Out orow = Cols::out_of(a, s, kvh);
+      const typename Cols::Out orow = Cols::out_of(a, s, kvh, tile);
       if (w0 == wl) {
         auto sink = [&](int gi, int d, float, float L, float O) {
           const int64_t oe = Cols::out_elem(a, orow, gi);
           if (oe >= 0) a.out[oe + d] = (_Float16)(Cols::finish(O, L));
         };
-        Cols::run(a, sm, kvh, s, n, ta, tv, last, sink);
+        Cols::run(a, sm, kvh, s, tile, n, ta, tv, last, sink);
       } else {
         const int64_t slot = (int64_t)w + q;
         auto sink = [&](int gi, int d, float mx, float L, float O) {
@@ -1410,7 +1436,7 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
           }
           publish(a.ws_out + pi * D + d, O);
         };
-        Cols::run(a, sm, kvh, s, n, ta, tv, last, sink);
+        Cols::run(a, sm, kvh, s, tile, n, ta, tv, last, sink);
         // every thread's state stores acknowledged, then count this range
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -1461,7 +1487,7 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
       }
     }
     pos = seg_end;
-    if (pos == E + (int64_t)Hkv * np) {
+    if (pos == E + (int64_t)Hkv * tl * np) {
       E = pos;
       ++s;
     }

@@ -26,7 +26,7 @@ from . import (pa_balanced_grid, pa_balanced_grid_fp8, pa_balanced_workspace_siz
                pa_cache_write, pa_cache_write_fp8, pa_copy_blocks, pa_decode,
                pa_decode_balanced, pa_decode_balanced_fp8, pa_decode_multi,
                pa_decode_step_fp8, pa_decode_multi_balanced, pa_multi_balanced_grid,
-               pa_multi_balanced_workspace_size,
+               pa_multi_balanced_workspace_size_tiles,
                pa_decode_reduce, pa_decode_shared_prefix, pa_decode_splitk,
                pa_decode_step, pa_multi_workspace_size, pa_prefix_workspace_size,
                pa_slot_mapping, pa_splitk_workspace_size)
@@ -114,14 +114,11 @@ def upload_multi(w, device: str = "cuda", pool: Optional[torch.Tensor] = None) -
     nbytes = pa_multi_workspace_size(Q, H, D, w.max_blocks_per_seq, w.block_size,
                                      w.partition_size)
     st.multi_workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
-    g = H // w.num_kv_heads
-    st.multi_grid = 0
-    if st.max_q * g <= 16:
-        with torch.cuda.device(dev):
-            st.multi_grid = pa_multi_balanced_grid(H, w.num_kv_heads, D, w.block_size,
-                                                   st.max_q)
-    nb = pa_multi_balanced_workspace_size(w.num_seqs, w.num_kv_heads, D,
-                                          max(st.multi_grid, 1))
+    with torch.cuda.device(dev):
+        st.multi_grid = pa_multi_balanced_grid(H, w.num_kv_heads, D, w.block_size,
+                                               st.max_q)
+    nb = pa_multi_balanced_workspace_size_tiles(w.num_seqs, H, w.num_kv_heads, D,
+                                                max(st.multi_grid, 1), st.max_q)
     st.multi_bal_workspace = torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev)
     return st
 
@@ -129,9 +126,12 @@ def upload_multi(w, device: str = "cuda", pool: Optional[torch.Tensor] = None) -
 def multi_step(step: DeviceStep, stream=None, balanced=None) -> None:
     """Attention of the step's query rows (their K/V already written):
     pa_decode_multi_balanced when every sequence's rows x heads fit one
-    16-column tile (or ``balanced`` says so), else pa_decode_multi."""
+    16-column tile (or ``balanced`` says so), else pa_decode_multi, which
+    measured faster once a pair needs several tiles (c3 layout, g = 4:
+    8 rows 145 vs 163 us, 64 rows 709 vs 1178 us)."""
     if balanced is None:
-        balanced = step.multi_grid > 0
+        g = step.query.shape[1] // step.key_cache.shape[2]
+        balanced = step.multi_grid > 0 and step.max_q * g <= 16
     if balanced:
         pa_decode_multi_balanced(step.out, step.query, step.key_cache, step.value_cache,
                                  step.block_tables, step.cu_seqlens_q, step.context_lens,

@@ -32,6 +32,7 @@ def test_header_declares_the_boundary():
                  "pa_cache_write_fp8", "pa_balanced_grid_fp8", "pa_decode_balanced_fp8",
                  "pa_decode_step_fp8", "pa_prefix_workspace_size",
                  "pa_multi_balanced_grid", "pa_multi_balanced_workspace_size",
+                 "pa_multi_balanced_workspace_size_tiles",
                  "pa_decode_multi_balanced",
                  "pa_decode_shared_prefix"]:
         assert name in syms
@@ -216,14 +217,20 @@ def test_multi_balanced_validation(pa):
     d = L.pa_decode_multi_balanced
     a = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 8]
     b = [FAKE, 2, 8, 2, 128, 16, 10, 0.1]
-    assert d(*a, 5, *b, 64, FAKE, need, None) == 3          # 5 rows x g=4 > 16
+    # 5 rows x g = 4 > 16: two column tiles per (sequence, kv head)
+    need5 = pa.pa_multi_balanced_workspace_size_tiles(2, 8, 2, 128, 64, 5)
+    assert need5 == HEADER + (64 + 4 * 2) * 16 * (2 + 128) * 4
+    assert pa.pa_multi_balanced_workspace_size_tiles(2, 8, 2, 128, 64, 4) == need
+    assert d(*a, 5, *b, 64, FAKE, need, None) == 5          # needs the tiled size
+    assert d(*a, 5, *b, 64, FAKE + 4, need5, None) == 4
+    assert pa.pa_multi_balanced_workspace_size_tiles(2, 8, 2, 128, 64, 0) == 0
+    assert pa.pa_multi_balanced_workspace_size_tiles(65535, 64, 8, 128, 64, 64) == 0
     assert d(*a, 4, *b, 0, FAKE, need, None) == 2           # grid
     assert d(*a, 4, *b, 64, FAKE, need - 1, None) == 5
     assert d(*a, 4, *b, 64, None, need, None) == 1
     assert d(FAKE, FAKE, FAKE, FAKE, FAKE, 8, None, 8, 4, *b, 64, FAKE, need, None) == 1
     assert d(*a, 4, FAKE, 0, *b[2:], 64, FAKE, need, None) == 0   # empty batch
     assert L.pa_multi_balanced_grid(8, 2, 96, 16, 4) == 0
-    assert L.pa_multi_balanced_grid(8, 2, 128, 16, 5) == 0                # 5 x 4 > 16
 
 
 def test_binding_rejects_host_tensors(pa):

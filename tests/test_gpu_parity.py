@@ -456,8 +456,7 @@ MULTI_SMALL = ["c1_prefill", "c2_small_spec4", "c3_small_spec4", "c3_small_chunk
 def run_multi(w, balanced=None):
     pa, runner = _gpu()
     st = runner.upload_multi(w)
-    if balanced and st.multi_grid <= 0:
-        pytest.skip("rows x heads of a sequence exceed one 16-column tile")
+    assert not balanced or st.multi_grid > 0
     runner.apply_history(w, st)
     runner.write_step(st)
     runner.multi_step(st, balanced=balanced)
@@ -529,17 +528,23 @@ def test_multi_and_prefix_repeat_calls_bitwise():
 
 
 @pytest.mark.parametrize("grid", [1, 5, 300])
-def test_multi_balanced_any_grid_and_empty_sequences(grid):
+@pytest.mark.parametrize("name", ["c3_small_spec4", "c3_small_chunk64"])
+def test_multi_balanced_any_grid_and_empty_sequences(name, grid):
     """The balanced multi-token kernel at grids other than the resident one,
-    with a sequence of context 0 (its rows are zeros) and one without rows."""
+    with a sequence of context 0 (its rows are zeros) and one without rows;
+    one column tile per (sequence, kv head) (4 rows x g = 4) and sixteen
+    (a 64-row chunk)."""
+    print(f"[multi-grid] {name} grid={grid}", flush=True)
     pa, runner = _gpu()
-    w = workloads.make("c3_small_spec4")
+    w = workloads.make(name)
     st = run_multi(w, True)
     cu = w.info["cu_seqlens_q"]
     ctx = w.context_lens.copy()
     ctx[2] = 0
     st.context_lens.copy_(torch.from_numpy(ctx))
-    nb = pa.pa_multi_balanced_workspace_size(w.num_seqs, w.num_kv_heads, w.head_size, grid)
+    nb = pa.pa_multi_balanced_workspace_size_tiles(w.num_seqs, w.query.shape[1],
+                                                   w.num_kv_heads, w.head_size, grid,
+                                                   st.max_q)
     ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     st.out.fill_(3.0)
     pa.pa_decode_multi_balanced(st.out, st.query, st.key_cache, st.value_cache,
