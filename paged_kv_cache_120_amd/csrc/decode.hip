@@ -1145,23 +1145,24 @@ __global__ __launch_bounds__(NT) void multi_reduce_kernel(ReduceArgs a) {
 // Balanced split
 // ---------------------------------------------------------------------------
 //
-// Flat work order: sequence-major, then kv head, then token; each pair
-// spans kPairCost units and then its length padded to a multiple of 16
+// Flat work order: sequence-major, then kv head, then column tile (one per
+// pair except for wide multi-token chunks), then token; each unit spans
+// kPairCost units and then its length padded to a multiple of 16
 // (span_len).  With T the flat total and C = ceil(T / grid) rounded up to
 // 16, workgroup w owns flat positions [w*C, (w+1)*C).  Pairs of one
 // sequence are adjacent, so neighbouring workgroups read neighbouring heads
 // of the same token rows.
 //
-// The part of pair q = seq*H_kv + kvh inside workgroup w is one range.  A
-// pair whose valid tokens [F, F+n) (F = the flat position of its token 0)
-// fall in a single
-// slice is finished in place.  Otherwise each of its k ranges stores its
-// state in slot w + q (distinct: along the flat order w and q never decrease
-// and one grows at every range boundary, so slots stay below grid + S*H_kv),
-// then counts itself in cnt[q].  The range that brings the count to k folds
-// the k states with the online-softmax recurrence, writes the output and
-// resets cnt[q] to zero for the next call.  Nothing waits on another
-// workgroup.
+// The part of unit q = (seq*H_kv + kvh)*TL + tile (TL = the most tiles of
+// any sequence, 1 for decode) inside workgroup w is one range.  A unit
+// whose valid tokens [F, F+n) (F = the flat position of its token 0) fall
+// in a single slice is finished in place.  Otherwise each of its k ranges
+// stores its state in slot w + q (distinct: along the flat order w and q
+// never decrease and one grows at every range boundary, so slots stay below
+// grid + S*H_kv*TL), then counts itself in cnt[q].  The range that brings
+// the count to k folds the k states with the online-softmax recurrence,
+// writes the output and resets cnt[q] to zero for the next call.  Nothing
+// waits on another workgroup.
 // Partial states cross XCDs (each has its own L2), so they are stored and
 // loaded with system-coherent accesses that bypass L2 (sc0 sc1) instead of
 // fencing whole caches; a writer waits for its stores to be acknowledged
@@ -1223,11 +1224,12 @@ __device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* wave_sum,
 }
 
 
-// What a (sequence, kv head) pair of the balanced split computes, and where
-// its NC columns go.  DecodeCols: one query row per sequence, the pair's g
-// heads.  MultiCols: the sequence's T query rows x g heads (T*g <= NC), each
-// row with its causal key limit, on the matrix-core body with NC = 4 or 8
-// columns (one score pass) or 16 (R score passes).
+// What a unit of the balanced split computes, and where its NC columns go.
+// A unit is one column tile of a (sequence, kv head) pair.  DecodeCols: one
+// tile, the sequence's query row x the pair's g heads.  MultiCols: the
+// sequence's T query rows x g heads in tiles of NC/g rows, each row with its
+// causal key limit, on the matrix-core body with NC = 4 or 8 columns (one
+// tile, one score pass) or 16 (R score passes; ceil(T*g/16) tiles).
 template <class P, int D, int G>
 struct DecodeCols {
   using Path = P;
