@@ -73,19 +73,29 @@ def split_kernel_bytes(w) -> int:
     return kv_bytes(w) + S * H * D * 2 + table + parts
 
 
-PAIR_COST = 64      # flat units the balanced split charges per (sequence, kv head)
+PAIR_COST = 64       # flat units the balanced split charges per (sequence, kv head)
+FULL_PAIR_COST = 160  # the same for the 16-column multi-token form
 
 
-def balanced_split_ranges(w, grid: int) -> int:
+def multi_full_form(w, max_q: int) -> bool:
+    """Whether the balanced multi-token kernel takes its 16-column form:
+    max_q * g query columns beyond what one narrow pass holds (4 at head
+    size 128 with g <= 4, else 8)."""
+    narrow = 4 if (w.head_size == 128 and w.group <= 4) else 8
+    return max_q * w.group > narrow
+
+
+def balanced_split_ranges(w, grid: int, pair_cost: int = PAIR_COST) -> int:
     """Ranges of the balanced decode that belong to (sequence, kv head)
     pairs cut across several workgroups: each stores one partial state per
     query head, which the pair's last workgroup reads back to merge.  Same
-    slicing as the kernel: a pair spans PAIR_COST units, then its length
-    padded to 16; equal 16-aligned slices of that space."""
+    slicing as the kernel: a pair spans pair_cost units, then its length
+    padded to 16; equal 16-aligned slices of that space (one column tile per
+    pair)."""
     M = w.max_blocks_per_seq * w.block_size
     n = np.minimum(w.context_lens.astype(np.int64), M)
     pad = np.where(n > 0, (n + 15) // 16 * 16, 0)
-    span = np.where(pad > 0, pad + PAIR_COST, 0)
+    span = np.where(pad > 0, pad + pair_cost, 0)
     Hkv = w.num_kv_heads
     total = int(span.sum()) * Hkv
     if total == 0:
@@ -98,7 +108,7 @@ def balanced_split_ranges(w, grid: int) -> int:
         if n[i] <= 0:
             continue
         for kvh in range(Hkv):
-            F = int(prefix[i]) * Hkv + kvh * int(span[i]) + PAIR_COST
+            F = int(prefix[i]) * Hkv + kvh * int(span[i]) + pair_cost
             k = (F + int(n[i]) - 1) // C - F // C + 1
             if k > 1:
                 count += k
@@ -523,7 +533,8 @@ def multi_bench(args, w, dev) -> int:
         table = int(((n + w.block_size - 1) // w.block_size).sum()) * 4
         cols = Q / w.num_seqs * w.group
         kb = int(kvb + 2 * Q * w.num_heads * w.head_size * 2 + table)
-        handoff = int(2 * balanced_split_ranges(w, steps[0].multi_grid) * cols
+        pc = FULL_PAIR_COST if multi_full_form(w, steps[0].max_q) else PAIR_COST
+        handoff = int(2 * balanced_split_ranges(w, steps[0].multi_grid, pc) * cols
                       * (w.head_size + 2) * 4)
         kname = "balanced_kernel (multi-token rows)"
     else:

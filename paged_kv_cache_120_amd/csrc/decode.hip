@@ -1147,8 +1147,8 @@ __global__ __launch_bounds__(NT) void multi_reduce_kernel(ReduceArgs a) {
 //
 // Flat work order: sequence-major, then kv head, then column tile (one per
 // pair except for wide multi-token chunks), then token; each unit spans
-// kPairCost units and then its length padded to a multiple of 16
-// (span_len).  With T the flat total and C = ceil(T / grid) rounded up to
+// a fixed pair cost (kPairCost, kFullPairCost for the 16-column multi-token
+// form) and then its length padded to a multiple of 16 (span_len).  With T the flat total and C = ceil(T / grid) rounded up to
 // 16, workgroup w owns flat positions [w*C, (w+1)*C).  Pairs of one
 // sequence are adjacent, so neighbouring workgroups read neighbouring heads
 // of the same token rows.
@@ -1187,11 +1187,16 @@ __device__ __forceinline__ int64_t padded_len(int n, int max_tok) {
 // cost of the range that starts it (table and query loads, the final merge),
 // then its padded tokens; equal slices of this space then hold fewer tokens
 // where they start more pairs.  Measured on MI355X: 64 (a multiple of 16)
-// lifts the GQA-4 workload by 4-6% and leaves the others unchanged.
+// lifts the GQA-4 workload by 4-6% and leaves the others unchanged.  The
+// 16-column multi-token form starts a pair at a higher cost (R query passes,
+// a 16-column LDS accumulator, 16 rows to merge and store): 160 there takes
+// 10% off the 4-token GQA-4 verify step (128: 4%, 192: 7%).
 constexpr int kPairCost = 64;
+constexpr int kFullPairCost = 160;
+template <int PC>
 __device__ __forceinline__ int64_t span_len(int n, int max_tok) {
   const int64_t np = padded_len(n, max_tok);
-  return np > 0 ? np + kPairCost : 0;
+  return np > 0 ? np + PC : 0;
 }
 
 __device__ __forceinline__ int64_t balanced_chunk(int64_t total, int grid) {
@@ -1235,6 +1240,7 @@ struct DecodeCols {
   using Path = P;
   static constexpr int NC = G;
   static constexpr int kMinWaves = P::kMinWaves;
+  static constexpr int kPC = kPairCost;        // flat units charged per pair
   // one column tile (the g heads) per (sequence, kv head)
   __device__ static int tiles(const DecodeArgs&, int) { return 1; }
   __device__ static int max_tiles(const DecodeArgs&) { return 1; }
@@ -1267,6 +1273,7 @@ struct MultiCols {
   using Path = P;
   static constexpr int NC = NCOLS;
   static constexpr int kMinWaves = P::kColsMinWaves;
+  static constexpr int kPC = NCOLS == 16 ? kFullPairCost : kPairCost;
   static constexpr int RT = NCOLS / G;         // query rows per column tile
   __device__ static int max_tiles(const DecodeArgs& a) {
     return a.q_tiles > 1 ? a.q_tiles : 1;
@@ -1347,7 +1354,7 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
   for (int s0 = 0; s0 < S; s0 += kThreads) {
     const int si = s0 + (int)threadIdx.x;
     const int ns = si < S ? a.context_lens[si] : 1;
-    const int64_t len = si < S ? span_len(ns, max_tok) * Cols::tiles(a, si) : 0;
+    const int64_t len = si < S ? span_len<Cols::kPC>(ns, max_tok) * Cols::tiles(a, si) : 0;
     if (w == 0 && ns <= 0) {
       if (a.slot_out) a.slot_out[si] = -1;
       Cols::clear_rows(a, si);
@@ -1378,7 +1385,7 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
     for (int s0 = 0; s0 < S; s0 += kThreads) {
       const int si = s0 + (int)threadIdx.x;
       const int64_t len =
-          si < S ? span_len(a.context_lens[si], max_tok) * Cols::tiles(a, si) * Hkv
+          si < S ? span_len<Cols::kPC>(a.context_lens[si], max_tok) * Cols::tiles(a, si) * Hkv
                  : 0;
       int64_t chunk = 0;
       const int64_t inc = block_scan(len, wave_sum, chunk);
@@ -1400,7 +1407,7 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
   while (pos < end && s < S) {
     int n = a.context_lens[s];
     n = n < max_tok ? n : max_tok;
-    const int64_t np = span_len(n, max_tok);
+    const int64_t np = span_len<Cols::kPC>(n, max_tok);
     const int tl = Cols::tiles(a, s);
     if (np == 0 || tl == 0) {
       ++s;
@@ -1410,7 +1417,7 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
     const int64_t u = (pos - E) / np;
     const int kvh = (int)(u / tl);
     const int tile = (int)(u % tl);
-    const int64_t F = E + u * np + kPairCost;          // flat token 0
+    const int64_t F = E + u * np + Cols::kPC;          // flat token 0
     const int64_t pair_end = E + (u + 1) * np;
     const int64_t seg_end = end < pair_end ? end : pair_end;
     const int ta = (int)(pos > F ? pos - F : 0);

@@ -65,9 +65,9 @@ def test_split_ranges_brute_force():
         w.max_blocks_per_seq = 64
         w.context_lens = rng.integers(0, 1025, size=w.num_seqs).astype(np.int32)
         grid = int(rng.integers(1, 40))
-        got = bench.balanced_split_ranges(w, grid)
+        pc = (bench.PAIR_COST, bench.FULL_PAIR_COST)[trial % 2]
+        got = bench.balanced_split_ranges(w, grid, pc)
         # brute force: owner workgroup of every token of every pair
-        pc = bench.PAIR_COST
         spans = [((n + 15) // 16 * 16 + pc) if n > 0 else 0 for n in w.context_lens]
         total = sum(spans) * w.num_kv_heads
         if total == 0:
