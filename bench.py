@@ -402,6 +402,53 @@ def stream_probe(dev, launches: int = 20) -> dict:
             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def stream_probe_sized(dev, nbytes: int, launches: int = 20) -> dict:
+    """Read rate of one plain sequential pass over nbytes (rounded up to 16),
+    the byte count of one decode launch: the same launch start, ramp and
+    tail at that size, with no paging, softmax or handoff.  Successive
+    launches read up to 4 disjoint regions in turn (as many as fit in 4 GiB)
+    so the 256 MB MALL cannot serve a repeat; best of 1, 2, 4 and 8
+    workgroups per CU, timed with events on the current stream."""
+    import torch
+    import paged_kv_cache_120_amd as pa
+    n = (int(nbytes) + 15) // 16 * 16
+    k = max(1, min(4, PROBE_BYTES // n))
+    buf = torch.zeros(k * n, dtype=torch.uint8, device=dev)
+    regions = [buf[i * n:(i + 1) * n] for i in range(k)]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(4 * 8 * cus, dtype=torch.int32, device=dev)
+    best = None
+    for grid in (cus, 2 * cus, 4 * cus, 8 * cus):
+        for i in range(3):
+            pa.pa_stream_read(regions[i % k], sink, grid)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(launches):
+            pa.pa_stream_read(regions[i % k], sink, grid)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        if best is None or ms < best[1]:
+            best = (grid, ms)
+    del regions, buf, sink
+    torch.cuda.empty_cache()
+    grid, ms = best
+    gbs = n / (ms * 1e-3) / 1e9
+    return {"bytes": n, "regions": k, "grid": grid, "us": round(ms * 1e3, 2),
+            "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def add_same_size_read(rec: dict, dev) -> None:
+    """Put a plain read of the dominant kernel's algorithmic bytes beside
+    its roofline: the ceiling a kernel moving that many bytes reaches here."""
+    rf = rec["roofline"]
+    sp = stream_probe_sized(dev, rf["algorithmic_bytes"])
+    rf["same_size_read"] = sp
+    rf["frac_of_same_size_read"] = round(rf["achieved"] / sp["gbs"], 4)
+
+
 HOST_LINK_PEAK_GBS = 64.0     # PCIe 5.0 x16, one direction (nominal)
 
 
@@ -968,10 +1015,12 @@ def long_context_record(name: str, args, dev) -> dict:
     grid = steps[0].grid
     del steps
     torch.cuda.empty_cache()
+    fused = decode_record(w, "fused", grid, fu["ms_step"], fu["kms"])
+    add_same_size_read(fused, dev)
     return {"workload": WORKLOADS[name], "num_seqs": w.num_seqs,
             "total_context_tokens": int(w.context_lens.sum()), "steps": n,
             "splitk_512": decode_record(w, "splitk", grid, sk["ms_step"], sk["kms"]),
-            "fused": decode_record(w, "fused", grid, fu["ms_step"], fu["kms"])}
+            "fused": fused}
 
 
 def main(argv=None) -> int:
@@ -1102,6 +1151,7 @@ def main(argv=None) -> int:
     probe = stream_probe(dev)
     main_rec["roofline"]["frac_of_stream_probe"] = round(
         main_rec["roofline"]["achieved"] / probe["gbs"], 4)
+    add_same_size_read(main_rec, dev)
 
     rec = {
         "metric": METRIC,
@@ -1156,6 +1206,7 @@ def main(argv=None) -> int:
             r3["roofline"]["traffic"] = t3["bytes"]
             r3["roofline"]["traffic_source"] = t3["source"]
         r3["roofline"]["frac_of_stream_probe"] = round(r3["roofline"]["achieved"] / probe["gbs"], 4)
+        add_same_size_read(r3, dev)
         c3c = load_counters("c3", "fused", ROOT)
         gq = {"workload": WORKLOADS["c3"], "num_seqs": w3.num_seqs,
               "num_heads": w3.num_heads, "num_kv_heads": w3.num_kv_heads,
