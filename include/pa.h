@@ -314,6 +314,52 @@ pa_status pa_decode_balanced(void* out, const void* query,
                              hipStream_t stream);
 
 /*
+ * Multi-token queries over the same block tables (speculative verify,
+ * chunked prefill): [BOOK] §4.5 (2) has the attention backend take the
+ * query tokens of every request delimited by cu_seqlens_q together with the
+ * per-request key counts and the block table; §4.5 (1) writes the new
+ * tokens' K/V into the cache first.  Sequence i owns query rows
+ * cu_seqlens_q[i] .. cu_seqlens_q[i+1]-1, the last T_i of its
+ * context_lens[i] = n_i tokens (already in the cache); row cu_seqlens_q[i]
+ * + j sits at position p = n_i - T_i + j and attends to keys 0 .. p only
+ * (causal).  Tolerance as pa_decode.
+ *   query, out     fp16 [num_q_tokens, num_heads, head_size], 16-byte
+ *                  aligned; out is written for every row of a sequence
+ *                  with T_i > 0 (zeros where context_lens[i] <= 0 or the
+ *                  row has no key, T_i > n_i)
+ *   cu_seqlens_q   int32 [num_seqs + 1], device, non-decreasing, from 0 to
+ *                  num_q_tokens (precondition, not checked)
+ *   max_q_per_seq  >= every T_i (host value sizing the launch; rows past
+ *                  it are not computed)
+ *   partition_size keys per partition, a multiple of block_size; the rows
+ *                  of a sequence are computed per partition of its keys in
+ *                  one kernel (up to 16 rows x heads, or 4-8 on the narrow
+ *                  matrix-core form, share one pass over a partition's
+ *                  keys) and a second kernel folds the partitions with the
+ *                  [BOOK] §4.6 recurrence
+ *   workspace      device, 16-byte aligned, >= pa_multi_workspace_size
+ *                  bytes: fp32 max and sum [num_q_tokens, num_heads,
+ *                  Pmax] and out [.., head_size] (Pmax as for
+ *                  pa_decode_splitk); no zero-fill needed
+ * Other arguments, preconditions and errors as pa_decode; additionally
+ * PA_ERR_SHAPE when num_q_tokens, num_seqs x tiles or Pmax exceeds 65535.
+ * num_q_tokens == 0 or num_seqs == 0 enqueues nothing.
+ */
+size_t pa_multi_workspace_size(int32_t num_q_tokens, int32_t num_heads,
+                               int32_t head_size, int32_t max_blocks_per_seq,
+                               int32_t block_size, int32_t partition_size);
+pa_status pa_decode_multi(void* out, const void* query, const void* key_cache,
+                          const void* value_cache, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq,
+                          const int32_t* cu_seqlens_q, int32_t num_q_tokens,
+                          int32_t max_q_per_seq, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_heads,
+                          int32_t num_kv_heads, int32_t head_size,
+                          int32_t block_size, int32_t num_blocks, float scale,
+                          int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Multi-token queries on the balanced split: pa_decode_multi's result
  * (same rows, causal limits and tolerance) in ONE kernel, with the work of
  * every (sequence, kv head) pair cut into equal slices as for

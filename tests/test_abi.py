@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
                  "pa_decode_step_fp8", "pa_prefix_workspace_size",
                  "pa_multi_balanced_grid", "pa_multi_balanced_workspace_size",
                  "pa_multi_balanced_workspace_size_tiles",
-                 "pa_decode_multi_balanced",
+                 "pa_decode_multi_balanced", "pa_decode_multi",
+                 "pa_multi_workspace_size",
                  "pa_decode_shared_prefix"]:
         assert name in syms
 
@@ -45,6 +46,17 @@ def test_library_exports_every_declared_symbol(pa):
     lib = ctypes.CDLL(pa.library_path)
     for name in header_symbols():
         ctypes.cast(getattr(lib, name), ctypes.c_void_p)
+
+
+def test_every_exported_entry_point_is_declared(pa):
+    """The library's dynamic symbols named pa_* are exactly the header's."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.library_path],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines()
+                if line.split() and line.split()[-1].startswith("pa_")}
+    assert exported == set(header_symbols()), (
+        sorted(exported - set(header_symbols())), sorted(set(header_symbols()) - exported))
 
 
 def test_binding_names_match_the_abi(pa):
