@@ -245,6 +245,24 @@ def test_multi_balanced_validation(pa):
     assert L.pa_multi_balanced_grid(8, 2, 96, 16, 4) == 0
 
 
+def test_multi_validation(pa):
+    """pa_decode_multi checks its host arguments before any launch."""
+    L = pa.lib
+    need = pa.pa_multi_workspace_size(8, 8, 128, 8, 16, 64)
+    assert need == pa.pa_splitk_workspace_size(8, 8, 128, 8, 16, 64) > 0
+    d = L.pa_decode_multi
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE]
+    b = [FAKE, 2, 8, 2, 128, 16, 10, 0.1]
+    assert d(*a, 8, 4, *b, 64, FAKE, need - 1, None) == 5       # PA_ERR_WORKSPACE
+    assert d(*a, 8, 4, *b, 64, None, need, None) == 1           # PA_ERR_NULL
+    assert d(FAKE, FAKE, FAKE, FAKE, FAKE, 8, None, 8, 4, *b, 64, FAKE, need, None) == 1
+    assert d(*a, 8, 4, *b, 64, FAKE + 4, need, None) == 4       # PA_ERR_ALIGN
+    assert d(*a, 8, 4, *b, 24, FAKE, need, None) == 2           # partition % block
+    assert d(*a, 8, 0, *b, 64, FAKE, need, None) == 2           # max_q_per_seq
+    assert d(*a, 65536, 4, *b, 64, FAKE, 1 << 40, None) == 2    # grid limit
+    assert d(*a, 0, 4, *b, 64, FAKE, need, None) == 0           # nothing to do
+
+
 def test_binding_rejects_host_tensors(pa):
     import torch
     x = torch.zeros((2, 8, 128), dtype=torch.float16)
