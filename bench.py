@@ -53,7 +53,10 @@ WORKLOADS = {
                 "ctx U[4,2048], 40/40 heads, D128, B16",
     "c3_spec4": "speculative verify, 4 query tokens per seq: GQA 32/8 heads, 64 seqs ctx "
                 "lognormal(700,1) in [4,8192], D128, B16",
+    "c3_chunk512": "chunked prefill, the last 512 tokens of each seq as the chunk: GQA 32/8 "
+                   "heads, 16 seqs ctx U[512,4096], D128, B16",
 }
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix throughput
 
 
 def kv_bytes(w) -> int:
@@ -531,6 +534,120 @@ def multi_kernel_bytes(w) -> int:
         pos = int(n[i]) - T + np.arange(T)
         parts += int((pos // P + 1).sum())
     return kv_bytes(w) + 2 * Q * H * D * 2 + table + 2 * parts * H * (D + 2) * 4
+
+
+def prefill_flops(w) -> float:
+    """Matrix flops of causal attention over the chunk rows: 2*D for the
+    score and 2*D for the weighted value of every (row, head, visible key);
+    row j of a T-row chunk over n keys sees n - T + j + 1 of them."""
+    cu = w.info["cu_seqlens_q"]
+    T = np.diff(cu).astype(np.int64)
+    n = w.context_lens.astype(np.int64)
+    vis = np.where(T > 0, (n - T) * T + T * (T + 1) // 2, 0)
+    return 4.0 * w.head_size * w.num_heads * float(vis.sum())
+
+
+def prefill_bench(args, w, dev) -> int:
+    """Chunked prefill steps: slot mapping + cache write of every sequence's
+    chunk, then pa_prefill (128 rows x heads per pass over the keys); the
+    pa_decode_multi step over the same rows is timed beside it."""
+    import torch
+    import paged_kv_cache_120_amd as pa
+    from paged_kv_cache_120_amd import runner
+    base = runner.upload_multi(w, dev)
+    runner.apply_history(w, base)
+    steps = [base] + [runner.upload_multi(w, dev, pool=base.pool.clone())
+                      for _ in range(1, max(1, args.rotate))]
+    torch.cuda.synchronize()
+    R = len(steps)
+
+    def attend(st):
+        pa.pa_prefill(st.out, st.query, st.key_cache, st.value_cache, st.block_tables,
+                      st.cu_seqlens_q, st.context_lens, st.max_q, st.scale)
+
+    def timed(fn, steps_n):
+        for i in range(args.warmup):
+            fn(steps[i % R])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps_n):
+            fn(steps[i % R])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps_n
+
+    ms_step = timed(lambda st: (runner.write_step(st), attend(st)), args.steps)
+    kms = timed(attend, args.steps)
+    ms_multi = timed(lambda st: (runner.write_step(st), runner.multi_step(st, balanced=False)),
+                     max(5, args.steps // 10))
+    last = steps[(args.steps - 1) % R]
+    runner.write_step(last)
+    attend(last)
+    torch.cuda.synchronize()
+    Q = int(w.query.shape[0])
+    fl = prefill_flops(w)
+    achieved = fl / (kms * 1e-3) / 1e12
+    rec = {
+        "metric": "paged chunked prefill TFLOP/s + query tokens/s",
+        "value": round(fl / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "name": args.config,
+                   "num_seqs": w.num_seqs, "query_tokens": Q, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_size": w.head_size,
+                   "block_size": w.block_size,
+                   "total_context_tokens": int(w.context_lens.sum()),
+                   "rotated_pool_copies": R, "seed": w.seed},
+        "accumulate": "f32", "flops_per_step": fl,
+        "query_tokens_per_s": round(Q / (ms_step * 1e-3), 1),
+        "decode_multi_step_ms": round(ms_multi, 5),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel", "kernel_ms": round(kms, 5),
+                     "algorithmic_flops": fl, "kv_bytes": kv_bytes(w)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        gpu = last.out.cpu().numpy().astype(np.float64)
+        kc, vc = w.pool_init[0].copy(), w.pool_init[1].copy()
+        oracle.apply_phases(kc, vc, list(w.history) + [w.step_write], w.block_size)
+        cu = w.info["cu_seqlens_q"]
+        try:
+            from threadpoolctl import threadpool_limits
+            ctx = threadpool_limits(1)
+        except Exception:                               # pragma: no cover
+            ctx = None
+        # a bounded sample: the first 32 rows of each sequence's chunk, as
+        # many sequences as about 10 s allow
+        t0 = time.perf_counter()
+        done, rows, ok_all = 0, 0, True
+        while time.perf_counter() - t0 < 10.0 and done < w.num_seqs:
+            i = done
+            T = int(cu[i + 1] - cu[i])
+            k = min(T, 32)
+            # rows 0..k-1 of a T-row chunk over n keys: as the first k rows
+            # of a k-row chunk over n - T + k keys
+            o = oracle.decode_multi(w.query[cu[i]:cu[i] + k], kc, vc, w.block_tables[i:i + 1],
+                                    np.array([0, k], np.int32),
+                                    np.array([w.context_lens[i] - T + k], np.int32), w.scale)
+            err = np.abs(gpu[cu[i]:cu[i] + k] - o)
+            ok_all &= bool(((err <= 2e-3) | (err <= 1e-2 * np.abs(o))).all())
+            rows += k
+            done += 1
+        el = time.perf_counter() - t0
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+        rec["parity"] = {"rows_checked": rows, "within_tolerance": ok_all}
+        rec["cpu_baseline"] = {"value": round(rows / el, 3), "unit": "query tokens/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"the first {min(32, int(np.diff(cu).max()))} rows of "
+                                         f"{done} sequences' chunks ({rows} rows x "
+                                         f"{w.num_heads} heads), float64 NumPy, 1 BLAS thread"}
+    print(json.dumps(rec), flush=True)
+    return 0
 
 
 def multi_bench(args, w, dev) -> int:
@@ -1031,7 +1148,7 @@ def main(argv=None) -> int:
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="fused",
                     choices=["fused", "balanced", "splitk", "single", "swap", "multi",
-                             "fp8", "prefix"],
+                             "fp8", "prefix", "prefill"],
                     help="fused: pa_decode_step (append + balanced decode, one kernel); "
                          "balanced/splitk/single: slot mapping + cache write + that decode; "
                          "swap: pa_swap_blocks of the batch's blocks to pinned host memory "
@@ -1091,6 +1208,12 @@ def main(argv=None) -> int:
         return fp8_bench(args, w, dev)
     if args.mode == "prefix":
         return prefix_bench(args, w, dev)
+    if args.mode == "prefill":
+        if "cu_seqlens_q" not in w.info:
+            print("--mode prefill goes with a multi-token config (c3_chunk512)",
+                  file=sys.stderr)
+            return 2
+        return prefill_bench(args, w, dev)
     if args.mode == "multi" or "cu_seqlens_q" in w.info:
         if args.mode != "multi" or "cu_seqlens_q" not in w.info:
             print("--mode multi goes with a multi-token config (c2_spec4, c3_spec4)",

@@ -360,6 +360,30 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache,
                           size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Chunked prefill: pa_decode_multi's result (same rows, causal limits,
+ * zeros and tolerance; no workspace) for chunks of many query rows per
+ * sequence.  Each workgroup takes 128 of a sequence's rows x heads of one
+ * kv head and walks the keys they see once, in tiles of 32 staged through
+ * LDS, with the scores and the weighted sum of values on the matrix cores;
+ * a key is read from memory once per 128 rows x heads instead of once per
+ * 16 (pa_decode_multi's column tile).  Launch: num_kv_heads x
+ * ceil(max_q_per_seq * g / 128) x num_seqs workgroups; workgroups past a
+ * sequence's own rows exit at once.  Arguments, preconditions and errors
+ * as pa_decode_multi without partition_size and the workspace;
+ * PA_ERR_SHAPE when ceil(max_q_per_seq * g / 128) exceeds 65535.  Row j of
+ * a T-row chunk sees keys 0 .. n - T + j; the rows need not be more than
+ * one ([BOOK] §4.5 (1)-(2); the running-max recurrence of §4.6 per row).
+ */
+pa_status pa_prefill(void* out, const void* query, const void* key_cache,
+                     const void* value_cache, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                     int32_t num_q_tokens, int32_t max_q_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs,
+                     int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                     int32_t block_size, int32_t num_blocks, float scale,
+                     hipStream_t stream);
+
+/*
  * Multi-token queries on the balanced split: pa_decode_multi's result
  * (same rows, causal limits and tolerance) in ONE kernel, with the work of
  * every (sequence, kv head) pair cut into equal slices as for

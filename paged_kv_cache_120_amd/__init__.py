@@ -19,7 +19,7 @@ __all__ = [
     "pa_slot_mapping", "pa_cache_write", "pa_copy_blocks", "pa_swap_blocks", "pa_decode",
     "pa_splitk_workspace_size", "pa_decode_splitk", "pa_decode_reduce",
     "pa_balanced_grid", "pa_balanced_workspace_size", "pa_decode_balanced",
-    "pa_decode_step", "pa_multi_workspace_size", "pa_decode_multi",
+    "pa_decode_step", "pa_multi_workspace_size", "pa_decode_multi", "pa_prefill",
     "pa_cache_write_fp8", "pa_balanced_grid_fp8", "pa_decode_balanced_fp8",
     "pa_decode_step_fp8", "pa_multi_balanced_grid", "pa_multi_balanced_workspace_size",
     "pa_multi_balanced_workspace_size_tiles",
@@ -71,6 +71,8 @@ def _load() -> ctypes.CDLL:
         "pa_multi_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
         "pa_decode_multi": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, i32,
                                            i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]),
+        "pa_prefill": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, i32,
+                                      i32, i32, i32, i32, i32, f32, vp]),
         "pa_balanced_grid": (i32, [i32, i32, i32, i32]),
         "pa_balanced_workspace_size": (sz, [i32, i32, i32, i32, i32]),
         "pa_decode_balanced": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
@@ -434,6 +436,29 @@ def pa_decode_multi(out, query, key_cache, value_cache, block_tables, cu_seqlens
         _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q", 1), Q, int(max_q_per_seq),
         _dev(context_lens, torch.int32, "context_lens", 1), S, H, Hkv, D, B, nb,
         float(scale), int(partition_size), ws, nbytes, _stream(stream)))
+
+
+def pa_prefill(out, query, key_cache, value_cache, block_tables, cu_seqlens_q,
+               context_lens, max_q_per_seq: int, scale: float, stream=None) -> None:
+    """pa_decode_multi's rows (causal within each sequence's chunk) for long
+    chunks: 128 rows x heads per pass over the keys, no workspace."""
+    torch = _torch()
+    Q, H, D = query.shape
+    nb, B, Hkv, D2 = key_cache.shape
+    S = context_lens.shape[0]
+    if D2 != D or tuple(value_cache.shape) != (nb, B, Hkv, D) or \
+            tuple(out.shape) != (Q, H, D):
+        raise ValueError("pa_prefill: inconsistent shapes")
+    if block_tables.shape[0] != S or cu_seqlens_q.shape != (S + 1,):
+        raise ValueError("pa_prefill: block_tables / cu_seqlens_q do not match")
+    _check("pa_prefill", _lib().pa_prefill(
+        _dev(out, torch.float16, "out", 3), _dev(query, torch.float16, "query", 3),
+        _dev(key_cache, torch.float16, "key_cache", 4),
+        _dev(value_cache, torch.float16, "value_cache", 4),
+        _dev(block_tables, torch.int32, "block_tables", 2), block_tables.shape[1],
+        _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q", 1), Q, int(max_q_per_seq),
+        _dev(context_lens, torch.int32, "context_lens", 1), S, H, Hkv, D, B, nb,
+        float(scale), _stream(stream)))
 
 
 def pa_decode_multi_balanced(out, query, key_cache, value_cache, block_tables,

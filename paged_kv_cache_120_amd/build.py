@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpagedkv.so")
 SOURCES = ["csrc/decode.hip", "csrc/cache_ops.hip", "csrc/probe.hip", "csrc/api.cpp",
-           "csrc/noalloc.hip", "csrc/check.hip"]
+           "csrc/noalloc.hip", "csrc/check.hip", "csrc/prefill.hip"]
 ARCH = "gfx950"
 
 

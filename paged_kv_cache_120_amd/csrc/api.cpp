@@ -7,6 +7,7 @@
 
 #include "api_internal.h"
 #include "decode.h"
+#include "prefill.h"
 
 namespace {
 
@@ -538,6 +539,48 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache,
   r.cu_seqlens_q = cu_seqlens_q;
   r.num_seqs = num_seqs;
   return hip_status(pa::launch_multi_reduce(r, head_size, num_q_tokens, stream));
+}
+
+pa_status pa_prefill(void* out, const void* query, const void* key_cache,
+                     const void* value_cache, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                     int32_t num_q_tokens, int32_t max_q_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs,
+                     int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                     int32_t block_size, int32_t num_blocks, float scale,
+                     hipStream_t stream) {
+  pa_status st = check_decode(query, key_cache, value_cache, block_tables,
+                              max_blocks_per_seq, context_lens, num_seqs,
+                              num_heads, num_kv_heads, head_size, block_size,
+                              num_blocks, scale);
+  if (st != PA_OK) return st;
+  if (num_q_tokens < 0 || max_q_per_seq <= 0) return PA_ERR_SHAPE;
+  const int32_t g = num_heads / num_kv_heads;
+  const int64_t tiles = ((int64_t)max_q_per_seq * g + pa::kPrefillRows - 1) /
+                        pa::kPrefillRows;
+  if (tiles > 65535) return PA_ERR_SHAPE;             // grid.y
+  if (num_seqs == 0 || num_q_tokens == 0) return PA_OK;
+  if (!out || !cu_seqlens_q) return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(cu_seqlens_q, 4)) return PA_ERR_ALIGN;
+  pa::PrefillArgs a = {};
+  a.out = static_cast<_Float16*>(out);
+  a.query = static_cast<const _Float16*>(query);
+  a.key_cache = static_cast<const char*>(key_cache);
+  a.value_cache = static_cast<const char*>(value_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.num_q_tokens = num_q_tokens;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.scale = scale;
+  st = checked_tables(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                      num_blocks, block_size, false, stream);
+  if (st != PA_OK) return st;
+  dim3 grid(num_kv_heads, (unsigned)tiles, num_seqs);
+  return hip_status(pa::launch_prefill(a, head_size, block_size, g, grid, stream));
 }
 
 // the narrow form of the matrix-core body when a sequence's rows x heads

@@ -1,0 +1,276 @@
+// Chunked prefill over the paged cache for gfx950: the attention of many
+// query rows per sequence (a prompt chunk) over that sequence's keys,
+// reached through its block table.  [BOOK] §4.5 (2): the backend takes the
+// query tokens of every request delimited by cu_seqlens_q, the keys per
+// request and the block table; §4.5 (1): the chunk's K/V are in the cache
+// before it is read.  Row j of a T-row chunk sits at position n - T + j and
+// attends to keys 0 .. n - T + j (causal).
+//
+// Where the decode kernels stream each key once per query column tile,
+// here the rows x heads that share a kv head are the columns of matrix-core
+// products, 128 per workgroup (32 per wave), so each key tile is read from
+// HBM once per 128 rows and from LDS once per 32:
+//  - a workgroup (kv head, row tile, sequence) walks the keys its rows can
+//    see in tiles of 32, staged through LDS (K and V rows as stored, padded
+//    by 16 bytes), the next tile's global loads in flight while the current
+//    one is computed;
+//  - scores S^T = K Q^T per 16-key block with 16x16x32 MFMAs (keys on the
+//    A rows, the wave's 16-row query blocks on the B columns, Q in
+//    registers for the whole walk);
+//  - the online softmax of [BOOK] §4.6 per query row against a lazy
+//    reference, as in the decode kernels: the accumulators are rescaled only
+//    when a tile's maximum passes the reference by more than 2^8 (weights
+//    stay <= 2^8 before the fp16 rounding of the product), and O / L cancels
+//    the reference at the end;
+//  - O^T += V^T P^T with 16x16x16 MFMAs, V^T read from the row-major tile
+//    and P^T taken from the score layout as it is.
+// Measured on MI355X (512-token chunks, GQA-4): the lazy reference is 5%
+// faster than the exact running maximum; masking only the tiles that reach
+// past a wave's first row (3% slower) and V stored as interleaved key pairs
+// (28% slower: the lane swaps and conflicted stores cost more than the
+// reads they save) are not kept.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "common.h"
+#include "prefill.h"
+
+namespace pa {
+namespace {
+
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kWaveRows = kPrefillRows / kPfWaves;   // 32: two 16-row blocks
+constexpr int kKeyTile = 32;                         // two 16-key blocks
+constexpr float kPfLog2e = 1.4426950408889634f;
+
+constexpr float kPfSlack = 8.f;      // reference slack, base-2 units
+
+// K and V rows as stored, padded by 8 halves (16 bytes)
+template <int D>
+struct PrefillSmem {
+  _Float16 k[kKeyTile][D + 8];
+  _Float16 v[kKeyTile][D + 8];
+};
+
+template <int D, int B, int G>
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3)))
+void prefill_kernel(PrefillArgs a) {
+  constexpr int KS = D / 32;            // 32-channel k-steps of the score MFMA
+  constexpr int DB = D / 16;            // 16-channel blocks of the output
+  constexpr int CPR = D / 8;            // 16-byte chunks per key row
+  constexpr int U = kKeyTile * CPR / kPfThreads;   // chunks per thread per tile
+  static_assert(U * kPfThreads == kKeyTile * CPR, "tile chunks split evenly");
+  __shared__ PrefillSmem<D> sm;
+
+  const int kvh = blockIdx.x;
+  const int s = blockIdx.z;
+  const int q0 = a.cu_seqlens_q[s];
+  const int T = a.cu_seqlens_q[s + 1] - q0;
+  const int rows = T * G;
+  const int r0 = blockIdx.y * kPrefillRows;
+  if (T <= 0 || r0 >= rows) return;
+  const int H = a.num_heads;
+  const int Hkv = a.num_kv_heads;
+  const int max_tok = a.max_blocks_per_seq * B;
+  int n = a.context_lens[s];
+  n = n < max_tok ? n : max_tok;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  // this lane's two B columns: query rows r = r0 + wave*32 + rb*16 + col,
+  // token r / G and head r % G of the chunk; key limit p (none below 0)
+  int prow[2];
+  int64_t orow[2];
+  f16x8 qf[2][KS];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = r0 + wave * kWaveRows + rb * 16 + col;
+    const int j = r / G;
+    const bool ok = r < rows && q0 + j < a.num_q_tokens;
+    prow[rb] = ok && n > 0 ? n - T + j : -1;    // no keys: the row gets zeros
+    orow[rb] = ok ? ((int64_t)(q0 + j) * H + (int64_t)kvh * G + r % G) * D : -1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = *reinterpret_cast<const u32x4*>(a.query + orow[rb] + ks * 32 + grp * 8);
+      qf[rb][ks] = __builtin_bit_cast(f16x8, v);
+    }
+  }
+  // keys any row of the workgroup sees: 0 .. n - T + last token
+  const int rl = (r0 + kPrefillRows < rows ? r0 + kPrefillRows : rows) - 1;
+  const int kend = n > 0 ? n - T + rl / G + 1 : 0;
+
+  const int* bt = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  const int64_t row_elems = (int64_t)Hkv * D;
+  const _Float16* kc = reinterpret_cast<const _Float16*>(a.key_cache) + (int64_t)kvh * D;
+  const _Float16* vc = reinterpret_cast<const _Float16*>(a.value_cache) + (int64_t)kvh * D;
+  u32x4 kr[U], vr[U];
+  // global loads of the key tile at kt0 (zeros past kend or off the pool)
+  auto fetch = [&](int kt0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = (int)threadIdx.x + u * kPfThreads;
+      const int t = kt0 + c / CPR;
+      kr[u] = (u32x4){0u, 0u, 0u, 0u};
+      vr[u] = (u32x4){0u, 0u, 0u, 0u};
+      if (t < kend) {
+        const int blk = bt[t / B];
+        if ((unsigned)blk < (unsigned)a.num_blocks) {
+          const int64_t off = ((int64_t)blk * B + t % B) * row_elems + (c % CPR) * 8;
+          kr[u] = *reinterpret_cast<const u32x4*>(kc + off);
+          vr[u] = *reinterpret_cast<const u32x4*>(vc + off);
+        }
+      }
+    }
+  };
+
+  const float sl2 = a.scale * kPfLog2e;
+  float m[2] = {-INFINITY, -INFINITY};
+  float l[2] = {0.f, 0.f};
+  f32x4 o[2][DB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[rb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  if (kend > 0) fetch(0);
+  for (int kt0 = 0; kt0 < kend; kt0 += kKeyTile) {
+    __syncthreads();                     // every wave is done with the last tile
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = (int)threadIdx.x + u * kPfThreads;
+      const int kk = c / CPR;
+      *reinterpret_cast<u32x4*>(&sm.k[kk][(c % CPR) * 8]) = kr[u];
+      *reinterpret_cast<u32x4*>(&sm.v[kk][(c % CPR) * 8]) = vr[u];
+    }
+    __syncthreads();
+    if (kt0 + kKeyTile < kend) fetch(kt0 + kKeyTile);
+
+    // S^T: A rows = keys kb*16 + col, B columns = query rows; lane keeps
+    // keys kt0 + kb*16 + 4*grp + i of its two rows (raw dot products)
+    float sc[2][2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f16x8 kf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[ks] = *reinterpret_cast<const f16x8*>(&sm.k[kb * 16 + col][ks * 32 + grp * 8]);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], qf[rb][ks], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[kb][rb][i] = kt0 + kb * 16 + grp * 4 + i <= prow[rb] ? acc[i] : -INFINITY;
+      }
+    }
+    // online softmax of each row (its keys spread over the 4 lane groups),
+    // in base-2 units against the lazy reference m
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kb][rb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx *= sl2;
+      if (__builtin_amdgcn_ballot_w64(mx > m[rb] + kPfSlack)) {
+        const float mn = fmaxf(m[rb], mx);
+        const float al = fast_exp2(m[rb] - (mn == -INFINITY ? 0.f : mn));
+        l[rb] *= al;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rb][db] *= al;
+        m[rb] = mn;
+      }
+      const float sh = m[rb] == -INFINITY ? 0.f : m[rb];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[kb][rb][i] = fast_exp2(__builtin_fmaf(sc[kb][rb][i], sl2, -sh));
+          l[rb] += sc[kb][rb][i];
+        }
+    }
+    // O^T += V^T P^T: A = V^T (channel db*16 + col, keys 4*grp + 0..3 of
+    // block kb), B = P^T as the score layout holds it
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f16x4 pb[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pb[rb][i] = (_Float16)sc[kb][rb][i];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f16x4 va;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) va[i] = sm.v[kb * 16 + grp * 4 + i][db * 16 + col];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb[rb], o[rb][db], 0, 0, 0);
+      }
+    }
+  }
+
+  // rows: the sum over the 4 lane groups, then O / L (zeros without keys);
+  // lane holds channels db*16 + 4*grp .. +3 of its rows
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    float L = l[rb];
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+    if (orow[rb] < 0) continue;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      f16x4 h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = (_Float16)(o[rb][db][i] * inv);
+      *reinterpret_cast<f16x4*>(a.out + orow[rb] + db * 16 + grp * 4) = h;
+    }
+  }
+}
+
+template <int D, int B>
+hipError_t launch_db(const PrefillArgs& a, int G, dim3 grid, hipStream_t st) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((prefill_kernel<D, B, 1>), grid, dim3(kPfThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<D, B, 2>), grid, dim3(kPfThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<D, B, 4>), grid, dim3(kPfThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<D, B, 8>), grid, dim3(kPfThreads), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const PrefillArgs& a, int B, int G, dim3 grid, hipStream_t st) {
+  switch (B) {
+    case 16: return launch_db<D, 16>(a, G, grid, st);
+    case 32: return launch_db<D, 32>(a, G, grid, st);
+    case 64: return launch_db<D, 64>(a, G, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, int head_size, int block_size,
+                          int group, dim3 grid, hipStream_t stream) {
+  switch (head_size) {
+    case 64: return launch_d<64>(a, block_size, group, grid, stream);
+    case 128: return launch_d<128>(a, block_size, group, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

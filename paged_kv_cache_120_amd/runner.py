@@ -29,7 +29,7 @@ from . import (pa_balanced_grid, pa_balanced_grid_fp8, pa_balanced_workspace_siz
                pa_multi_balanced_workspace_size_tiles,
                pa_decode_reduce, pa_decode_shared_prefix, pa_decode_splitk,
                pa_decode_step, pa_multi_workspace_size, pa_prefix_workspace_size,
-               pa_slot_mapping, pa_splitk_workspace_size)
+               pa_prefill, pa_slot_mapping, pa_splitk_workspace_size)
 
 
 def _t(a, dev, dtype=None):
@@ -123,12 +123,37 @@ def upload_multi(w, device: str = "cuda", pool: Optional[torch.Tensor] = None) -
     return st
 
 
-def multi_step(step: DeviceStep, stream=None, balanced=None) -> None:
+PREFILL_ROWS = 128          # rows x heads per workgroup of pa_prefill
+PREFILL_MIN_WORKGROUPS = 256
+
+
+def prefill_preferred(step: DeviceStep) -> bool:
+    """pa_prefill once a sequence's rows x heads fill one of its 128-row
+    tiles and the launch has a workgroup per CU: 512-token chunks of the
+    GQA-4 layout (2048 workgroups) 0.49 vs 1.75 ms for pa_decode_multi; 64-
+    token chunks of 6 sequences (96 workgroups) 71 vs 56 us."""
+    g = step.query.shape[1] // step.key_cache.shape[2]
+    rows = step.max_q * g
+    tiles = -(-rows // PREFILL_ROWS)
+    wgs = step.block_tables.shape[0] * step.key_cache.shape[2] * tiles
+    return rows >= PREFILL_ROWS and wgs >= PREFILL_MIN_WORKGROUPS
+
+
+def multi_step(step: DeviceStep, stream=None, balanced=None, prefill=None) -> None:
     """Attention of the step's query rows (their K/V already written):
-    pa_decode_multi_balanced when every sequence's rows x heads fit one
-    16-column tile (or ``balanced`` says so), else pa_decode_multi, which
-    measured faster once a pair needs several tiles (c3 layout, g = 4:
-    8 rows 145 vs 163 us, 64 rows 709 vs 1178 us)."""
+    pa_prefill for long chunks (``prefill_preferred``, or ``prefill`` says
+    so); otherwise pa_decode_multi_balanced when every sequence's rows x
+    heads fit one 16-column tile (or ``balanced`` says so), else
+    pa_decode_multi, which measured faster once a pair needs several tiles
+    (c3 layout, g = 4: 8 rows 145 vs 163 us, 64 rows 709 vs 1178 us).  An
+    explicit ``balanced`` selects between the two decode forms."""
+    if prefill is None:
+        prefill = balanced is None and prefill_preferred(step)
+    if prefill:
+        pa_prefill(step.out, step.query, step.key_cache, step.value_cache,
+                   step.block_tables, step.cu_seqlens_q, step.context_lens,
+                   step.max_q, step.scale, stream=stream)
+        return
     if balanced is None:
         g = step.query.shape[1] // step.key_cache.shape[2]
         balanced = step.multi_grid > 0 and step.max_q * g <= 16

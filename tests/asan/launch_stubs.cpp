@@ -4,6 +4,7 @@
 // launch; every stub reports failure.  split_columns is host arithmetic the
 // validation uses, so it keeps the decode source's definition.
 #include "decode.h"
+#include "prefill.h"
 
 namespace pa {
 
@@ -37,5 +38,8 @@ hipError_t launch_balanced(const DecodeArgs&, int, int, int, int, hipStream_t, i
   return hipErrorNotSupported;
 }
 int balanced_grid(int, int, int, int) { return 0; }
+hipError_t launch_prefill(const PrefillArgs&, int, int, int, dim3, hipStream_t) {
+  return hipErrorNotSupported;
+}
 
 }  // namespace pa

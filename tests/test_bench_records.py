@@ -109,3 +109,38 @@ def test_roofline_counts_method_bytes_only():
 def test_host_cores_are_reported():
     c = bench.host_cores()
     assert c["sched_getaffinity"] >= 1 and 1 <= c["workers"] <= 16
+
+
+def test_prefill_flops_brute_force():
+    """The chunked-prefill flop count equals 4*D*H per visible (row, key)
+    pair counted one by one (row j of a T-row chunk over n keys sees keys
+    0 .. n - T + j)."""
+    import workloads
+    for name in ("c3_small_chunk64", "c1_prefill", "c3_small_spec4"):
+        w = workloads.make(name)
+        cu = w.info["cu_seqlens_q"]
+        pairs = 0
+        for i in range(w.num_seqs):
+            n = int(w.context_lens[i])
+            T = int(cu[i + 1] - cu[i])
+            for j in range(T):
+                pairs += sum(1 for t in range(n) if t <= n - T + j)
+        assert bench.prefill_flops(w) == 4.0 * w.head_size * w.num_heads * pairs
+
+
+def test_prefill_routing_rule():
+    """The runner takes pa_prefill once a sequence's rows x heads fill a
+    128-row tile and the launch has at least 256 workgroups."""
+    from types import SimpleNamespace
+    pytest = __import__("pytest")
+    runner = pytest.importorskip("paged_kv_cache_120_amd.runner")
+
+    def step(S, H, Hkv, max_q):
+        return SimpleNamespace(query=np.zeros((S * max_q, H, 1)),
+                               key_cache=np.zeros((1, 16, Hkv, 1)),
+                               block_tables=np.zeros((S, 1)), max_q=max_q)
+    assert runner.prefill_preferred(step(16, 32, 8, 512))        # 2048 workgroups
+    assert not runner.prefill_preferred(step(6, 32, 8, 64))      # 96 workgroups
+    assert not runner.prefill_preferred(step(64, 32, 8, 4))      # 16 rows x heads
+    assert runner.prefill_preferred(step(32, 40, 40, 128))       # g = 1, one tile each
+    assert not runner.prefill_preferred(step(32, 40, 40, 127))

@@ -503,6 +503,113 @@ def test_multi_token_shapes(D, B, H, Hkv, T, balanced):
     assert_attention_close(st.out.cpu().numpy(), ref, f"multi D{D} g{H // Hkv} T{T}")
 
 
+def run_prefill(w):
+    pa, runner = _gpu()
+    st = runner.upload_multi(w)
+    runner.apply_history(w, st)
+    runner.write_step(st)
+    st.out.fill_(7.0)
+    pa.pa_prefill(st.out, st.query, st.key_cache, st.value_cache, st.block_tables,
+                  st.cu_seqlens_q, st.context_lens, st.max_q, w.scale)
+    torch.cuda.synchronize()
+    return st
+
+
+@pytest.mark.parametrize("name", MULTI_SMALL + ["c3_small_chunk512"])
+def test_prefill_parity(name):
+    """pa_prefill (128 rows x heads per pass over the keys) against
+    oracle.decode_multi on every row and head: chunks of 2-4 rows, 64 and
+    512 rows (several row tiles, causal limits inside a key tile), and the
+    whole prompt as the chunk."""
+    print(f"[prefill] {name}", flush=True)
+    w = workloads.make(name)
+    st = run_prefill(w)
+    kc, vc = oracle_pool(w, oracle)
+    ref = oracle.decode_multi(w.query, kc, vc, w.block_tables, w.info["cu_seqlens_q"],
+                              w.context_lens, w.scale)
+    assert_attention_close(st.out.cpu().numpy(), ref, f"{name}/prefill")
+
+
+@pytest.mark.parametrize("D,B,H,Hkv,T", [(64, 32, 8, 8, 40), (128, 64, 16, 8, 33),
+                                         (128, 16, 16, 16, 7), (64, 16, 16, 4, 100),
+                                         (128, 32, 32, 8, 1), (128, 16, 16, 8, 70)])
+def test_prefill_shapes(D, B, H, Hkv, T):
+    """Head sizes 64 and 128, blocks of 16-64, groups of 1, 2, 4 and 8, and
+    chunk lengths that leave partial row tiles (T*g not a multiple of 128)."""
+    print(f"[prefill-shape] D{D} B{B} H{H}/{Hkv} T{T}", flush=True)
+    w = workloads.make("c2_small_spec4", D=D, B=B, H=H, Hkv=Hkv, q_len=T,
+                       seed=3 * D + B + H + T)
+    st = run_prefill(w)
+    kc, vc = oracle_pool(w, oracle)
+    ref = oracle.decode_multi(w.query, kc, vc, w.block_tables, w.info["cu_seqlens_q"],
+                              w.context_lens, w.scale)
+    assert_attention_close(st.out.cpu().numpy(), ref, f"prefill D{D} g{H // Hkv} T{T}")
+
+
+def test_prefill_full_size_sampled_rows():
+    """The 512-token-chunk workload at full size through the runner's default
+    (pa_prefill), checked on sampled rows of every sequence: the first and
+    last 8 rows of each chunk (the fewest and the most visible keys) against
+    oracle.decode_multi on those rows alone."""
+    pa, runner = _gpu()
+    w = workloads.make("c3_chunk512")
+    st = runner.upload_multi(w)
+    assert runner.prefill_preferred(st)
+    runner.apply_history(w, st)
+    runner.write_step(st)
+    runner.multi_step(st)
+    torch.cuda.synchronize()
+    out = st.out.cpu().numpy().astype(np.float64)
+    kc, vc = oracle_pool(w, oracle)
+    cu = w.info["cu_seqlens_q"]
+    for i in range(w.num_seqs):
+        n, T = int(w.context_lens[i]), int(cu[i + 1] - cu[i])
+        for j0 in (0, T - 8):
+            # rows j0 .. j0+7 of a T-row chunk over n keys are the 8 rows of
+            # an 8-row chunk over n - T + j0 + 8 keys
+            ref = oracle.decode_multi(w.query[cu[i] + j0:cu[i] + j0 + 8], kc, vc,
+                                      w.block_tables[i:i + 1], np.array([0, 8], np.int32),
+                                      np.array([n - T + j0 + 8], np.int32), w.scale)
+            assert_attention_close(out[cu[i] + j0:cu[i] + j0 + 8], ref,
+                                   f"c3_chunk512 seq {i} rows {j0}..")
+
+
+def test_prefill_edge_rows():
+    """Rows placed before the first key (T > n) and a sequence of context 0
+    get zeros; a sequence without rows writes nothing; repeated calls give
+    the same bits; pa_prefill and pa_decode_multi agree within tolerance."""
+    pa, runner = _gpu()
+    w = workloads.make("c3_small_chunk64")
+    st = run_prefill(w)
+    first = st.out.clone()
+    pa.pa_prefill(st.out, st.query, st.key_cache, st.value_cache, st.block_tables,
+                  st.cu_seqlens_q, st.context_lens, st.max_q, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), st.out.view(torch.int16))
+    cu = w.info["cu_seqlens_q"]
+    ctx = w.context_lens.copy()
+    ctx[1] = 0                                  # no keys: its rows are zeros
+    T2 = int(cu[3] - cu[2])
+    ctx[2] = T2 // 2                            # first T2 - T2//2 rows see no key
+    st.context_lens.copy_(torch.from_numpy(ctx))
+    st.out.fill_(7.0)
+    pa.pa_prefill(st.out, st.query, st.key_cache, st.value_cache, st.block_tables,
+                  st.cu_seqlens_q, st.context_lens, st.max_q, w.scale)
+    torch.cuda.synchronize()
+    out = st.out.cpu().numpy().astype(np.float64)
+    assert (out[cu[1]:cu[2]] == 0).all()
+    assert (out[cu[2]:cu[2] + T2 - ctx[2]] == 0).all()
+    kc, vc = oracle_pool(w, oracle)
+    keep = [i for i in range(w.num_seqs) if i not in (1, 2)]
+    rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in keep] +
+                          [np.arange(cu[2] + T2 - ctx[2], cu[3])])
+    Ts = [int(cu[i + 1] - cu[i]) for i in keep] + [int(ctx[2])]
+    cu2 = np.concatenate([[0], np.cumsum(Ts)]).astype(np.int32)
+    ref = oracle.decode_multi(w.query[rows], kc, vc, w.block_tables[keep + [2]], cu2,
+                              ctx[keep + [2]], w.scale)
+    assert_attention_close(out[rows], ref, "prefill edge rows")
+
+
 def test_multi_and_prefix_repeat_calls_bitwise():
     """The multi-token and shared-prefix decodes give the same bits on
     repeated calls (no atomics in their reductions)."""

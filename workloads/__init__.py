@@ -298,6 +298,14 @@ PRESETS: Dict[str, dict] = {
                              lens=_lens_uniform(40, 1500),
                              pool=("choice_scale", 1.25), max_context=8192, q_len=64,
                              seed=1026),
+    # chunked prefill: a 512-token chunk at the end of each sequence (the
+    # whole context when it is shorter), GQA 32/8 heads
+    "c3_chunk512": dict(S=16, H=32, Hkv=8, D=128, B=16, lens=_lens_uniform(512, 4096),
+                        pool=("choice_scale", 1.25), max_context=8192, q_len=512,
+                        seed=1028),
+    "c3_small_chunk512": dict(S=3, H=32, Hkv=8, D=128, B=16, lens=_lens_uniform(300, 1500),
+                              pool=("choice_scale", 1.25), max_context=8192, q_len=512,
+                              seed=1029),
     "c5_b32_small_spec2": dict(S=3, H=64, Hkv=8, D=128, B=32,
                                lens=_lens_uniform(1500, 5000),
                                pool=("choice_scale", 1.25), max_context=131072,
