@@ -363,14 +363,15 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache,
  * Chunked prefill: pa_decode_multi's result (same rows, causal limits,
  * zeros and tolerance; no workspace) for chunks of many query rows per
  * sequence.  Each workgroup takes 128 of a sequence's rows x heads of one
- * kv head and walks the keys they see once, in tiles of 32 staged through
+ * kv head and walks the keys they see once, in tiles of 64 staged through
  * LDS, with the scores and the weighted sum of values on the matrix cores;
  * a key is read from memory once per 128 rows x heads instead of once per
  * 16 (pa_decode_multi's column tile).  Launch: num_kv_heads x
  * ceil(max_q_per_seq * g / 128) x num_seqs workgroups; workgroups past a
  * sequence's own rows exit at once.  Arguments, preconditions and errors
  * as pa_decode_multi without partition_size and the workspace;
- * PA_ERR_SHAPE when ceil(max_q_per_seq * g / 128) exceeds 65535.  Row j of
+ * PA_ERR_SHAPE when ceil(max_q_per_seq * g / 128) exceeds 65535 or
+ * num_q_tokens * num_heads * head_size reaches 2^31.  Row j of
  * a T-row chunk sees keys 0 .. n - T + j; the rows need not be more than
  * one ([BOOK] §4.5 (1)-(2); the running-max recurrence of §4.6 per row).
  */

@@ -559,6 +559,8 @@ pa_status pa_prefill(void* out, const void* query, const void* key_cache,
   const int64_t tiles = ((int64_t)max_q_per_seq * g + pa::kPrefillRows - 1) /
                         pa::kPrefillRows;
   if (tiles > 65535) return PA_ERR_SHAPE;             // grid.y
+  // row offsets of query and out are 32-bit in the kernel
+  if ((int64_t)num_q_tokens * num_heads * head_size >= (1ll << 31)) return PA_ERR_SHAPE;
   if (num_seqs == 0 || num_q_tokens == 0) return PA_OK;
   if (!out || !cu_seqlens_q) return PA_ERR_NULL;
   if (!aligned(out, 16) || !aligned(cu_seqlens_q, 4)) return PA_ERR_ALIGN;

@@ -11,24 +11,27 @@
 // products, 128 per workgroup (32 per wave), so each key tile is read from
 // HBM once per 128 rows and from LDS once per 32:
 //  - a workgroup (kv head, row tile, sequence) walks the keys its rows can
-//    see in tiles of 32, staged through LDS (K and V rows as stored, padded
-//    by 16 bytes), the next tile's global loads in flight while the current
-//    one is computed;
+//    see in tiles of 64, staged through LDS (K and V rows as stored,
+//    padded), the next tile's global loads in flight while the current one
+//    is computed;
 //  - scores S^T = K Q^T per 16-key block with 16x16x32 MFMAs (keys on the
 //    A rows, the wave's 16-row query blocks on the B columns, Q in
-//    registers for the whole walk);
-//  - the online softmax of [BOOK] §4.6 per query row against a lazy
-//    reference, as in the decode kernels: the accumulators are rescaled only
-//    when a tile's maximum passes the reference by more than 2^8 (weights
-//    stay <= 2^8 before the fp16 rounding of the product), and O / L cancels
-//    the reference at the end;
-//  - O^T += V^T P^T with 16x16x16 MFMAs, V^T read from the row-major tile
-//    and P^T taken from the score layout as it is.
-// Measured on MI355X (512-token chunks, GQA-4): the lazy reference is 5%
-// faster than the exact running maximum; masking only the tiles that reach
-// past a wave's first row (3% slower) and V stored as interleaved key pairs
-// (28% slower: the lane swaps and conflicted stores cost more than the
-// reads they save) are not kept.
+//    registers for the whole walk; four key blocks in flight);
+//  - the online softmax of [BOOK] §4.6 per query row (each row's maximum
+//    and sum reduced over its four lane groups with permlane swaps)
+//    against a lazy reference, as in the decode kernels: the accumulators
+//    are rescaled only when a tile's maximum passes the reference by more
+//    than 2^8 (weights stay <= 2^8 before the fp16 rounding of the
+//    product), and O / L cancels the reference at the end;
+//  - O^T += V^T P^T with 16x16x16 MFMAs, each V^T fragment one transposing
+//    LDS read (gfx950's ds_read_b64_tr_b16) of the row-major tile, and P^T
+//    taken from the score layout as it is.
+// Measured on MI355X (512-token chunks, GQA-4): transposing reads 12%
+// faster than four 16-bit reads per fragment, 64-key tiles 2.5% faster
+// than 32, the lazy reference 5% faster than the exact running maximum.
+// Slower and not kept: masking only the tiles past a wave's first row, V
+// stored as interleaved key pairs or transposed by scatter stores, two LDS
+// buffers with one barrier per tile, 8 waves of 16 rows.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -42,17 +45,47 @@ namespace {
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kWaveRows = kPrefillRows / kPfWaves;   // 32: two 16-row blocks
-constexpr int kKeyTile = 32;                         // two 16-key blocks
+constexpr int kKeyTile = 64;                         // four 16-key blocks
+constexpr int KB = kKeyTile / 16;
 constexpr float kPfLog2e = 1.4426950408889634f;
 
 constexpr float kPfSlack = 8.f;      // reference slack, base-2 units
 
-// K and V rows as stored, padded by 8 halves (16 bytes)
+// K and V rows as stored.  K rows padded by 8 halves (the 16 rows of a
+// fragment read land 4 banks apart); V rows by 16 (a transposing read takes
+// 4 rows x 32 bytes per lane group: rows 8 banks apart, groups 32)
 template <int D>
 struct PrefillSmem {
   _Float16 k[kKeyTile][D + 8];
-  _Float16 v[kKeyTile][D + 8];
+  _Float16 v[kKeyTile][D + 16];
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Values of lane l and lane l ^ 16 (l ^ 32): gfx950's permlane swaps with
+// both operands x leave the pair {x[l], x[l ^ 16]} in the two results, in
+// a lane-dependent order, so a max or a sum of the two is the xor
+// reduction without a round trip through LDS
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int D, int B, int G>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3)))
@@ -85,7 +118,7 @@ void prefill_kernel(PrefillArgs a) {
   // this lane's two B columns: query rows r = r0 + wave*32 + rb*16 + col,
   // token r / G and head r % G of the chunk; key limit p (none below 0)
   int prow[2];
-  int64_t orow[2];
+  int orow[2];                 // element offsets (< 2^31: checked by the host)
   f16x8 qf[2][KS];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
@@ -93,7 +126,7 @@ void prefill_kernel(PrefillArgs a) {
     const int j = r / G;
     const bool ok = r < rows && q0 + j < a.num_q_tokens;
     prow[rb] = ok && n > 0 ? n - T + j : -1;    // no keys: the row gets zeros
-    orow[rb] = ok ? ((int64_t)(q0 + j) * H + (int64_t)kvh * G + r % G) * D : -1;
+    orow[rb] = ok ? ((q0 + j) * H + kvh * G + r % G) * D : -1;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
@@ -153,9 +186,9 @@ void prefill_kernel(PrefillArgs a) {
 
     // S^T: A rows = keys kb*16 + col, B columns = query rows; lane keeps
     // keys kt0 + kb*16 + 4*grp + i of its two rows (raw dot products)
-    float sc[2][2][4];
+    float sc[KB][2][4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       f16x8 kf[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
@@ -177,11 +210,10 @@ void prefill_kernel(PrefillArgs a) {
     for (int rb = 0; rb < 2; ++rb) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kb][rb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_xor32(max_xor16(mx));
       mx *= sl2;
       if (__builtin_amdgcn_ballot_w64(mx > m[rb] + kPfSlack)) {
         const float mn = fmaxf(m[rb], mx);
@@ -193,7 +225,7 @@ void prefill_kernel(PrefillArgs a) {
       }
       const float sh = m[rb] == -INFINITY ? 0.f : m[rb];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           sc[kb][rb][i] = fast_exp2(__builtin_fmaf(sc[kb][rb][i], sl2, -sh));
@@ -203,7 +235,7 @@ void prefill_kernel(PrefillArgs a) {
     // O^T += V^T P^T: A = V^T (channel db*16 + col, keys 4*grp + 0..3 of
     // block kb), B = P^T as the score layout holds it
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       f16x4 pb[2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
@@ -211,9 +243,14 @@ void prefill_kernel(PrefillArgs a) {
         for (int i = 0; i < 4; ++i) pb[rb][i] = (_Float16)sc[kb][rb][i];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        f16x4 va;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) va[i] = sm.v[kb * 16 + grp * 4 + i][db * 16 + col];
+        // ds_read_b64_tr_b16: within each 16-lane group, lane j receives
+        // element j % 4 of the 8-byte rows that lanes 4e + j / 4 address
+        // (e = 0..3); lane s of group grp addresses channels
+        // db*16 + 4*(s%4) .. +3 of key kb*16 + 4*grp + s/4, so lane col gets
+        // channel db*16 + col of keys 4*grp + 0..3: the A fragment
+        const f16x4 va = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)&sm.v[kb * 16 + grp * 4 + col / 4]
+                                                             [db * 16 + 4 * (col % 4)]));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
           o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb[rb], o[rb][db], 0, 0, 0);
@@ -226,8 +263,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     float L = l[rb];
-    L += __shfl_xor(L, 16);
-    L += __shfl_xor(L, 32);
+    L = sum_xor32(sum_xor16(L));
     if (orow[rb] < 0) continue;
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll

@@ -263,6 +263,21 @@ def test_multi_validation(pa):
     assert d(*a, 0, 4, *b, 64, FAKE, need, None) == 0           # nothing to do
 
 
+def test_prefill_validation(pa):
+    """pa_prefill checks its host arguments before any launch."""
+    d = pa.lib.pa_prefill
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE]
+    b = [FAKE, 2, 8, 2, 128, 16, 10, 0.1]
+    assert d(None, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 8, 4, *b, None) == 1    # PA_ERR_NULL
+    assert d(*a[:6], None, 8, 4, *b, None) == 1
+    assert d(FAKE + 4, *a[1:], 8, 4, *b, None) == 4                         # PA_ERR_ALIGN
+    assert d(*a, 8, 0, *b, None) == 2                                       # max_q_per_seq
+    assert d(*a, -1, 4, *b, None) == 2
+    assert d(*a, 1 << 21, 4, FAKE, 2, 8, 2, 128, 16, 10, 0.1, None) == 2   # 2^31 elements
+    assert d(*a, 8, 4, FAKE, 2, 8, 2, 96, 16, 10, 0.1, None) == 3          # head size
+    assert d(*a, 0, 4, *b, None) == 0                                       # nothing to do
+
+
 def test_binding_rejects_host_tensors(pa):
     import torch
     x = torch.zeros((2, 8, 128), dtype=torch.float16)
