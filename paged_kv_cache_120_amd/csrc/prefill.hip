@@ -13,10 +13,11 @@
 //  - a workgroup (kv head, row tile, sequence) walks the keys its rows can
 //    see in tiles of 64, staged through LDS (K and V rows as stored,
 //    padded), the next tile's global loads in flight while the current one
-//    is computed;
+//    is computed, block addressing scalar;
 //  - scores S^T = K Q^T per 16-key block with 16x16x32 MFMAs (keys on the
 //    A rows, the wave's 16-row query blocks on the B columns, Q in
-//    registers for the whole walk; four key blocks in flight);
+//    registers for the whole walk; four key blocks in flight), the causal
+//    mask only on tiles that reach past a wave's first row;
 //  - the online softmax of [BOOK] §4.6 per query row (each row's maximum
 //    and sum reduced over its four lane groups with permlane swaps)
 //    against a lazy reference, as in the decode kernels: the accumulators
@@ -28,10 +29,11 @@
 //    taken from the score layout as it is.
 // Measured on MI355X (512-token chunks, GQA-4): transposing reads 12%
 // faster than four 16-bit reads per fragment, 64-key tiles 2.5% faster
-// than 32, the lazy reference 5% faster than the exact running maximum.
-// Slower and not kept: masking only the tiles past a wave's first row, V
-// stored as interleaved key pairs or transposed by scatter stores, two LDS
-// buffers with one barrier per tile, 8 waves of 16 rows.
+// than 32, scalar block addressing with the mask on edge tiles only 21%
+// faster than per-lane addressing and masking, the lazy reference 5%
+// faster than the exact running maximum.  Slower and not kept: V stored as
+// interleaved key pairs or transposed by scatter stores, two LDS buffers
+// with one barrier per tile, 8 waves of 16 rows.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -138,27 +140,39 @@ void prefill_kernel(PrefillArgs a) {
   const int rl = (r0 + kPrefillRows < rows ? r0 + kPrefillRows : rows) - 1;
   const int kend = n > 0 ? n - T + rl / G + 1 : 0;
 
+  // the wave's first row sees the fewest keys: tiles within them need no
+  // causal mask (wave-uniform)
+  const int rw = r0 + wave * kWaveRows;
+  const int pfirst = rw < rows && n > 0 ? n - T + rw / G : -1;
+
+  // Chunk u of a lane: key kw(u) + lane / CPR of the tile, channels
+  // (lane % CPR) * 8 .. +7 of head kvh.  A wave's chunk u covers 64 / CPR
+  // consecutive keys, aligned to that count, so they lie in one block
+  // (B >= 16): the table entry, the block base and the record limit are
+  // scalar, and a lane adds a 32-bit offset.  Keys past kend, or a block id
+  // outside the pool, read as zeros (buffer record limit).
   const int* bt = a.block_tables + (size_t)s * a.max_blocks_per_seq;
-  const int64_t row_elems = (int64_t)Hkv * D;
-  const _Float16* kc = reinterpret_cast<const _Float16*>(a.key_cache) + (int64_t)kvh * D;
-  const _Float16* vc = reinterpret_cast<const _Float16*>(a.value_cache) + (int64_t)kvh * D;
+  const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
+  const uint64_t blk_bytes = (uint64_t)B * row_bytes;
+  const char* kbase = a.key_cache + (size_t)kvh * D * 2;
+  const char* vbase = a.value_cache + (size_t)kvh * D * 2;
+  const uint32_t lane_off = (uint32_t)(lane / CPR) * row_bytes + (lane % CPR) * 16;
   u32x4 kr[U], vr[U];
-  // global loads of the key tile at kt0 (zeros past kend or off the pool)
   auto fetch = [&](int kt0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = (int)threadIdx.x + u * kPfThreads;
-      const int t = kt0 + c / CPR;
-      kr[u] = (u32x4){0u, 0u, 0u, 0u};
-      vr[u] = (u32x4){0u, 0u, 0u, 0u};
-      if (t < kend) {
-        const int blk = bt[t / B];
-        if ((unsigned)blk < (unsigned)a.num_blocks) {
-          const int64_t off = ((int64_t)blk * B + t % B) * row_elems + (c % CPR) * 8;
-          kr[u] = *reinterpret_cast<const u32x4*>(kc + off);
-          vr[u] = *reinterpret_cast<const u32x4*>(vc + off);
-        }
-      }
+      const int kw = __builtin_amdgcn_readfirstlane((64 * wave + kPfThreads * u) / CPR);
+      const int tw = kt0 + kw;
+      const int lb = tw / B;
+      const int blk = tw < kend ? bt[lb] : -1;
+      int valid = kend - lb * B;
+      valid = valid < B ? valid : B;
+      const bool ok = tw < kend && (unsigned)blk < (unsigned)a.num_blocks;
+      const uint32_t nrec = ok ? (uint32_t)valid * row_bytes : 0u;
+      const uint64_t boff = ok ? (uint64_t)blk * blk_bytes : 0;
+      const uint32_t voff = (uint32_t)(tw % B) * row_bytes + lane_off;
+      kr[u] = load16<0>(make_rsrc(kbase + boff, nrec), voff);
+      vr[u] = load16<0>(make_rsrc(vbase + boff, nrec), voff);
     }
   };
 
@@ -200,9 +214,17 @@ void prefill_kernel(PrefillArgs a) {
         for (int ks = 0; ks < KS; ++ks)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], qf[rb][ks], acc, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc[kb][rb][i] = kt0 + kb * 16 + grp * 4 + i <= prow[rb] ? acc[i] : -INFINITY;
+        for (int i = 0; i < 4; ++i) sc[kb][rb][i] = acc[i];
       }
+    }
+    if (kt0 + kKeyTile - 1 > pfirst) {          // a tile on the causal edge
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kt0 + kb * 16 + grp * 4 + i > prow[rb]) sc[kb][rb][i] = -INFINITY;
     }
     // online softmax of each row (its keys spread over the 4 lane groups),
     // in base-2 units against the lazy reference m
