@@ -126,17 +126,18 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, int kvh,
 // as (head in group, channel, max in base-2 units, sum, unnormalised out).
 template <int D, int G, class Smem, class Sink>
 __device__ __forceinline__ void merge_waves(Smem& sm, Sink& sink) {
+  constexpr int W = sizeof(sm.m) / sizeof(sm.m[0]);    // waves of the body
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
     const int gi = idx / D;
     const int d = idx % D;
     float mx = sm.m[0][gi];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][gi]);
+    for (int w = 1; w < W; ++w) mx = fmaxf(mx, sm.m[w][gi]);
     const float sh = mx == -INFINITY ? 0.f : mx;
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < W; ++w) {
       const float f = fast_exp2(sm.m[w][gi] - sh);
       L += sm.l[w][gi] * f;
       O += sm.acc[w][gi][d] * f;
@@ -177,8 +178,9 @@ __device__ __forceinline__ u32x4 widen(u32x2 v) { return fp8x8_to_f16x8(v); }
 // product is reduced across the row with four DPP adds (bitwise identical in
 // every lane) and everything else is lane-local until the end, where row
 // groups merge with cross-lane shuffles and waves through LDS.
-template <int D, int B, int G, int NJ, int EB = 2>
+template <int D, int B, int G, int NJ, int EB = 2, int W = kWaves>
 struct ValuPath {
+  static constexpr int kWavesWG = W;      // waves per workgroup
   static constexpr int LPR = D / 8;       // lanes per token row
   static constexpr int RPI = 64 / LPR;    // token rows per wave load
   static constexpr int TB = RPI * NJ;     // tokens per wave batch
@@ -188,9 +190,9 @@ struct ValuPath {
   static_assert(B % RPI == 0, "a load must not straddle two blocks");
 
   struct Smem {
-    float acc[kWaves][G][D];
-    float m[kWaves][G];
-    float l[kWaves][G];
+    float acc[W][G][D];
+    float m[W][G];
+    float l[W][G];
   };
 
   // t0 must be a multiple of RPI (callers pass multiples of 16).  `last` is
@@ -310,7 +312,7 @@ struct ValuPath {
         }
       }
     };
-    for (int base = t0 + wave * TB; base < t1; base += kWaves * TB) {
+    for (int base = t0 + wave * TB; base < t1; base += W * TB) {
       Raw kk[NJ], vv[NJ];
       issue(base, kk, vv);
       consume(base, kk, vv);
@@ -409,8 +411,9 @@ struct ValuPath {
 // score product is repeated.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <int D, int B, int G, int EB, bool F = false>
+template <int D, int B, int G, int EB, bool F = false, int W = kWaves>
 struct MfmaSplitPath {
+  static constexpr int kWavesWG = W;      // waves per workgroup
   static constexpr int R = 16 / G;              // channel splits = rows per token
   static constexpr int U = 4 / R;               // useful D values per lane per MFMA
   // 16-token tiles per batch.  The 16-column form at D = 128 takes two
@@ -441,20 +444,20 @@ struct MfmaSplitPath {
   using Raw = std::conditional_t<CPL * EB == 16, u32x4, u32x2>;
 
   struct SmemSplit {
-    _Float16 vs[kWaves][TB][VS];
-    float acc[kWaves][G][D];
-    float m[kWaves][G];
-    float l[kWaves][G];
+    _Float16 vs[W][TB][VS];
+    float acc[W][G][D];
+    float m[W][G];
+    float l[W][G];
   };
   // 16 columns: the V staging rows are dead once every wave has left its
   // loop, so the per-wave results take their place (4 workgroups per CU)
   struct SmemFull {
     union {
-      _Float16 vs[kWaves][TB][VS];
-      float acc[kWaves][16][D];
+      _Float16 vs[W][TB][VS];
+      float acc[W][16][D];
     };
-    float m[kWaves][16];
-    float l[kWaves][16];
+    float m[W][16];
+    float l[W][16];
   };
   using Smem = std::conditional_t<F, SmemFull, SmemSplit>;
 
@@ -568,7 +571,7 @@ struct MfmaSplitPath {
     for (int dt = 0; dt < DT; ++dt) o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     _Float16* vw = &sm.vs[wave][0][0];
 
-    for (int base = t0 + wave * TB; base < t1; base += kWaves * TB) {
+    for (int base = t0 + wave * TB; base < t1; base += W * TB) {
       bw.cover(base / B, (base + TB - 1) / B, lane);
       Raw kr[MT][R][KL], vr[MT][R][KL];
 #pragma unroll
@@ -1212,8 +1215,9 @@ __device__ __forceinline__ int64_t balanced_chunk(int64_t total, int grid) {
   return (c + 15) & ~(int64_t)15;
 }
 
-// Inclusive scan over the 256 threads of a workgroup: shuffles within each
+// Inclusive scan over the W waves of a workgroup: shuffles within each
 // wave, then the wave totals through LDS.  `tot` receives the grand total.
+template <int W>
 __device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* wave_sum,
                                               int64_t& tot) {
   const int lane = threadIdx.x & 63;
@@ -1228,7 +1232,7 @@ __device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* wave_sum,
   int64_t before = 0;
   tot = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < W; ++i) {
     before += i < w ? wave_sum[i] : 0;
     tot += wave_sum[i];
   }
@@ -1339,12 +1343,14 @@ struct MultiCols {
 };
 
 template <class Cols, int D, int B, int G>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(64 * Cols::Path::kWavesWG)
 __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
     DecodeArgs a) {
   constexpr int NC = Cols::NC;
+  constexpr int NW = Cols::Path::kWavesWG;   // waves per workgroup
+  constexpr int NT = 64 * NW;
   __shared__ typename Cols::Path::Smem sm;
-  __shared__ int64_t wave_sum[kWaves];
+  __shared__ int64_t wave_sum[NW];
   __shared__ int64_t found_start;
   __shared__ int found_seq;
   __shared__ int merge_here;
@@ -1359,7 +1365,7 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
   if (threadIdx.x == 0) found_seq = -1;
   int64_t total_per_kvh = 0;
   int64_t my_len = 0, my_inc = 0;          // this thread's sequence (pass 0)
-  for (int s0 = 0; s0 < S; s0 += kThreads) {
+  for (int s0 = 0; s0 < S; s0 += NT) {
     const int si = s0 + (int)threadIdx.x;
     const int ns = si < S ? a.context_lens[si] : 1;
     const int64_t len = si < S ? span_len<Cols::kPC>(ns, max_tok) * Cols::tiles(a, si) : 0;
@@ -1368,7 +1374,7 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
       Cols::clear_rows(a, si);
     }
     int64_t chunk = 0;
-    const int64_t inc = block_scan(len, wave_sum, chunk);
+    const int64_t inc = block_scan<NW>(len, wave_sum, chunk);
     if (s0 == 0) {
       my_len = len;
       my_inc = inc;
@@ -1381,7 +1387,7 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
   if (total == 0 || start >= total) return;
   const int64_t end = start + C < total ? start + C : total;
 
-  if (S <= kThreads) {
+  if (S <= NT) {
     // flat span of sequence si: [(inc - len) * H_kv, inc * H_kv)
     if (my_len > 0 && (my_inc - my_len) * Hkv <= start && start < my_inc * Hkv) {
       found_seq = (int)threadIdx.x;
@@ -1390,13 +1396,13 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
     __syncthreads();
   } else {
     int64_t run = 0;
-    for (int s0 = 0; s0 < S; s0 += kThreads) {
+    for (int s0 = 0; s0 < S; s0 += NT) {
       const int si = s0 + (int)threadIdx.x;
       const int64_t len =
           si < S ? span_len<Cols::kPC>(a.context_lens[si], max_tok) * Cols::tiles(a, si) * Hkv
                  : 0;
       int64_t chunk = 0;
-      const int64_t inc = block_scan(len, wave_sum, chunk);
+      const int64_t inc = block_scan<NW>(len, wave_sum, chunk);
       if (len > 0 && run + inc - len <= start && start < run + inc) {
         found_seq = si;
         found_start = run + inc - len;
@@ -1463,7 +1469,7 @@ __attribute__((amdgpu_waves_per_eu(Cols::kMinWaves))) void balanced_kernel(
                        (int)(wl - w0);
         __syncthreads();
         if (merge_here) {
-          for (int idx = threadIdx.x; idx < NC * D; idx += kThreads) {
+          for (int idx = threadIdx.x; idx < NC * D; idx += NT) {
             const int gi = idx / D;
             const int d = idx % D;
             const int64_t oe = Cols::out_elem(a, orow, gi);
@@ -1528,18 +1534,27 @@ template <int G, int EB>
 constexpr int valu_loads() {
   return EB == 2 ? (G >= 4 ? 2 : 8) : (G == 4 ? 4 : G == 2 ? 8 : 16);
 }
-template <int D, int B, int G, int EB = 2>
+template <int D, int B, int G, int EB = 2, int W = kWaves>
 struct PathFor {
-  using type = ValuPath<D, B, G, valu_loads<G, EB>(), EB>;
+  using type = ValuPath<D, B, G, valu_loads<G, EB>(), EB, W>;
 };
-template <int D, int B, int EB>
-struct PathFor<D, B, 8, EB> {
-  using type = MfmaSplitPath<D, B, 8, EB>;
+template <int D, int B, int EB, int W>
+struct PathFor<D, B, 8, EB, W> {
+  using type = MfmaSplitPath<D, B, 8, EB, false, W>;
 };
-template <int B, int EB>
-struct PathFor<128, B, 4, EB> {
-  using type = MfmaSplitPath<128, B, 4, EB>;
+template <int B, int EB, int W>
+struct PathFor<128, B, 4, EB, W> {
+  using type = MfmaSplitPath<128, B, 4, EB, false, W>;
 };
+
+// Waves per workgroup of the balanced decode kernel: 8 (two workgroups per
+// CU) halves the slices' count against 4 waves and four workgroups, so
+// fewer pairs are cut and merged.  Measured on MI355X: Llama-2-13B decode
+// 135.6 -> 129.8 us, GQA-4 70.7 -> 68.6, long context 434.8 -> 433.5; 16
+// waves (one workgroup per CU) were slower (141.7, 82.8).  The multi-token
+// bodies keep 4 (the 16-column form at 8 waves fits one workgroup per CU:
+// 4-token GQA-4 verify 82.4 -> 106.9 us).
+constexpr int kDecodeWaves = 8;
 
 enum class Op { kPartition, kBalanced, kOccupancy, kMulti, kPrefix, kMultiSplit,
                 kPrefixSplit, kMultiBalancedFull, kMultiFullOccupancy,
@@ -1551,14 +1566,16 @@ template <int D, int B, int G, int EB>
 static hipError_t run_op(Op op, const DecodeArgs* a, dim3 grid,
                          hipStream_t st, int* occ) {
   using P = typename PathFor<D, B, G, EB>::type;
-  using DC = DecodeCols<P, D, G>;
+  using DC = DecodeCols<typename PathFor<D, B, G, EB, kDecodeWaves>::type, D, G>;
   switch (op) {
     case Op::kBalanced:
-      hipLaunchKernelGGL((balanced_kernel<DC, D, B, G>), grid, dim3(kThreads), 0, st, *a);
+      hipLaunchKernelGGL((balanced_kernel<DC, D, B, G>), grid, dim3(64 * kDecodeWaves), 0,
+                         st, *a);
       return hipGetLastError();
     case Op::kOccupancy:
       return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          occ, reinterpret_cast<const void*>(&balanced_kernel<DC, D, B, G>), kThreads, 0);
+          occ, reinterpret_cast<const void*>(&balanced_kernel<DC, D, B, G>),
+          64 * kDecodeWaves, 0);
     default:
       break;
   }
