@@ -76,7 +76,7 @@ def split_kernel_bytes(w) -> int:
     return kv_bytes(w) + S * H * D * 2 + table + parts
 
 
-PAIR_COST = 64       # flat units the balanced split charges per (sequence, kv head)
+PAIR_COST = 128      # flat units the balanced split charges per (sequence, kv head)
 FULL_PAIR_COST = 160  # the same for the 16-column multi-token form
 
 

@@ -1197,12 +1197,14 @@ __device__ __forceinline__ int64_t padded_len(int n, int max_tok) {
 // Flat span of one (sequence, kv head) pair: kPairCost units for the fixed
 // cost of the range that starts it (table and query loads, the final merge),
 // then its padded tokens; equal slices of this space then hold fewer tokens
-// where they start more pairs.  Measured on MI355X: 64 (a multiple of 16)
-// lifts the GQA-4 workload by 4-6% and leaves the others unchanged.  The
+// where they start more pairs.  Measured on MI355X with 8-wave workgroups
+// (GQA-4 / Llama-2-13B, us): 32: 79.9 / 130.5, 64: 68.9 / 130.0, 96: 68.4 /
+// 130.7, 128: 67.8 / 130.7 and 67.9 / 130.8 (64: 69.1 / 130.9 in the same
+// run), 160: 69.5 / 132.0, 192: 68.1 / 132.6, 256: 69.6 / 133.8.  The
 // 16-column multi-token form starts a pair at a higher cost (R query passes,
 // a 16-column LDS accumulator, 16 rows to merge and store): 160 there takes
 // 10% off the 4-token GQA-4 verify step (128: 4%, 192: 7%).
-constexpr int kPairCost = 64;
+constexpr int kPairCost = 128;
 constexpr int kFullPairCost = 160;
 template <int PC>
 __device__ __forceinline__ int64_t span_len(int n, int max_tok) {
@@ -1553,8 +1555,13 @@ struct PathFor<128, B, 4, EB, W> {
 // 135.6 -> 129.8 us, GQA-4 70.7 -> 68.6, long context 434.8 -> 433.5; 16
 // waves (one workgroup per CU) were slower (141.7, 82.8).  The multi-token
 // bodies keep 4 (the 16-column form at 8 waves fits one workgroup per CU:
-// 4-token GQA-4 verify 82.4 -> 106.9 us).
-constexpr int kDecodeWaves = 8;
+// 4-token GQA-4 verify 82.4 -> 106.9 us), and so do the fp8 bodies (fp8
+// decode kernel at 8 waves: Llama-2-13B 79.6 -> 83.4 us, long context at
+// block 64 280.2 -> 314.2).
+template <int EB>
+constexpr int decode_waves() {
+  return EB == 2 ? 8 : 4;
+}
 
 enum class Op { kPartition, kBalanced, kOccupancy, kMulti, kPrefix, kMultiSplit,
                 kPrefixSplit, kMultiBalancedFull, kMultiFullOccupancy,
@@ -1566,16 +1573,15 @@ template <int D, int B, int G, int EB>
 static hipError_t run_op(Op op, const DecodeArgs* a, dim3 grid,
                          hipStream_t st, int* occ) {
   using P = typename PathFor<D, B, G, EB>::type;
-  using DC = DecodeCols<typename PathFor<D, B, G, EB, kDecodeWaves>::type, D, G>;
+  constexpr int DW = decode_waves<EB>();
+  using DC = DecodeCols<typename PathFor<D, B, G, EB, DW>::type, D, G>;
   switch (op) {
     case Op::kBalanced:
-      hipLaunchKernelGGL((balanced_kernel<DC, D, B, G>), grid, dim3(64 * kDecodeWaves), 0,
-                         st, *a);
+      hipLaunchKernelGGL((balanced_kernel<DC, D, B, G>), grid, dim3(64 * DW), 0, st, *a);
       return hipGetLastError();
     case Op::kOccupancy:
       return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          occ, reinterpret_cast<const void*>(&balanced_kernel<DC, D, B, G>),
-          64 * kDecodeWaves, 0);
+          occ, reinterpret_cast<const void*>(&balanced_kernel<DC, D, B, G>), 64 * DW, 0);
     default:
       break;
   }
