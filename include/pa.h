@@ -333,10 +333,14 @@ pa_status pa_decode_balanced(void* out, const void* query,
  *                  it are not computed)
  *   partition_size keys per partition, a multiple of block_size; the rows
  *                  of a sequence are computed per partition of its keys in
- *                  one kernel (up to 16 rows x heads, or 4-8 on the narrow
- *                  matrix-core form, share one pass over a partition's
- *                  keys) and a second kernel folds the partitions with the
- *                  [BOOK] §4.6 recurrence
+ *                  one kernel and a second kernel folds the partitions with
+ *                  the [BOOK] §4.6 recurrence.  Up to 16 rows x heads per
+ *                  sequence share a pass over a partition's keys on the
+ *                  decode bodies (4-8 on the narrow form); beyond 16
+ *                  (chunked prefill) 128 of them do, on pa_prefill's
+ *                  matrix-core body (when num_seqs * Pmax <= 65535 and
+ *                  num_q_tokens * num_heads * head_size < 2^31, else the
+ *                  16-column decode body in tiles)
  *   workspace      device, 16-byte aligned, >= pa_multi_workspace_size
  *                  bytes: fp32 max and sum [num_q_tokens, num_heads,
  *                  Pmax] and out [.., head_size] (Pmax as for

@@ -522,9 +522,38 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache,
   st = checked_tables(block_tables, max_blocks_per_seq, context_lens, num_seqs,
                       num_blocks, block_size, false, stream);
   if (st != PA_OK) return st;
-  dim3 grid(num_kv_heads, (unsigned)(num_seqs * tiles), (unsigned)pm);
-  st = hip_status(pa::launch_multi(a, head_size, block_size, g, grid,
-                                   whole_line, stream));
+  // more than 16 rows x heads per sequence: the matrix-core prefill body,
+  // 128 of them per pass over a partition's keys, states in the same layout
+  const int64_t ptiles = ((int64_t)max_q_per_seq * g + pa::kPrefillRows - 1) /
+                         pa::kPrefillRows;
+  if ((int64_t)max_q_per_seq * g > 16 && (int64_t)num_seqs * pm <= 65535 &&
+      (int64_t)num_q_tokens * num_heads * head_size < (1ll << 31)) {
+    pa::PrefillArgs p = {};
+    p.query = a.query;
+    p.key_cache = a.key_cache;
+    p.value_cache = a.value_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.cu_seqlens_q = cu_seqlens_q;
+    p.num_q_tokens = num_q_tokens;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.num_blocks = num_blocks;
+    p.scale = scale;
+    p.ws_max = a.ws_max;
+    p.ws_sum = a.ws_sum;
+    p.ws_out = a.ws_out;
+    p.partition_size = partition_size;
+    p.max_partitions = (int)pm;
+    p.num_seqs = num_seqs;
+    dim3 pgrid(num_kv_heads, (unsigned)ptiles, (unsigned)(num_seqs * pm));
+    st = hip_status(pa::launch_prefill(p, head_size, block_size, g, pgrid, true, stream));
+  } else {
+    dim3 grid(num_kv_heads, (unsigned)(num_seqs * tiles), (unsigned)pm);
+    st = hip_status(pa::launch_multi(a, head_size, block_size, g, grid,
+                                     whole_line, stream));
+  }
   if (st != PA_OK) return st;
   pa::ReduceArgs r = {};
   r.out = static_cast<_Float16*>(out);
@@ -582,7 +611,7 @@ pa_status pa_prefill(void* out, const void* query, const void* key_cache,
                       num_blocks, block_size, false, stream);
   if (st != PA_OK) return st;
   dim3 grid(num_kv_heads, (unsigned)tiles, num_seqs);
-  return hip_status(pa::launch_prefill(a, head_size, block_size, g, grid, stream));
+  return hip_status(pa::launch_prefill(a, head_size, block_size, g, grid, false, stream));
 }
 
 // the narrow form of the matrix-core body when a sequence's rows x heads

@@ -6,7 +6,7 @@
 // query head h, over exactly context_len tokens:
 //   out[i,h] = sum_t softmax_t(scale <q[i,h], K_t>) V_t,  kv head = h / g.
 //
-// A workgroup (4 waves) processes a token range [t0, t1) of one (kv head,
+// A workgroup (4 or 8 waves) processes a token range [t0, t1) of one (kv head,
 // sequence) and serves all g query heads of that kv head, so each K/V byte is
 // fetched from HBM once and reused g times.  Two range bodies exist:
 //   ValuPath      -- vector ALU, dot products reduced with DPP (g = 1, 2,
@@ -172,7 +172,7 @@ __device__ __forceinline__ u32x4 widen(u32x2 v) { return fp8x8_to_f16x8(v); }
 //
 // A 16-byte load per lane covers one token row of one head (D/8 lanes per
 // row), so one load instruction reads whole 128-byte lines.  A wave batch is
-// NJ loads of K and NJ of V per lane in flight; the 4 waves take batches
+// NJ loads of K and NJ of V per lane in flight; the W waves take batches
 // round-robin.  Each row group (one token of a load) keeps its own online
 // softmax state (m, l, acc[8] per head, replicated in the row): the dot
 // product is reduced across the row with four DPP adds (bitwise identical in
@@ -450,7 +450,8 @@ struct MfmaSplitPath {
     float l[W][G];
   };
   // 16 columns: the V staging rows are dead once every wave has left its
-  // loop, so the per-wave results take their place (4 workgroups per CU)
+  // loop, so the per-wave results take their place (4-wave workgroups:
+  // four per CU)
   struct SmemFull {
     union {
       _Float16 vs[W][TB][VS];

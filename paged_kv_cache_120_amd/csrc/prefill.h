@@ -21,13 +21,23 @@ struct PrefillArgs {
   int num_kv_heads;
   int num_blocks;
   float scale;
+  // split mode: one workgroup per (row tile, key partition) writes each
+  // row's (max in natural-log units, sum, unnormalised out) for the
+  // partition to [row, head, max_partitions] states (the split-K layout)
+  float* ws_max;
+  float* ws_sum;
+  float* ws_out;
+  int partition_size;        // keys, a multiple of 16
+  int max_partitions;
+  int num_seqs;
 };
 
 // query rows x heads of one workgroup (grid.y tiles them per sequence)
 constexpr int kPrefillRows = 128;
 
-// grid: (num_kv_heads, ceil(max_q_per_seq * group / kPrefillRows), num_seqs)
+// grid: (num_kv_heads, ceil(max_q_per_seq * group / kPrefillRows), num_seqs),
+// and max_partitions * num_seqs in z (partition-major) for the split mode
 hipError_t launch_prefill(const PrefillArgs& a, int head_size, int block_size,
-                          int group, dim3 grid, hipStream_t stream);
+                          int group, dim3 grid, bool split, hipStream_t stream);
 
 }  // namespace pa

@@ -51,6 +51,7 @@ constexpr int kWaveRows = kPrefillRows / kPfWaves;   // 32: two 16-row blocks
 constexpr int kKeyTile = 64;                         // four 16-key blocks
 constexpr int KB = kKeyTile / 16;
 constexpr float kPfLog2e = 1.4426950408889634f;
+constexpr float kPfLn2 = 0.6931471805599453f;
 
 constexpr float kPfSlack = 8.f;      // reference slack, base-2 units
 
@@ -90,7 +91,7 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int B, int G>
+template <int D, int B, int G, bool SPLIT>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int KS = D / 32;            // 32-channel k-steps of the score MFMA
@@ -106,8 +107,12 @@ void prefill_kernel(PrefillArgs a) {
   // by index; batches of up to 256 sequences, larger ones in batch order),
   // and its row tiles go last to first (later rows see more keys)
   int s = blockIdx.z;
+  int part = 0;
   const int S = gridDim.z;
-  if (S <= kPfThreads) {
+  if constexpr (SPLIT) {           // z = partition * num_seqs + sequence
+    part = blockIdx.z / a.num_seqs;
+    s = blockIdx.z % a.num_seqs;
+  } else if (S <= kPfThreads) {
     __shared__ int lens[kPfThreads];
     __shared__ int pick;
     const int c = (int)threadIdx.x;
@@ -141,6 +146,17 @@ void prefill_kernel(PrefillArgs a) {
   const int col = lane & 15;
   const int grp = lane >> 4;
 
+  // keys any row of the workgroup sees: 0 .. n - T + last token; in the
+  // split mode the partition's keys [k0, kend) of them (none: no states,
+  // the reduce reads only partitions that hold keys of a row)
+  const int rl = (r0 + kPrefillRows < rows ? r0 + kPrefillRows : rows) - 1;
+  int kend = n > 0 ? n - T + rl / G + 1 : 0;
+  const int k0 = SPLIT ? part * a.partition_size : 0;
+  if constexpr (SPLIT) {
+    kend = kend < k0 + a.partition_size ? kend : k0 + a.partition_size;
+    if (kend <= k0) return;
+  }
+
   // this lane's two B columns: query rows r = r0 + wave*32 + rb*16 + col,
   // token r / G and head r % G of the chunk; key limit p (none below 0)
   int prow[2];
@@ -160,14 +176,16 @@ void prefill_kernel(PrefillArgs a) {
       qf[rb][ks] = __builtin_bit_cast(f16x8, v);
     }
   }
-  // keys any row of the workgroup sees: 0 .. n - T + last token
-  const int rl = (r0 + kPrefillRows < rows ? r0 + kPrefillRows : rows) - 1;
-  const int kend = n > 0 ? n - T + rl / G + 1 : 0;
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) prow[rb] = prow[rb] < kend - 1 ? prow[rb] : kend - 1;
+  }
 
   // the wave's first row sees the fewest keys: tiles within them need no
   // causal mask (wave-uniform)
   const int rw = r0 + wave * kWaveRows;
-  const int pfirst = rw < rows && n > 0 ? n - T + rw / G : -1;
+  int pfirst = rw < rows && n > 0 ? n - T + rw / G : -1;
+  if constexpr (SPLIT) pfirst = pfirst < kend - 1 ? pfirst : kend - 1;
 
   // Chunk u of a lane: key kw(u) + lane / CPR of the tile, channels
   // (lane % CPR) * 8 .. +7 of head kvh.  A wave's chunk u covers 64 / CPR
@@ -209,8 +227,8 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[rb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  if (kend > 0) fetch(0);
-  for (int kt0 = 0; kt0 < kend; kt0 += kKeyTile) {
+  if (kend > k0) fetch(k0);
+  for (int kt0 = k0; kt0 < kend; kt0 += kKeyTile) {
     __syncthreads();                     // every wave is done with the last tile
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -311,6 +329,19 @@ void prefill_kernel(PrefillArgs a) {
     float L = l[rb];
     L = sum_xor32(sum_xor16(L));
     if (orow[rb] < 0) continue;
+    if constexpr (SPLIT) {
+      // the partition's state of rows that see one of its keys
+      if (prow[rb] < k0) continue;
+      const size_t pi = (size_t)(orow[rb] / D) * a.max_partitions + part;
+      if (grp == 0) {
+        a.ws_max[pi] = m[rb] * kPfLn2;
+        a.ws_sum[pi] = L;
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<f32x4*>(a.ws_out + pi * D + db * 16 + grp * 4) = o[rb][db];
+      continue;
+    }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -322,24 +353,28 @@ void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, int B>
-hipError_t launch_db(const PrefillArgs& a, int G, dim3 grid, hipStream_t st) {
+template <int D, int B, bool SP>
+hipError_t launch_dbs(const PrefillArgs& a, int G, dim3 grid, hipStream_t st) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<D, B, 1>), grid, dim3(kPfThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<D, B, 2>), grid, dim3(kPfThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<D, B, 4>), grid, dim3(kPfThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<D, B, 8>), grid, dim3(kPfThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<D, B, 1, SP>), grid, dim3(kPfThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<D, B, 2, SP>), grid, dim3(kPfThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<D, B, 4, SP>), grid, dim3(kPfThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<D, B, 8, SP>), grid, dim3(kPfThreads), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const PrefillArgs& a, int B, int G, dim3 grid, hipStream_t st) {
+hipError_t launch_d(const PrefillArgs& a, int B, int G, dim3 grid, bool split,
+                    hipStream_t st) {
   switch (B) {
-    case 16: return launch_db<D, 16>(a, G, grid, st);
-    case 32: return launch_db<D, 32>(a, G, grid, st);
-    case 64: return launch_db<D, 64>(a, G, grid, st);
+    case 16: return split ? launch_dbs<D, 16, true>(a, G, grid, st)
+                          : launch_dbs<D, 16, false>(a, G, grid, st);
+    case 32: return split ? launch_dbs<D, 32, true>(a, G, grid, st)
+                          : launch_dbs<D, 32, false>(a, G, grid, st);
+    case 64: return split ? launch_dbs<D, 64, true>(a, G, grid, st)
+                          : launch_dbs<D, 64, false>(a, G, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -347,10 +382,10 @@ hipError_t launch_d(const PrefillArgs& a, int B, int G, dim3 grid, hipStream_t s
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_size, int block_size,
-                          int group, dim3 grid, hipStream_t stream) {
+                          int group, dim3 grid, bool split, hipStream_t stream) {
   switch (head_size) {
-    case 64: return launch_d<64>(a, block_size, group, grid, stream);
-    case 128: return launch_d<128>(a, block_size, group, grid, stream);
+    case 64: return launch_d<64>(a, block_size, group, grid, split, stream);
+    case 128: return launch_d<128>(a, block_size, group, grid, split, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -110,6 +110,11 @@ def upload_multi(w, device: str = "cuda", pool: Optional[torch.Tensor] = None) -
     cu = w.info["cu_seqlens_q"]
     st.cu_seqlens_q = _t(cu, dev)
     st.max_q = int(max(1, int(np.diff(cu).max(initial=1))))
+    # host-side context statistics of the sequences with rows (routing only)
+    has_rows = np.diff(cu) > 0
+    ctx = w.context_lens[has_rows].astype(np.float64) if has_rows.any() else np.ones(1)
+    st.max_context = int(ctx.max())
+    st.mean_context = float(ctx.mean())
     Q, H, D = w.query.shape
     nbytes = pa_multi_workspace_size(Q, H, D, w.max_blocks_per_seq, w.block_size,
                                      w.partition_size)
@@ -125,28 +130,40 @@ def upload_multi(w, device: str = "cuda", pool: Optional[torch.Tensor] = None) -
 
 PREFILL_ROWS = 128          # rows x heads per workgroup of pa_prefill
 PREFILL_MIN_WORKGROUPS = 256
+PREFILL_MAX_TAIL = 4.0      # longest context over the mean one
 
 
 def prefill_preferred(step: DeviceStep) -> bool:
-    """pa_prefill once a sequence's rows x heads fill one of its 128-row
-    tiles and the launch has a workgroup per CU: 512-token chunks of the
-    GQA-4 layout (2048 workgroups) 0.49 vs 1.75 ms for pa_decode_multi; 64-
-    token chunks of 6 sequences (96 workgroups) 71 vs 56 us."""
+    """pa_prefill (one workgroup walks all the keys of 128 rows x heads)
+    for chunks of more than 16 rows x heads per sequence when the launch has
+    at least 256 workgroups and no context is much longer than the mean
+    (that workgroup would finish last); otherwise pa_decode_multi, whose
+    prefill body splits the keys into partitions and folds them after.
+    Measured on MI355X (us, pa_prefill vs pa_decode_multi): 512-token chunks
+    of 16 sequences ctx U[512, 4096] 293 vs 1745; 2048 rows of one sequence
+    390 vs 559; 8 rows x 64 sequences of 512 keys 36 vs 48; 64 rows of the
+    Llama-2-13B layout 159 vs 276; 16 rows x 64 sequences with lognormal
+    contexts up to 8192 220 vs 134; 512 rows of one sequence of 4096 keys
+    (128 workgroups) 133 vs 76; 64-row chunks of 6 sequences 49 vs 34."""
     g = step.query.shape[1] // step.key_cache.shape[2]
     rows = step.max_q * g
+    if rows <= 16:
+        return False
     tiles = -(-rows // PREFILL_ROWS)
     wgs = step.block_tables.shape[0] * step.key_cache.shape[2] * tiles
-    return rows >= PREFILL_ROWS and wgs >= PREFILL_MIN_WORKGROUPS
+    mean = max(getattr(step, "mean_context", 0.0), 1.0)
+    tail = getattr(step, "max_context", 0) / mean
+    return wgs >= PREFILL_MIN_WORKGROUPS and tail <= PREFILL_MAX_TAIL
 
 
 def multi_step(step: DeviceStep, stream=None, balanced=None, prefill=None) -> None:
     """Attention of the step's query rows (their K/V already written):
-    pa_prefill for long chunks (``prefill_preferred``, or ``prefill`` says
-    so); otherwise pa_decode_multi_balanced when every sequence's rows x
-    heads fit one 16-column tile (or ``balanced`` says so), else
-    pa_decode_multi, which measured faster once a pair needs several tiles
-    (c3 layout, g = 4: 8 rows 145 vs 163 us, 64 rows 709 vs 1178 us).  An
-    explicit ``balanced`` selects between the two decode forms."""
+    pa_prefill when ``prefill_preferred`` (or ``prefill``) says so;
+    otherwise pa_decode_multi_balanced when every sequence's rows x heads
+    fit one 16-column tile (or ``balanced`` says so), else pa_decode_multi
+    (key partitions, then a per-row fold; its prefill body above 16 rows x
+    heads).  An explicit ``balanced`` selects between the two decode
+    forms."""
     if prefill is None:
         prefill = balanced is None and prefill_preferred(step)
     if prefill:

@@ -38,7 +38,7 @@ hipError_t launch_balanced(const DecodeArgs&, int, int, int, int, hipStream_t, i
   return hipErrorNotSupported;
 }
 int balanced_grid(int, int, int, int) { return 0; }
-hipError_t launch_prefill(const PrefillArgs&, int, int, int, dim3, hipStream_t) {
+hipError_t launch_prefill(const PrefillArgs&, int, int, int, dim3, bool, hipStream_t) {
   return hipErrorNotSupported;
 }
 

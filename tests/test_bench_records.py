@@ -129,18 +129,22 @@ def test_prefill_flops_brute_force():
 
 
 def test_prefill_routing_rule():
-    """The runner takes pa_prefill once a sequence's rows x heads fill a
-    128-row tile and the launch has at least 256 workgroups."""
+    """The runner takes pa_prefill for more than 16 rows x heads per
+    sequence when the launch has at least 256 workgroups and the longest
+    context is at most 4x the mean; otherwise the decode-shaped kernels."""
     from types import SimpleNamespace
     pytest = __import__("pytest")
     runner = pytest.importorskip("paged_kv_cache_120_amd.runner")
 
-    def step(S, H, Hkv, max_q):
+    def step(S, H, Hkv, max_q, mx=2048, mean=1024.0):
         return SimpleNamespace(query=np.zeros((S * max_q, H, 1)),
                                key_cache=np.zeros((1, 16, Hkv, 1)),
-                               block_tables=np.zeros((S, 1)), max_q=max_q)
+                               block_tables=np.zeros((S, 1)), max_q=max_q,
+                               max_context=mx, mean_context=mean)
     assert runner.prefill_preferred(step(16, 32, 8, 512))        # 2048 workgroups
     assert not runner.prefill_preferred(step(6, 32, 8, 64))      # 96 workgroups
     assert not runner.prefill_preferred(step(64, 32, 8, 4))      # 16 rows x heads
-    assert runner.prefill_preferred(step(32, 40, 40, 128))       # g = 1, one tile each
-    assert not runner.prefill_preferred(step(32, 40, 40, 127))
+    assert runner.prefill_preferred(step(64, 32, 8, 8))          # 32 rows x heads, 512
+    assert not runner.prefill_preferred(step(64, 32, 8, 16, mx=8192, mean=1150.0))
+    assert runner.prefill_preferred(step(32, 40, 40, 17))        # g = 1, 1280 workgroups
+    assert not runner.prefill_preferred(step(32, 40, 40, 16))

@@ -574,6 +574,30 @@ def test_prefill_full_size_sampled_rows():
                                    f"c3_chunk512 seq {i} rows {j0}..")
 
 
+@pytest.mark.parametrize("P", [16, 64, 512, 4096])
+@pytest.mark.parametrize("name", ["c3_small_chunk64", "c1_prefill", "c3_small_chunk512"])
+def test_multi_wide_chunks_split_prefill_body(name, P):
+    """pa_decode_multi with more than 16 rows x heads per sequence runs the
+    matrix-core prefill body per key partition (128 rows x heads per pass)
+    and the row reduce: every row and head against oracle.decode_multi, at
+    partition sizes from one block to longer than any context."""
+    print(f"[multi-split-prefill] {name} P={P}", flush=True)
+    pa, runner = _gpu()
+    w = workloads.make(name)
+    B = w.block_size
+    w.partition_size = max(P, B)
+    st = runner.upload_multi(w)
+    runner.apply_history(w, st)
+    runner.write_step(st)
+    st.out.fill_(7.0)
+    runner.multi_step(st, balanced=False)
+    torch.cuda.synchronize()
+    kc, vc = oracle_pool(w, oracle)
+    ref = oracle.decode_multi(w.query, kc, vc, w.block_tables, w.info["cu_seqlens_q"],
+                              w.context_lens, w.scale)
+    assert_attention_close(st.out.cpu().numpy(), ref, f"{name}/split prefill P={P}")
+
+
 def test_prefill_edge_rows():
     """Rows placed before the first key (T > n) and a sequence of context 0
     get zeros; a sequence without rows writes nothing; repeated calls give
