@@ -1160,8 +1160,9 @@ __global__ __launch_bounds__(NT) void multi_reduce_kernel(ReduceArgs a) {
 // Flat work order: sequence-major, then kv head, then column tile (one per
 // pair except for wide multi-token chunks), then token; each unit spans
 // a fixed pair cost (kPairCost, kFullPairCost for the 16-column multi-token
-// form) and then its length padded to a multiple of 16 (span_len).  With T the flat total and C = ceil(T / grid) rounded up to
-// 16, workgroup w owns flat positions [w*C, (w+1)*C).  Pairs of one
+// form) and then its length padded to a multiple of 16 (span_len).  With T
+// the flat total and C = ceil(T / grid) rounded up to 16, workgroup w owns
+// flat positions [w*C, (w+1)*C).  Pairs of one
 // sequence are adjacent, so neighbouring workgroups read neighbouring heads
 // of the same token rows.
 //
