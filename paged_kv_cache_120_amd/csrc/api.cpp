@@ -547,8 +547,12 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache,
     p.partition_size = partition_size;
     p.max_partitions = (int)pm;
     p.num_seqs = num_seqs;
+    p.max_tokens = max_blocks_per_seq * block_size;
+    p.out = static_cast<_Float16*>(out);
     dim3 pgrid(num_kv_heads, (unsigned)ptiles, (unsigned)(num_seqs * pm));
     st = hip_status(pa::launch_prefill(p, head_size, block_size, g, pgrid, true, stream));
+    if (st != PA_OK) return st;
+    return hip_status(pa::launch_prefill_fold(p, head_size, stream));
   } else {
     dim3 grid(num_kv_heads, (unsigned)(num_seqs * tiles), (unsigned)pm);
     st = hip_status(pa::launch_multi(a, head_size, block_size, g, grid,

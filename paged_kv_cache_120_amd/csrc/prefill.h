@@ -30,6 +30,7 @@ struct PrefillArgs {
   int partition_size;        // keys, a multiple of 16
   int max_partitions;
   int num_seqs;
+  int max_tokens;            // max_blocks_per_seq * block_size (the fold)
 };
 
 // query rows x heads of one workgroup (grid.y tiles them per sequence)
@@ -39,5 +40,10 @@ constexpr int kPrefillRows = 128;
 // and max_partitions * num_seqs in z (partition-major) for the split mode
 hipError_t launch_prefill(const PrefillArgs& a, int head_size, int block_size,
                           int group, dim3 grid, bool split, hipStream_t stream);
+
+// The fold after the split mode: out[row, head] from the partitions that
+// hold keys 0 .. the row's position (one wave per row and head).
+hipError_t launch_prefill_fold(const PrefillArgs& a, int head_size,
+                               hipStream_t stream);
 
 }  // namespace pa

@@ -353,13 +353,108 @@ void prefill_kernel(PrefillArgs a) {
   }
 }
 
+// The fold: D/16 lanes per (row, head), each lane 16 channels, so a wave
+// holds 1024/D rows x heads and their load chains overlap.  The row's
+// partitions 0 .. pos / partition_size are folded with the [BOOK] §4.6
+// recurrence: the max of their m, then L and O scaled by exp(m_p - max)
+// and summed in partition order (bitwise repeatable; every lane of a row
+// takes the same sums).  Partitions go four at a time, their scalars and
+// rows loaded together.  A row before the first key, or of a sequence
+// without keys, gets zeros.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_fold_kernel(PrefillArgs a) {
+  constexpr int CH = 16;                        // channels per lane
+  constexpr int NV = CH / 4;
+  constexpr int LPI = D / CH;                   // lanes per (row, head)
+  constexpr int IPW = 64 / LPI;
+  constexpr int K = 4;                          // partitions per step
+  const int H = a.num_heads;
+  const int lane = threadIdx.x & 63;
+  const int li = lane % LPI;
+  const int64_t item = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * IPW + lane / LPI;
+  if (item >= (int64_t)a.num_q_tokens * H) return;   // uniform per row x head
+  const int r = (int)(item / H);
+  int lo = 0, hi = a.num_seqs - 1;              // sequence holding row r
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.cu_seqlens_q[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  const int T = a.cu_seqlens_q[lo + 1] - a.cu_seqlens_q[lo];
+  int n = a.context_lens[lo];
+  n = n < a.max_tokens ? n : a.max_tokens;
+  const int pos = n - T + (r - a.cu_seqlens_q[lo]);
+  _Float16* o = a.out + item * D + li * CH;
+  if (n <= 0 || pos < 0) {
+#pragma unroll
+    for (int i = 0; i < CH / 8; ++i) reinterpret_cast<u32x4*>(o)[i] = (u32x4){0u, 0u, 0u, 0u};
+    return;
+  }
+  int np = pos / a.partition_size + 1;
+  np = np < a.max_partitions ? np : a.max_partitions;
+  const size_t base = (size_t)item * a.max_partitions;
+  const float* wo = a.ws_out + base * D + li * CH;
+
+  float m[K], l[K];
+  f32x4 v[K][NV];
+  auto load = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+      const bool in = c + u < np;
+      m[u] = in ? a.ws_max[base + c + u] : -INFINITY;
+      l[u] = in ? a.ws_sum[base + c + u] : 0.f;
+#pragma unroll
+      for (int e = 0; e < NV; ++e)
+        v[u][e] = in ? *reinterpret_cast<const f32x4*>(wo + (size_t)(c + u) * D + 4 * e)
+                     : (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  load(0);                                      // the first step in flight
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < K; ++u) mx = fmaxf(mx, m[u]);
+  for (int c = K; c < np; c += K) {
+#pragma unroll
+    for (int u = 0; u < K; ++u) if (c + u < np) mx = fmaxf(mx, a.ws_max[base + c + u]);
+  }
+  float S = 0.f;
+  f32x4 acc[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) acc[e] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < np; c += K) {
+    if (c > 0) load(c);
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+      if (c + u >= np) break;
+      const float f = fast_exp2((m[u] - mx) * kPfLog2e);
+      S += l[u] * f;
+#pragma unroll
+      for (int e = 0; e < NV; ++e) acc[e] += v[u][e] * f;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < NV; e += 2) {
+    f16x8 h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = (_Float16)(acc[e][i] / S);
+      h[4 + i] = (_Float16)(acc[e + 1][i] / S);
+    }
+    reinterpret_cast<u32x4*>(o)[e / 2] = __builtin_bit_cast(u32x4, h);
+  }
+}
+
 template <int D, int B, bool SP>
 hipError_t launch_dbs(const PrefillArgs& a, int G, dim3 grid, hipStream_t st) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<D, B, 1, SP>), grid, dim3(kPfThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<D, B, 2, SP>), grid, dim3(kPfThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<D, B, 4, SP>), grid, dim3(kPfThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<D, B, 8, SP>), grid, dim3(kPfThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<D, B, 1, SP>),
+                               grid, dim3(kPfThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<D, B, 2, SP>),
+                               grid, dim3(kPfThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<D, B, 4, SP>),
+                               grid, dim3(kPfThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<D, B, 8, SP>),
+                               grid, dim3(kPfThreads), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -380,6 +475,20 @@ hipError_t launch_d(const PrefillArgs& a, int B, int G, dim3 grid, bool split,
 }
 
 }  // namespace
+
+hipError_t launch_prefill_fold(const PrefillArgs& a, int head_size,
+                               hipStream_t stream) {
+  const int64_t items = (int64_t)a.num_q_tokens * a.num_heads;
+  if (items <= 0) return hipSuccess;
+  const int64_t per_wg = 4 * (64 / (head_size / 16));  // rows x heads per workgroup
+  const dim3 grid((unsigned)((items + per_wg - 1) / per_wg));
+  switch (head_size) {
+    case 64: hipLaunchKernelGGL((prefill_fold_kernel<64>), grid, dim3(256), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((prefill_fold_kernel<128>), grid, dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_size, int block_size,
                           int group, dim3 grid, bool split, hipStream_t stream) {

@@ -41,5 +41,8 @@ int balanced_grid(int, int, int, int) { return 0; }
 hipError_t launch_prefill(const PrefillArgs&, int, int, int, dim3, bool, hipStream_t) {
   return hipErrorNotSupported;
 }
+hipError_t launch_prefill_fold(const PrefillArgs&, int, hipStream_t) {
+  return hipErrorNotSupported;
+}
 
 }  // namespace pa
