@@ -634,6 +634,45 @@ def test_prefill_edge_rows():
     assert_attention_close(out[rows], ref, "prefill edge rows")
 
 
+@pytest.mark.parametrize("P", [16, 512])
+def test_multi_split_prefill_edge_rows(P):
+    """pa_decode_multi's split prefill body and its fold: rows of a sequence
+    with context 0, and rows placed before the first key (T > n), get zeros;
+    the other rows match the oracle; a repeated call gives the same bits."""
+    print(f"[multi-split-prefill-edge] P={P}", flush=True)
+    pa, runner = _gpu()
+    w = workloads.make("c3_small_chunk64")
+    w.partition_size = P
+    st = runner.upload_multi(w)
+    runner.apply_history(w, st)
+    runner.write_step(st)
+    cu = w.info["cu_seqlens_q"]
+    ctx = w.context_lens.copy()
+    ctx[1] = 0
+    T2 = int(cu[3] - cu[2])
+    ctx[2] = T2 // 2                            # first T2 - T2//2 rows see no key
+    st.context_lens.copy_(torch.from_numpy(ctx))
+    st.out.fill_(7.0)
+    runner.multi_step(st, balanced=False)
+    torch.cuda.synchronize()
+    first = st.out.clone()
+    runner.multi_step(st, balanced=False)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), st.out.view(torch.int16))
+    out = st.out.cpu().numpy().astype(np.float64)
+    assert (out[cu[1]:cu[2]] == 0).all()
+    assert (out[cu[2]:cu[2] + T2 - ctx[2]] == 0).all()
+    kc, vc = oracle_pool(w, oracle)
+    keep = [i for i in range(w.num_seqs) if i not in (1, 2)]
+    rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in keep] +
+                          [np.arange(cu[2] + T2 - ctx[2], cu[3])])
+    Ts = [int(cu[i + 1] - cu[i]) for i in keep] + [int(ctx[2])]
+    cu2 = np.concatenate([[0], np.cumsum(Ts)]).astype(np.int32)
+    ref = oracle.decode_multi(w.query[rows], kc, vc, w.block_tables[keep + [2]], cu2,
+                              ctx[keep + [2]], w.scale)
+    assert_attention_close(out[rows], ref, f"split prefill edge rows P={P}")
+
+
 def test_multi_and_prefix_repeat_calls_bitwise():
     """The multi-token and shared-prefix decodes give the same bits on
     repeated calls (no atomics in their reductions)."""
