@@ -1538,6 +1538,11 @@ template <int G, int EB>
 constexpr int valu_loads() {
   return EB == 2 ? (G >= 4 ? 2 : 8) : (G == 4 ? 4 : G == 2 ? 8 : 16);
 }
+// the decode columns run on the matrix cores (MfmaSplitPath below)
+template <int D, int G>
+constexpr bool is_mfma_decode() {
+  return G == 8 || (D == 128 && G == 4);
+}
 template <int D, int B, int G, int EB = 2, int W = kWaves>
 struct PathFor {
   using type = ValuPath<D, B, G, valu_loads<G, EB>(), EB, W>;
@@ -1559,10 +1564,20 @@ struct PathFor<128, B, 4, EB, W> {
 // bodies keep 4 (the 16-column form at 8 waves fits one workgroup per CU:
 // 4-token GQA-4 verify 82.4 -> 106.9 us), and so do the fp8 bodies (fp8
 // decode kernel at 8 waves: Llama-2-13B 79.6 -> 83.4 us, long context at
-// block 64 280.2 -> 314.2).
-template <int EB>
+// block 64 280.2 -> 314.2).  The matrix-core decode bodies (g = 8, g = 4 at
+// head size 128) run 4 waves at two workgroups per CU instead: the same
+// slices and cut pairs, half the waves, each with a longer run of batches.
+// Measured on MI355X: GQA-4 67.6 -> 66.4 us, long context 434.1 -> 425.2
+// (the vector body for g = 1 lost 1%: 130.9 -> 132.2; four workgroups of
+// four waves per CU: GQA-4 69.6 at three, 70.7 at four).
+template <int D, int G, int EB>
 constexpr int decode_waves() {
-  return EB == 2 ? 8 : 4;
+  return EB == 2 && !is_mfma_decode<D, G>() ? 8 : 4;
+}
+// workgroups per CU of the balanced decode grid (0: as many as fit)
+template <int D, int G, int EB>
+constexpr int decode_per_cu() {
+  return EB == 2 && is_mfma_decode<D, G>() ? 2 : 0;
 }
 
 enum class Op { kPartition, kBalanced, kOccupancy, kMulti, kPrefix, kMultiSplit,
@@ -1575,15 +1590,19 @@ template <int D, int B, int G, int EB>
 static hipError_t run_op(Op op, const DecodeArgs* a, dim3 grid,
                          hipStream_t st, int* occ) {
   using P = typename PathFor<D, B, G, EB>::type;
-  constexpr int DW = decode_waves<EB>();
+  constexpr int DW = decode_waves<D, G, EB>();
   using DC = DecodeCols<typename PathFor<D, B, G, EB, DW>::type, D, G>;
   switch (op) {
     case Op::kBalanced:
       hipLaunchKernelGGL((balanced_kernel<DC, D, B, G>), grid, dim3(64 * DW), 0, st, *a);
       return hipGetLastError();
-    case Op::kOccupancy:
-      return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+    case Op::kOccupancy: {
+      const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
           occ, reinterpret_cast<const void*>(&balanced_kernel<DC, D, B, G>), 64 * DW, 0);
+      constexpr int cap = decode_per_cu<D, G, EB>();
+      if (e == hipSuccess && cap > 0 && *occ > cap) *occ = cap;
+      return e;
+    }
     default:
       break;
   }
