@@ -403,7 +403,8 @@ pa_status pa_prefill(void* out, const void* query, const void* key_cache,
  * the pair's keys again; from two tiles up the two-kernel pa_decode_multi,
  * whose partitions the hardware dispatcher balances, measured faster.
  * pa_multi_balanced_grid: resident workgroups of this kernel for this
- *   max_q_per_seq (0 if unsupported or unknown); pass the same
+ *   max_q_per_seq, at most two per CU for the 4-column body (0 if
+ *   unsupported or unknown); pass the same
  *   max_q_per_seq to pa_decode_multi_balanced, which picks the matrix-core
  *   body with 4 or 8 columns when max_q_per_seq * g fits them and its
  *   16-column form otherwise.
