@@ -1574,10 +1574,17 @@ template <int D, int G, int EB>
 constexpr int decode_waves() {
   return EB == 2 && !is_mfma_decode<D, G>() ? 8 : 4;
 }
-// workgroups per CU of the balanced decode grid (0: as many as fit)
+// Workgroups per CU of the balanced decode grid (0: as many as fit).  The
+// fp8 matrix-core bodies fit four 4-wave workgroups per CU; fewer run
+// faster.  Measured on MI355X, fp8 decode kernel at grid 1024 / 768 / 512:
+// g = 8 long context 239.7 / 218.5 / 215.4 us (B32) and 282.2 / 280.9 /
+// 259.0 (B64); g = 4 GQA-4 42.8 / 40.8 / 47.8; the fp8 vector body (g = 1)
+// is fastest at four (80.4 / 81.0 / 85.1).
 template <int D, int G, int EB>
 constexpr int decode_per_cu() {
-  return EB == 2 && is_mfma_decode<D, G>() ? 2 : 0;
+  if (!is_mfma_decode<D, G>()) return 0;
+  if (EB == 2) return 2;
+  return G == 8 ? 2 : 3;
 }
 
 enum class Op { kPartition, kBalanced, kOccupancy, kMulti, kPrefix, kMultiSplit,
