@@ -131,12 +131,19 @@ def balanced_kernel_bytes(w, grid: int, fused: bool) -> int:
     return kv_bytes(w) + 2 * S * H * D * 2 + table + extra
 
 
-def balanced_handoff_bytes(w, grid: int) -> int:
+def decode_pair_cost(w, fp8: bool = False) -> int:
+    """The balanced decode's flat units per pair: 192 for the fp16 g = 4
+    matrix-core body at head size 128, else PAIR_COST."""
+    return 192 if (not fp8 and w.group == 4 and w.head_size == 128) else PAIR_COST
+
+
+def balanced_handoff_bytes(w, grid: int, fp8: bool = False) -> int:
     """Bytes of the partial states that cut (sequence, kv head) pairs hand
     between workgroups in one balanced-kernel launch: each range of a cut
     pair writes g (max, sum, out[D]) fp32 states and the merging range reads
     them back."""
-    return 2 * balanced_split_ranges(w, grid) * w.group * (w.head_size + 2) * 4
+    return (2 * balanced_split_ranges(w, grid, decode_pair_cost(w, fp8)) * w.group
+            * (w.head_size + 2) * 4)
 
 
 def single_kernel_bytes(w) -> int:
@@ -813,7 +820,7 @@ def fp8_bench(args, w, dev) -> int:
     kvb = kv_bytes(w) // 2                         # one byte per element
     S, H, D = w.query.shape
     kb = balanced_kernel_bytes(w, steps[0].grid, False) - kv_bytes(w) // 2
-    handoff = balanced_handoff_bytes(w, steps[0].grid)
+    handoff = balanced_handoff_bytes(w, steps[0].grid, fp8=True)
     achieved = kb / (kms * 1e-3) / 1e9
     value = kvb / (ms_step * 1e-3) / 1e9
     rec = {

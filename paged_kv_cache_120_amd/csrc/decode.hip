@@ -1208,6 +1208,17 @@ __device__ __forceinline__ int64_t padded_len(int n, int max_tok) {
 // 10% off the 4-token GQA-4 verify step (128: 4%, 192: 7%).
 constexpr int kPairCost = 128;
 constexpr int kFullPairCost = 160;
+// The fp16 g = 4 matrix-core decode body charges 192: GQA-4 decode 66.2 ->
+// 65.3 us (224: 66.0, 256: 66.1, 96: 67.5); the long-context g = 8 body and
+// the vector body keep 128 (160 / 192: +0.2 / +0.3% and +0.7 / +0.6%).
+template <class P>
+struct DecodePairCost {
+  static constexpr int value = kPairCost;
+};
+template <int B, int W>
+struct DecodePairCost<MfmaSplitPath<128, B, 4, 2, false, W>> {
+  static constexpr int value = 192;
+};
 template <int PC>
 __device__ __forceinline__ int64_t span_len(int n, int max_tok) {
   const int64_t np = padded_len(n, max_tok);
@@ -1256,7 +1267,7 @@ struct DecodeCols {
   using Path = P;
   static constexpr int NC = G;
   static constexpr int kMinWaves = P::kMinWaves;
-  static constexpr int kPC = kPairCost;        // flat units charged per pair
+  static constexpr int kPC = DecodePairCost<P>::value;   // flat units per pair
   // one column tile (the g heads) per (sequence, kv head)
   __device__ static int tiles(const DecodeArgs&, int) { return 1; }
   __device__ static int max_tiles(const DecodeArgs&) { return 1; }

@@ -99,7 +99,8 @@ def test_roofline_counts_method_bytes_only():
     assert bench.balanced_kernel_bytes(w, 64, True) == kv + 2 * S * H * D * 2 + table + appended
     assert bench.balanced_kernel_bytes(w, 64, False) == kv + 2 * S * H * D * 2 + table
     ho = bench.balanced_handoff_bytes(w, 64)
-    assert ho == 2 * bench.balanced_split_ranges(w, 64) * w.group * (D + 2) * 4 and ho > 0
+    pc = bench.decode_pair_cost(w)
+    assert ho == 2 * bench.balanced_split_ranges(w, 64, pc) * w.group * (D + 2) * 4 and ho > 0
     rec = bench.decode_record(w, "fused", 64, 0.01, 0.008)
     rf = rec["roofline"]
     assert rf["handoff_bytes"] == ho
